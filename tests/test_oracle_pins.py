@@ -1,0 +1,302 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test ties an oracle function to something the pages or mathematics fix:
+a brute-force loop implementation, a textbook library routine (PyTorch's
+scaled-dot-product attention on the CPU in float64), a closed form, an exact
+identity (complex-number rotation, relative-position invariance), or a number
+the pages print (``tests/golden/page_numbers.txt``).  ``test_oracle_mutants``
+checks that planted mistakes in the oracle make these pins fail.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_15_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_numbers():
+    out = {}
+    with open(os.path.join(GOLDEN, "page_numbers.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, v = line.split()
+                out[k] = float(v)
+    return out
+
+
+def _weights64(shape, cid):
+    return {k: v.f64() for k, v in inputs.make_weights(shape, cid, "f32").items()}
+
+
+def _rel(a, b):
+    return oracle.max_rel_error(a, b)
+
+
+SMALL_SHAPES = [
+    inputs.TINY,
+    inputs.Shape(d=24, n_h=3, d_h=8, d_c=12, d_cq=10, d_r=4),
+    inputs.Shape(d=40, n_h=2, d_h=6, d_c=20, d_cq=16, d_r=6),
+]
+
+
+# ---------------------------------------------------------------------------
+# page numbers
+# ---------------------------------------------------------------------------
+
+def test_page_numbers_cache_sizes():
+    g = _golden_numbers()
+    V2 = inputs.V2
+    assert (V2.d, V2.d_c, V2.d_r, V2.n_h, V2.d_h, V2.d_cq) == tuple(
+        int(g[k]) for k in ("v2.d", "v2.d_c", "v2.d_r", "v2.n_h", "v2.d_h", "v2.d_cq"))
+    assert V2.d_h + V2.d_r == g["v2.score_dim"]
+    assert V2.n_h * V2.d_h == g["v2.concat"]
+    # per-token cache: 576 numbers for MLA against 32768 for MHA at the V2 shape
+    assert oracle.mla_numbers_per_token(V2.d_c, V2.d_r) == 576
+    assert oracle.mha_numbers_per_token(V2.n_h, V2.d_h) == 32768
+    # the worked ratio on the formula page
+    r = oracle.latent_compression_ratio(int(g["p3.d_c"]), int(g["p3.n_h"]), int(g["p3.d_h"]))
+    assert r == g["p3.ratio_num"] / g["p3.ratio_den"]
+    assert abs((1 - r) * 100 - g["p3.reduction_pct"]) < 1e-12
+
+
+def test_layer_dimensions_v2():
+    """Tensor shapes the oracle produces at the V2 layer shape (small token count)."""
+    s = inputs.V2
+    W = {k: np.asarray(v.f32, np.float64) for k, v in inputs.make_weights(s, 91, "f32").items()}
+    H = inputs.make_hidden(3, s, 91, "f32").f64()
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(3), 10000.0)
+    assert c.shape == (3, 512) and kr.shape == (3, 64)
+    q_c, q_r = oracle.query(H[-1], W["W_DQ"], W["W_UQ"], W["W_QR"], 2, s.n_h, 10000.0)
+    assert q_c.shape == (128, 128) and q_r.shape == (128, 64)
+    Qt = oracle.absorbed_query(q_c, q_r, W["W_UK"], oracle.default_scale(128, 64))
+    assert Qt.shape == (128, 576)
+    u = oracle.decode(H[-1], 2, c, kr, W, s.n_h, 10000.0)
+    assert u.shape == (5120,)
+
+
+# ---------------------------------------------------------------------------
+# brute force and order A == order B
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+@pytest.mark.parametrize("N", [1, 5, 17])
+def test_bruteforce_equals_order_a(si, N):
+    s = SMALL_SHAPES[si]
+    W = _weights64(s, 100 + si)
+    H = inputs.make_hidden(N, s, 100 + si, "f32", sub=N).f64()
+    scale = oracle.default_scale(s.d_h, s.d_r)
+    u_bf = oracle.decode_bruteforce(H, W, s.n_h, 10000.0, scale)
+    u_a = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="A")
+    assert _rel(u_a, u_bf) < 1e-12
+
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+def test_order_a_equals_order_b(si):
+    s = SMALL_SHAPES[si]
+    W = _weights64(s, 200 + si)
+    H = inputs.make_hidden(33, s, 200 + si, "f32").f64()
+    u_a = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="A")
+    u_b = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="B")
+    assert _rel(u_b, u_a) < 1e-12
+
+
+def test_order_a_equals_order_b_v2_heads():
+    """V2 head geometry (d_h=128, d_c=512, d_R=64) with fewer heads and a smaller d."""
+    s = inputs.Shape(d=256, n_h=4, d_h=128, d_c=512, d_cq=192, d_r=64)
+    W = _weights64(s, 301)
+    H = inputs.make_hidden(70, s, 301, "f32").f64()
+    u_a = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="A")
+    u_b = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="B")
+    assert _rel(u_b, u_a) < 1e-12
+
+
+def test_softmax_rows_sum_to_one():
+    s = inputs.TINY
+    W = _weights64(s, 7)
+    H = inputs.make_hidden(17, s, 7, "f32").f64()
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(17), 10000.0)
+    q_c, q_r = oracle.query(H[-1], W["W_DQ"], W["W_UQ"], W["W_QR"], 16, s.n_h, 10000.0)
+    _, p = oracle.attend_order_a(q_c, q_r, c, kr, W["W_UK"], W["W_UV"], 0.2, return_p=True)
+    assert np.all(p >= 0)
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# textbook special case: W_QR = 0 reduces MLA to MHA with K = W_UK W_DKV h and
+# V = W_UV W_DKV h; compared with torch's scaled_dot_product_attention (fp64)
+# ---------------------------------------------------------------------------
+
+def _sdpa_reference(H, W, n_h, scale, causal):
+    Hq = torch.from_numpy(H)
+    d_h = W["W_UQ"].shape[0] // n_h
+    WDKV = torch.from_numpy(W["W_DKV"])
+    Wq = torch.from_numpy(W["W_UQ"]) @ torch.from_numpy(W["W_DQ"])      # merged query map
+    Q = (Hq @ Wq.T).reshape(-1, n_h, d_h).transpose(0, 1)               # [n_h][T][d_h]
+    K = (Hq @ (torch.from_numpy(W["W_UK"]) @ WDKV).T).reshape(-1, n_h, d_h).transpose(0, 1)
+    V = (Hq @ (torch.from_numpy(W["W_UV"]) @ WDKV).T).reshape(-1, n_h, d_h).transpose(0, 1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        Q.contiguous(), K.contiguous(), V.contiguous(), is_causal=causal, scale=scale)
+    o = o.transpose(0, 1).reshape(H.shape[0], n_h * d_h)
+    return (o @ torch.from_numpy(W["W_O"]).T).numpy()
+
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+def test_mha_special_case_decode(si):
+    s = SMALL_SHAPES[si]
+    W = _weights64(s, 400 + si)
+    W["W_QR"] = np.zeros_like(W["W_QR"])
+    H = inputs.make_hidden(29, s, 400 + si, "f32").f64()
+    scale = oracle.default_scale(s.d_h, s.d_r)
+    ref = _sdpa_reference(H, W, s.n_h, scale, causal=True)[-1]
+    for order in ("A", "B"):
+        u = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order=order)
+        assert _rel(u, ref) < 1e-12
+
+
+def test_mha_special_case_causal_prefill():
+    s = SMALL_SHAPES[1]
+    W = _weights64(s, 450)
+    W["W_QR"] = np.zeros_like(W["W_QR"])
+    T = 23
+    H = inputs.make_hidden(T, s, 450, "f32").f64()
+    scale = oracle.default_scale(s.d_h, s.d_r)
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(T), 10000.0)
+    u = oracle.prefill_order_a(H, np.arange(T), c, kr, W, s.n_h, 10000.0, scale)
+    ref = _sdpa_reference(H, W, s.n_h, scale, causal=True)
+    assert _rel(u, ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def test_single_token_closed_form():
+    """kv_len = 1: softmax of one score is 1, so o_i = W_UV,i c_0."""
+    s = SMALL_SHAPES[0]
+    W = _weights64(s, 500)
+    H = inputs.make_hidden(1, s, 500, "f32").f64()
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], [0], 10000.0)
+    q_c, q_r = oracle.query(H[0], W["W_DQ"], W["W_UQ"], W["W_QR"], 0, s.n_h, 10000.0)
+    expect = W["W_UV"].reshape(s.n_h, s.d_h, s.d_c) @ c[0]
+    for f in (oracle.attend_order_a, oracle.attend_order_b):
+        o = f(q_c, q_r, c, kr, W["W_UK"], W["W_UV"], 0.3)
+        assert np.max(np.abs(o - expect)) < 1e-13
+    u = oracle.decode_from_hidden(H, W, s.n_h, 10000.0)
+    assert _rel(u, W["W_O"] @ expect.reshape(-1)) < 1e-13
+
+
+def test_uniform_attention_closed_form():
+    """W_UQ = W_QR = 0 makes every score 0, so o~_i is the plain mean of the latents."""
+    s = SMALL_SHAPES[2]
+    W = _weights64(s, 510)
+    W["W_UQ"] = np.zeros_like(W["W_UQ"])
+    W["W_QR"] = np.zeros_like(W["W_QR"])
+    rows = inputs.make_cache_rows(41, s, 510, "f32").f64()
+    q_c, q_r = oracle.query(np.ones(s.d), W["W_DQ"], W["W_UQ"], W["W_QR"], 40, s.n_h, 10000.0)
+    Qt = oracle.absorbed_query(q_c, q_r, W["W_UK"], 0.5)
+    o_lat = oracle.latent_attention(Qt, rows, s.d_c)
+    mean = rows[:, :s.d_c].sum(axis=0) / rows.shape[0]
+    assert np.max(np.abs(o_lat - mean[None, :])) < 1e-14
+
+
+def test_prefill_row0_closed_form_and_decode_consistency():
+    s = SMALL_SHAPES[1]
+    W = _weights64(s, 520)
+    T = 12
+    H = inputs.make_hidden(T, s, 520, "f32").f64()
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(T), 10000.0)
+    u = oracle.prefill_order_a(H, np.arange(T), c, kr, W, s.n_h, 10000.0)
+    row0 = W["W_O"] @ (W["W_UV"].reshape(s.n_h, s.d_h, s.d_c) @ c[0]).reshape(-1)
+    assert _rel(u[0], row0) < 1e-13
+    for t in (5, T - 1):
+        assert _rel(u[t], oracle.decode_from_hidden(H[:t + 1], W, s.n_h, 10000.0)) < 1e-12
+
+
+def test_latent_pipeline_equals_order_b():
+    """absorbed_query -> latent_attention -> latent_output is order B end to end."""
+    s = SMALL_SHAPES[0]
+    W = _weights64(s, 530)
+    H = inputs.make_hidden(17, s, 530, "f32").f64()
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(17), 10000.0)
+    q_c, q_r = oracle.query(H[-1], W["W_DQ"], W["W_UQ"], W["W_QR"], 16, s.n_h, 10000.0)
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    Qt = oracle.absorbed_query(q_c, q_r, W["W_UK"], sc)
+    o_lat = oracle.latent_attention(Qt, np.concatenate([c, kr], 1), s.d_c)
+    u = oracle.latent_output(o_lat, W["W_UV"], W["W_O"])
+    assert _rel(u, oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="A")) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def test_rope_matches_complex_rotation():
+    """Pair (x_2k, x_2k+1) as z = x_2k + i x_2k+1, rotated by exp(i pos theta_k)."""
+    rng = np.random.default_rng(5)
+    for d_r in (2, 8, 64):
+        x = rng.standard_normal((7, d_r))
+        pos = np.array([0, 1, 2, 17, 1000, 65536, 131072])
+        theta = 10000.0 ** (-np.arange(0, d_r, 2) / d_r)
+        z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * pos[:, None] * theta[None, :])
+        ref = np.empty_like(x)
+        ref[:, 0::2], ref[:, 1::2] = z.real, z.imag
+        assert np.max(np.abs(oracle.rope(x, pos, 10000.0) - ref)) < 1e-12
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal(64)
+    k = rng.standard_normal(64)
+    assert np.array_equal(oracle.rope(q, 0, 10000.0), q)                       # identity at 0
+    for p in (1, 99, 4096, 131072):
+        assert abs(np.linalg.norm(oracle.rope(q, p, 10000.0)) - np.linalg.norm(q)) < 1e-12
+    # scores depend only on the relative position
+    s0 = oracle.rope(q, 40, 1e4) @ oracle.rope(k, 13, 1e4)
+    for delta in (1, 1000, 100000):
+        s1 = oracle.rope(q, 40 + delta, 1e4) @ oracle.rope(k, 13 + delta, 1e4)
+        assert abs(s1 - s0) < 1e-9
+    th = oracle.rope_frequencies(64, 10000.0)
+    assert th[0] == 1.0 and abs(th[-1] - 10000.0 ** (-62 / 64)) < 1e-18
+
+
+def test_relative_position_invariance_of_decode():
+    """Shifting every position (cache rows and query) by the same amount leaves
+    the decode output unchanged: only the RoPE term sees positions."""
+    s = SMALL_SHAPES[0]
+    W = _weights64(s, 540)
+    H = inputs.make_hidden(9, s, 540, "f32").f64()
+    out = []
+    for shift in (0, 777):
+        pos = np.arange(9) + shift
+        c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], pos, 10000.0)
+        out.append(oracle.decode(H[-1], int(pos[-1]), c, kr, W, s.n_h, 10000.0))
+    assert _rel(out[1], out[0]) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# stored regression fixture (written by tests/golden/make_golden.py from the oracle)
+# ---------------------------------------------------------------------------
+
+def test_tiny_decode_fixture():
+    path = os.path.join(GOLDEN, "tiny_decode_u.txt")
+    ref = np.loadtxt(path)
+    s = inputs.TINY
+    W = _weights64(s, 1)
+    H = inputs.make_hidden(17, s, 1, "f32").f64()
+    u = oracle.decode_from_hidden(H, W, s.n_h, 10000.0)
+    assert np.max(np.abs(u - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_max_rel_error_metric():
+    ref = np.array([[1.0, -4.0, 2.0], [0.5, 0.5, 0.0]])
+    y = ref + np.array([[0.04, 0.0, 0.0], [0.0, 0.0, 0.01]])
+    assert math.isclose(oracle.max_rel_error(y, ref), 0.02)
+    y[0, 0] = np.nan
+    assert oracle.max_rel_error(y, ref) == float("inf")
