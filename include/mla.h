@@ -1,0 +1,175 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention library.
+ *
+ * The layer follows the MLA pages:
+ *   [walkthrough] "MLA（多头潜在注意力）" walkthrough (h.sjds.net/a/578141),
+ *                 §1 steps 1-5 and §3 (orders A and B);
+ *   [formulas]    DeepSeek-V2 MLA formula walk-through (modelers.csdn.net),
+ *                 equations (9)-(13) and §三 (absorption);
+ *   [wiki]        "MLA 多头潜在注意力" (chenshi221.pages.dev), "与 RoPE 的兼容性".
+ *
+ * Conventions for every call
+ *  - Every pointer argument named d_* or documented as "device" is a device
+ *    pointer owned by the caller.  The library never allocates, never frees
+ *    and never synchronises: each call enqueues kernels on `stream` (a
+ *    hipStream_t; NULL is the null stream) and returns.  Scratch memory is the
+ *    caller-provided `workspace` of at least mla_workspace_size() bytes,
+ *    256-byte aligned.
+ *  - Matrices are row-major.  Weights are [out][in] with y = W x.  Head i owns
+ *    rows [i*d_h, (i+1)*d_h) of W_UQ, W_UK, W_UV, rows [i*d_r, (i+1)*d_r) of
+ *    W_QR and columns [i*d_h, (i+1)*d_h) of W_O.
+ *  - Activations, weights and the cache share one storage dtype (cfg->dtype);
+ *    all products accumulate in fp32.
+ *  - The latent cache is [num_pages][page_size][d_c + d_r]: each token's row
+ *    is its latent c^KV followed by its RoPE key k^R, with no head index
+ *    ([walkthrough] step 1).  Token t of a sequence lives at page
+ *    page_table[t / page_size], slot t % page_size.
+ *  - RoPE rotates interleaved pairs (x_2k, x_2k+1) by pos * base^(-2k/d_r),
+ *    with cos/sin read from a table filled by mla_rope_table_init.
+ *  - Errors: host-side argument checks run before anything is enqueued and
+ *    return a negative mla_status; nothing is launched then.  Device-resident
+ *    indices (lengths, positions, page ids, slots) are checked inside the
+ *    kernels: no kernel reads or writes outside the buffers described by the
+ *    size arguments; a decode/prefill output row whose indices are invalid is
+ *    filled with NaN, and an append row with an invalid slot or position is
+ *    not written.  MLA_ERR_HIP reports a failed launch (hipGetLastError).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,  /* null pointer, bad size or shape */
+  MLA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+  MLA_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small */
+  MLA_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_OP_APPEND = 0,
+  MLA_OP_DECODE = 1,
+  MLA_OP_PREFILL = 2,
+  MLA_OP_DECODE_QUERY = 3,
+  MLA_OP_DECODE_ATTENTION = 4,
+  MLA_OP_DECODE_OUTPUT = 5
+} mla_op;
+
+/* Layer geometry.  DeepSeek-V2: d=5120, n_h=128, d_h=128, d_c=512,
+ * d_cq=1536, d_r=64 ([walkthrough] §1). */
+typedef struct mla_config {
+  int d;              /* model (hidden) dim */
+  int n_h;            /* heads */
+  int d_h;            /* per-head content dim of q, k and v */
+  int d_c;            /* KV latent dim (cached) */
+  int d_cq;           /* query latent dim */
+  int d_r;            /* decoupled RoPE dim (cached once per token), even */
+  int page_size;      /* tokens per cache page */
+  mla_dtype dtype;    /* storage dtype of weights, activations and cache */
+  float softmax_scale;/* <= 0 selects 1/sqrt(d_h + d_r) */
+  double rope_base;   /* <= 0 selects 10000 */
+} mla_config;
+
+/* Device pointers to the eight projection matrices, each [out][in]:
+ * W_DKV [d_c][d], W_KR [d_r][d], W_DQ [d_cq][d], W_UQ [n_h*d_h][d_cq],
+ * W_QR [n_h*d_r][d_cq], W_UK [n_h*d_h][d_c], W_UV [n_h*d_h][d_c],
+ * W_O [d][n_h*d_h].  A call reads only the ones it uses. */
+typedef struct mla_weights {
+  const void *W_DKV, *W_KR, *W_DQ, *W_UQ, *W_QR, *W_UK, *W_UV, *W_O;
+} mla_weights;
+
+/* Text for a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int mla_version(void);
+
+/* Fill the RoPE table d_table [max_pos][d_r/2][2] (cos, sin as fp32) for
+ * positions 0..max_pos-1; angles pos * base^(-2k/d_r) are formed in fp64.
+ * ([wiki] "与 RoPE 的兼容性": the decoupled RoPE part carries positions.) */
+int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void* stream);
+
+/* Bytes of workspace `op` needs.  batch: B for decode ops, T for append and
+ * prefill.  max_kv_len: longest kv_len the call may see (decode, prefill).
+ * num_splits: as passed to mla_decode / mla_decode_attention (0 = auto).
+ * Returns 0 for an invalid request. */
+size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_len,
+                          int num_splits);
+
+/* Write memory ([walkthrough] step 1, [formulas] eq. (9)):
+ *   c^KV_t = W_DKV h_t,  k^R_t = RoPE(W_KR h_t, positions[t])
+ * and store [c^KV_t | k^R_t], rounded to cfg->dtype, at cache slot
+ * slot_mapping[t] (= page * page_size + offset).  A row whose slot is outside
+ * [0, num_pages*page_size) or whose position is outside [0, rope_len) is not
+ * written.  h: device [T][d].  positions, slot_mapping: device int32 [T].
+ * rope_table: device, from mla_rope_table_init with max_pos = rope_len. */
+int mla_append_kv(const mla_config* cfg, const mla_weights* w, const void* h,
+                  const int32_t* positions, const int32_t* slot_mapping, int T,
+                  const float* rope_table, int rope_len, void* kv_cache, int num_pages,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Decode, order B ([walkthrough] §3 顺序 B; [formulas] §三): for each sequence
+ * b, the query from h[b] at position positions[b] attends to cached tokens
+ * 0..kv_lens[b]-1 (the caller appends the query's own row first, so
+ * kv_lens[b] = positions[b] + 1 in the usual case) and out[b] receives
+ *   u = W_O [W_UV,i o~_i]_i,  o~_i = sum_j softmax_j(Q~_i . row_j) c^KV_j,
+ *   Q~_i = [W_UK,i^T q^C_i | q^R_i] * scale.
+ * h: device [B][d]; positions, kv_lens: device int32 [B];
+ * page_table: device int32 [B][max_pages]; out: device [B][d].
+ * max_kv_len bounds every kv_lens[b] (1 <= kv_lens[b] <= max_kv_len <=
+ * max_pages*page_size); a sequence outside that gets a NaN output row.
+ * num_splits: 0 balances the tokens of all sequences over the GPU's compute
+ * units; k > 0 cuts every sequence into k token ranges. */
+int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
+               const int32_t* positions, const void* kv_cache, int num_pages,
+               const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+               int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+               void* workspace, size_t ws_bytes, void* out, void* stream);
+
+/* Decode steps 1-3 of mla_decode ([formulas] eq. (12), (13); [walkthrough]
+ * step 3 and §3 顺序 B): q_abs[b][i] = [W_UK,i^T q^C_i | RoPE(q^R_i)] * scale,
+ * device [B][n_h][d_c + d_r] in cfg->dtype. */
+int mla_decode_query(const mla_config* cfg, const mla_weights* w, const void* h,
+                     const int32_t* positions, int B, const float* rope_table, int rope_len,
+                     void* workspace, size_t ws_bytes, void* q_abs, void* stream);
+
+/* Decode steps 4-7: latent_out[b][i] = sum_j softmax_j(q_abs[b][i] . row_j) c^KV_j
+ * over the cached rows j < kv_lens[b] (split over token ranges and merged by
+ * log-sum-exp).  q_abs: device [B][n_h][d_c + d_r]; latent_out: device
+ * [B][n_h][d_c], both cfg->dtype. */
+int mla_decode_attention(const mla_config* cfg, const void* q_abs, const void* kv_cache,
+                         int num_pages, const int32_t* page_table, int max_pages,
+                         const int32_t* kv_lens, int B, int max_kv_len, int num_splits,
+                         void* workspace, size_t ws_bytes, void* latent_out, void* stream);
+
+/* Decode steps 8-9 ([walkthrough] step 5 and §3 顺序 B): o_i = W_UV,i o~_i,
+ * out[b] = W_O [o_0 | ... | o_{n_h-1}].  latent_out: device [B][n_h][d_c];
+ * out: device [B][d]. */
+int mla_decode_output(const mla_config* cfg, const mla_weights* w, const void* latent_out,
+                      int B, void* workspace, size_t ws_bytes, void* out, void* stream);
+
+/* Prefill, order A ([walkthrough] §3 顺序 A and step 4): per head the cached
+ * rows are decompressed into k_j = [W_UK,i c^KV_j | k^R_j] and
+ * v_j = W_UV,i c^KV_j; query t (from h[t] at positions[t]) attends causally to
+ * rows 0..positions[t] of the one sequence described by page_table (device
+ * int32 [max_pages]) and kv_len; out: device [T][d].  Query rows with
+ * positions outside [0, kv_len) get NaN outputs. */
+int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
+                const int32_t* positions, const void* kv_cache, int num_pages,
+                const int32_t* page_table, int max_pages, int kv_len, int T,
+                const float* rope_table, int rope_len, void* workspace, size_t ws_bytes,
+                void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

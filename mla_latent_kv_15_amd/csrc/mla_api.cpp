@@ -1,0 +1,434 @@
+// Host side of the C ABI declared in include/mla.h: argument checks,
+// workspace carving and the stream-ordered launch sequence of each call.
+//
+// Layer steps and where the pages define them:
+//   write memory    c^KV = W_DKV h, k^R = RoPE(W_KR h)   eq. (9) of the formula
+//                   page; walkthrough §1 step 1
+//   query side      c^Q = W_DQ h, q^C = W_UQ c^Q,        eq. (12), (13); step 3
+//                   q^R = RoPE(W_QR c^Q)
+//   absorption      q~_i = W_UK,i^T q^C_i (order B)      walkthrough §3 顺序 B
+//   attention       softmax over [c^KV | k^R] rows       step 4, §3
+//   integrate       o_i = W_UV,i o~_i, u = W_O [o_i]     step 5, §3
+#include <math.h>
+#include <string.h>
+
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += al(bytes);
+    return p;
+  }
+};
+
+bool resolve(const mla_config* cfg, Geo* g) {
+  if (!cfg) return false;
+  if (cfg->d <= 0 || cfg->n_h <= 0 || cfg->d_h <= 0 || cfg->d_c <= 0 || cfg->d_cq <= 0 ||
+      cfg->d_r <= 0 || (cfg->d_r & 1) || cfg->page_size <= 0)
+    return false;
+  if (cfg->dtype != MLA_F32 && cfg->dtype != MLA_BF16) return false;
+  g->d = cfg->d;
+  g->n_h = cfg->n_h;
+  g->d_h = cfg->d_h;
+  g->d_c = cfg->d_c;
+  g->d_cq = cfg->d_cq;
+  g->d_r = cfg->d_r;
+  g->page = cfg->page_size;
+  g->row = cfg->d_c + cfg->d_r;
+  g->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale
+                                      : (float)(1.0 / sqrt((double)(cfg->d_h + cfg->d_r)));
+  g->base = cfg->rope_base > 0.0 ? cfg->rope_base : 10000.0;
+  g->bf16 = cfg->dtype == MLA_BF16;
+  return true;
+}
+
+// The generic kernels hold per-thread accumulators for d_c <= 1024 and d_h <= 512.
+bool generic_ok(const Geo& g) { return g.d_c <= 1024 && g.d_h <= 512; }
+
+GType st(const Geo& g) { return g.bf16 ? G_BF16 : G_F32; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+#define MLA_TRY(expr)                         \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return MLA_ERR_HIP; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+// ---------------------------------------------------------------------------
+struct QueryWs {
+  float *cq, *qc, *qr;
+};
+void carve_query(Carver& c, const Geo& g, int B, QueryWs* w) {
+  w->cq = (float*)c.take(sizeof(float) * (size_t)B * g.d_cq);
+  w->qc = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_h);
+  w->qr = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_r);
+}
+
+struct AttnWs {
+  void* plan;
+  float *part_o, *part_ml;
+  int max_segs, max_wg;
+};
+void carve_attn(Carver& c, const Geo& g, int B, int num_splits, AttnWs* w) {
+  PlanDims pd = plan_dims(B, num_splits);
+  w->max_segs = pd.max_segs;
+  w->max_wg = pd.max_wg;
+  w->plan = c.take(plan_bytes(B, num_splits));
+  w->part_o = (float*)c.take(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_c);
+  w->part_ml = (float*)c.take(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
+}
+
+struct OutWs {
+  float* o;
+};
+void carve_out(Carver& c, const Geo& g, int B, OutWs* w) {
+  w->o = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_h);
+}
+
+struct DecodeWs {
+  void *q_abs, *lat;
+  size_t sub_off;
+};
+
+struct PrefillWs {
+  float *cq, *q, *rows, *kbuf, *vbuf, *o;
+};
+void carve_prefill(Carver& c, const Geo& g, int T, int kv_len, PrefillWs* w) {
+  size_t wq = (size_t)g.n_h * (g.d_h + g.d_r);
+  w->cq = (float*)c.take(sizeof(float) * (size_t)T * g.d_cq);
+  w->q = (float*)c.take(sizeof(float) * (size_t)T * wq);
+  w->rows = (float*)c.take(sizeof(float) * (size_t)kv_len * g.row);
+  w->kbuf = (float*)c.take(sizeof(float) * (size_t)kv_len * wq);
+  w->vbuf = (float*)c.take(sizeof(float) * (size_t)kv_len * g.n_h * g.d_h);
+  w->o = (float*)c.take(sizeof(float) * (size_t)T * g.n_h * g.d_h);
+}
+
+size_t ws_query(const Geo& g, int B) {
+  Carver c(nullptr);
+  QueryWs w;
+  carve_query(c, g, B, &w);
+  return c.used;
+}
+size_t ws_attn(const Geo& g, int B, int ns) {
+  Carver c(nullptr);
+  AttnWs w;
+  carve_attn(c, g, B, ns, &w);
+  return c.used;
+}
+size_t ws_out(const Geo& g, int B) {
+  Carver c(nullptr);
+  OutWs w;
+  carve_out(c, g, B, &w);
+  return c.used;
+}
+size_t ws_decode_head(const Geo& g, int B) {
+  return al((size_t)B * g.n_h * g.row * g.esize()) + al((size_t)B * g.n_h * g.d_c * g.esize());
+}
+size_t ws_decode(const Geo& g, int B, int ns) {
+  size_t sub = ws_query(g, B);
+  size_t a = ws_attn(g, B, ns), o = ws_out(g, B);
+  if (a > sub) sub = a;
+  if (o > sub) sub = o;
+  return ws_decode_head(g, B) + sub;
+}
+size_t ws_append(const Geo& g, int T) { return al(sizeof(float) * (size_t)T * g.row); }
+size_t ws_prefill(const Geo& g, int T, int kv_len) {
+  Carver c(nullptr);
+  PrefillWs w;
+  carve_prefill(c, g, T, kv_len, &w);
+  return c.used;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MLA_OK;
+  if (!ws || ((uintptr_t)ws & (kAlign - 1)) || have < need) return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// step implementations (arguments already checked)
+// ---------------------------------------------------------------------------
+int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* positions, int B,
+              const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s) {
+  Carver c(ws);
+  QueryWs q;
+  carve_query(c, g, B, &q);
+  const GType T = st(g);
+  // c^Q = W_DQ h  (eq. (12))
+  MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, q.cq,
+                       g.d_cq, 0, 1, 1.f, s));
+  // q^C = W_UQ c^Q (eq. (13)) and the per-head RoPE query input W_QR c^Q
+  MLA_TRY(gemm_generic(G_F32, T, G_F32, false, B, g.n_h * g.d_h, g.d_cq, q.cq, g.d_cq, 0, w->W_UQ,
+                       g.d_cq, 0, q.qc, (long)g.n_h * g.d_h, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, T, G_F32, false, B, g.n_h * g.d_r, g.d_cq, q.cq, g.d_cq, 0, w->W_QR,
+                       g.d_cq, 0, q.qr, (long)g.n_h * g.d_r, 0, 1, 1.f, s));
+  // absorbed query q~_i = W_UK,i^T q^C_i, scaled (order B)
+  MLA_TRY(gemm_generic(G_F32, T, T, true, B, g.d_c, g.d_h, q.qc, (long)g.n_h * g.d_h, g.d_h,
+                       w->W_UK, g.d_c, (long)g.d_h * g.d_c, q_abs, (long)g.n_h * g.row, g.row,
+                       g.n_h, g.scale, s));
+  // RoPE(q^R_i), scaled, packed after q~_i
+  MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
+  return MLA_OK;
+}
+
+int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+                  const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+                  int max_kv_len, int num_splits, void* ws, void* lat, hipStream_t s) {
+  Carver c(ws);
+  AttnWs a;
+  carve_attn(c, g, B, num_splits, &a);
+  PlanPtrs plan;
+  carve_plan(a.plan, B, num_splits, &plan);
+  const bool fast = is_v2_fast(g);
+  MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
+  if (fast) {
+    MLA_TRY(attn_decode_v2(g, q_abs, cache, num_pages, page_table, max_pages, plan, a.max_wg,
+                           a.part_o, a.part_ml, lat, s));
+  } else {
+    MLA_TRY(attn_decode_generic(g, q_abs, cache, num_pages, page_table, max_pages, plan,
+                                a.max_segs, a.part_o, a.part_ml, lat, s));
+  }
+  MLA_TRY(combine_partials(g, plan, B, a.part_o, a.part_ml, lat, s));
+  return MLA_OK;
+}
+
+int run_output(const Geo& g, const mla_weights* w, const void* lat, int B, void* ws, void* out,
+               hipStream_t s) {
+  Carver c(ws);
+  OutWs o;
+  carve_out(c, g, B, &o);
+  const GType T = st(g);
+  // o_i = W_UV,i o~_i
+  MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_h, g.d_c, lat, (long)g.n_h * g.d_c, g.d_c,
+                       w->W_UV, g.d_c, (long)g.d_h * g.d_c, o.o, (long)g.n_h * g.d_h, g.d_h, g.n_h,
+                       1.f, s));
+  // u = W_O [o_0 | ... | o_{n_h-1}]
+  MLA_TRY(gemm_generic(G_F32, T, T, false, B, g.d, g.n_h * g.d_h, o.o, (long)g.n_h * g.d_h, 0,
+                       w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1, 1.f, s));
+  return MLA_OK;
+}
+
+bool weights_ok(const mla_weights* w, bool query, bool output, bool append, bool kv) {
+  if (!w) return false;
+  if (query && (!w->W_DQ || !w->W_UQ || !w->W_QR || !w->W_UK)) return false;
+  if (output && (!w->W_UV || !w->W_O)) return false;
+  if (append && (!w->W_DKV || !w->W_KR)) return false;
+  if (kv && (!w->W_UK || !w->W_UV)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MLA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_version(void) { return 100; }
+
+int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || max_pos <= 0 || !d_table) return MLA_ERR_INVALID_ARG;
+  return hip_status(rope_table_fill(d_table, max_pos, g.d_r, g.base, (hipStream_t)stream));
+}
+
+size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_len,
+                          int num_splits) {
+  Geo g;
+  if (!resolve(cfg, &g) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
+  switch (op) {
+    case MLA_OP_APPEND: return ws_append(g, batch);
+    case MLA_OP_DECODE: return ws_decode(g, batch, num_splits);
+    case MLA_OP_PREFILL: return ws_prefill(g, batch, max_kv_len);
+    case MLA_OP_DECODE_QUERY: return ws_query(g, batch);
+    case MLA_OP_DECODE_ATTENTION: return ws_attn(g, batch, num_splits);
+    case MLA_OP_DECODE_OUTPUT: return ws_out(g, batch);
+    default: return 0;
+  }
+}
+
+int mla_append_kv(const mla_config* cfg, const mla_weights* w, const void* h,
+                  const int32_t* positions, const int32_t* slot_mapping, int T,
+                  const float* rope_table, int rope_len, void* kv_cache, int num_pages,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, false, false, true, false) || T < 0 || num_pages < 0 ||
+      rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!h || !positions || !slot_mapping || !rope_table || !kv_cache || num_pages == 0 ||
+      rope_len == 0)
+    return MLA_ERR_INVALID_ARG;
+  int r = check_ws(workspace, ws_bytes, ws_append(g, T));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  float* y = (float*)workspace;
+  const GType Ty = st(g);
+  // c^KV_t = W_DKV h_t into columns [0, d_c); W_KR h_t into [d_c, d_c + d_r)
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_c, g.d, h, g.d, 0, w->W_DKV, g.d, 0, y, g.row,
+                       0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_r, g.d, h, g.d, 0, w->W_KR, g.d, 0,
+                       y + g.d_c, g.row, 0, 1, 1.f, s));
+  MLA_TRY(append_finish(g, y, positions, slot_mapping, T, rope_table, rope_len, kv_cache,
+                        num_pages, s));
+  return MLA_OK;
+}
+
+int mla_decode_query(const mla_config* cfg, const mla_weights* w, const void* h,
+                     const int32_t* positions, int B, const float* rope_table, int rope_len,
+                     void* workspace, size_t ws_bytes, void* q_abs, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, true, false, false, false) || B < 0 || rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!h || !positions || !rope_table || rope_len == 0 || !q_abs) return MLA_ERR_INVALID_ARG;
+  int r = check_ws(workspace, ws_bytes, ws_query(g, B));
+  if (r) return r;
+  return run_query(g, w, h, positions, B, rope_table, rope_len, workspace, q_abs,
+                   (hipStream_t)stream);
+}
+
+static int check_attn_args(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+                           const int32_t* page_table, int max_pages, const int32_t* kv_lens,
+                           int B, int max_kv_len, int num_splits) {
+  if (B < 0 || num_pages < 0 || max_pages < 0 || max_kv_len < 0 || num_splits < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q_abs || !cache || !page_table || !kv_lens || num_pages == 0 || max_pages == 0 ||
+      max_kv_len == 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((long)max_kv_len > (long)max_pages * g.page) return MLA_ERR_INVALID_ARG;
+  if (num_splits > 4096) return MLA_ERR_INVALID_ARG;
+  if (!is_v2_fast(g) && !generic_ok(g)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int mla_decode_attention(const mla_config* cfg, const void* q_abs, const void* kv_cache,
+                         int num_pages, const int32_t* page_table, int max_pages,
+                         const int32_t* kv_lens, int B, int max_kv_len, int num_splits,
+                         void* workspace, size_t ws_bytes, void* latent_out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g)) return MLA_ERR_INVALID_ARG;
+  int r = check_attn_args(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B,
+                          max_kv_len, num_splits);
+  if (r || B == 0) return r;
+  if (!latent_out) return MLA_ERR_INVALID_ARG;
+  r = check_ws(workspace, ws_bytes, ws_attn(g, B, num_splits));
+  if (r) return r;
+  return run_attention(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B,
+                       max_kv_len, num_splits, workspace, latent_out, (hipStream_t)stream);
+}
+
+int mla_decode_output(const mla_config* cfg, const mla_weights* w, const void* latent_out, int B,
+                      void* workspace, size_t ws_bytes, void* out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, false, true, false, false) || B < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!latent_out || !out) return MLA_ERR_INVALID_ARG;
+  int r = check_ws(workspace, ws_bytes, ws_out(g, B));
+  if (r) return r;
+  return run_output(g, w, latent_out, B, workspace, out, (hipStream_t)stream);
+}
+
+int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
+               const int32_t* positions, const void* kv_cache, int num_pages,
+               const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+               int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+               void* workspace, size_t ws_bytes, void* out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, false) || rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  // q_abs stands in for the (not yet computed) absorbed query in the checks
+  int r = check_attn_args(g, h, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
+                          num_splits);
+  if (r || B == 0) return r;
+  if (!h || !positions || !rope_table || rope_len == 0 || !out) return MLA_ERR_INVALID_ARG;
+  r = check_ws(workspace, ws_bytes, ws_decode(g, B, num_splits));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  void* q_abs = c.take((size_t)B * g.n_h * g.row * g.esize());
+  void* lat = c.take((size_t)B * g.n_h * g.d_c * g.esize());
+  void* sub = c.base + c.used;
+  r = run_query(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s);
+  if (r) return r;
+  r = run_attention(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
+                    num_splits, sub, lat, s);
+  if (r) return r;
+  return run_output(g, w, lat, B, sub, out, s);
+}
+
+int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
+                const int32_t* positions, const void* kv_cache, int num_pages,
+                const int32_t* page_table, int max_pages, int kv_len, int T,
+                const float* rope_table, int rope_len, void* workspace, size_t ws_bytes,
+                void* out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, true) || T < 0 || kv_len < 0 ||
+      num_pages < 0 || max_pages < 0 || rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!h || !positions || !kv_cache || !page_table || !rope_table || !out || kv_len == 0 ||
+      num_pages == 0 || rope_len == 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((long)kv_len > (long)max_pages * g.page) return MLA_ERR_INVALID_ARG;
+  if (!generic_ok(g)) return MLA_ERR_UNSUPPORTED;
+  int r = check_ws(workspace, ws_bytes, ws_prefill(g, T, kv_len));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  PrefillWs p;
+  carve_prefill(c, g, T, kv_len, &p);
+  const GType Ty = st(g);
+  const long wq = (long)g.n_h * (g.d_h + g.d_r);
+  // query: c^Q, then per head [q^C_i | q^R_i] (192-d at V2), RoPE on q^R
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, p.cq,
+                       g.d_cq, 0, 1, 1.f, s));
+  // (the softmax scale is folded into q; RoPE is linear, so rotating the
+  // scaled q^R equals scaling the rotated one)
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, T, g.d_h, g.d_cq, p.cq, g.d_cq, 0, w->W_UQ,
+                       g.d_cq, (long)g.d_h * g.d_cq, p.q, wq, g.d_h + g.d_r, g.n_h, g.scale, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, T, g.d_r, g.d_cq, p.cq, g.d_cq, 0, w->W_QR,
+                       g.d_cq, (long)g.d_r * g.d_cq, p.q + g.d_h, wq, g.d_h + g.d_r, g.n_h,
+                       g.scale, s));
+  MLA_TRY(rope_inplace_heads(g, p.q, T, wq, g.d_h, positions, rope_table, rope_len, s));
+  // order A: decompress k_j = [W_UK,i c_j | k^R_j] and v_j = W_UV,i c_j per head
+  MLA_TRY(gather_rows_f32(g, kv_cache, num_pages, page_table, max_pages, kv_len, p.rows, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, kv_len, g.d_h, g.d_c, p.rows, g.row, 0, w->W_UK,
+                       g.d_c, (long)g.d_h * g.d_c, p.kbuf, wq, g.d_h + g.d_r, g.n_h, 1.f, s));
+  MLA_TRY(broadcast_kr(g, p.rows, kv_len, p.kbuf, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, kv_len, g.d_h, g.d_c, p.rows, g.row, 0, w->W_UV,
+                       g.d_c, (long)g.d_h * g.d_c, p.vbuf, (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f,
+                       s));
+  // causal softmax attention with 192-d scores and 128-d values, then W_O
+  MLA_TRY(attn_prefill_generic(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, rope_len, p.o, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, Ty, false, T, g.d, g.n_h * g.d_h, p.o, (long)g.n_h * g.d_h, 0,
+                       w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1, 1.f, s));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the host API and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// Resolved layer geometry (defaults applied).
+struct Geo {
+  int d, n_h, d_h, d_c, d_cq, d_r, page;
+  int row;        // d_c + d_r: numbers cached per token
+  float scale;    // softmax scale
+  double base;    // RoPE base
+  bool bf16;      // storage dtype
+  int esize() const { return bf16 ? 2 : 4; }
+};
+
+// The DeepSeek-V2 decode shape served by the MFMA kernels.
+constexpr bool kHaveV2Attention = false;
+inline bool is_v2_fast(const Geo& g) {
+  return kHaveV2Attention && g.bf16 && g.n_h == 128 && g.d_c == 512 && g.d_r == 64 && g.d_h == 128 &&
+         g.page % 64 == 0 && g.d % 256 == 0 && g.d_cq % 256 == 0;
+}
+
+// ---------------------------------------------------------------------------
+// split-KV plan (device arrays carved from the workspace)
+// ---------------------------------------------------------------------------
+struct Seg {
+  int b;    // sequence
+  int t0;   // first token
+  int t1;   // one past the last token
+  int pad;
+};
+
+struct PlanPtrs {
+  Seg* segs;            // [max_segs]
+  int* seq_seg_start;   // [B]
+  int* seq_seg_count;   // [B]; 0 marks an invalid sequence (NaN output)
+  int* wg_seg_start;    // [max_wg + 1]
+  int* counts;          // [0] = segments, [1] = work-groups in use
+};
+
+struct PlanDims {
+  int max_segs;
+  int max_wg;
+};
+
+// Work-group budget of the auto split mode for this device.
+int auto_wg_budget();
+PlanDims plan_dims(int B, int num_splits);
+size_t plan_bytes(int B, int num_splits);
+void carve_plan(void* base, int B, int num_splits, PlanPtrs* p);
+hipError_t launch_plan(const PlanPtrs& p, const int32_t* kv_lens, int B, int max_kv_len,
+                       int max_pages, int page, int tile, int num_splits, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// generic kernels (any geometry, fp32 or bf16 storage)
+// ---------------------------------------------------------------------------
+enum GType { G_F32 = 0, G_BF16 = 1 };
+
+// C[z][m][n] = alpha * sum_k A[z][m][k] * B[z](n, k); B(n,k) = B[n*ldb+k] or
+// B[k*ldb+n] when b_kmajor.  Types are element types of A, B, C.
+hipError_t gemm_generic(GType ta, GType tb, GType tc, bool b_kmajor, int M, int N, int K,
+                        const void* A, long lda, long sA, const void* B, long ldb, long sB,
+                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s);
+
+hipError_t rope_table_fill(float* table, int max_pos, int d_r, double base, hipStream_t s);
+
+// q_abs[b][i][d_c + k] = RoPE(q_r[b][i][k]) * scale (fp32 source), storage out.
+hipError_t pack_query_rope(const Geo& g, const float* q_r, const int32_t* positions, int B,
+                           const float* rope, int rope_len, void* q_abs, hipStream_t s);
+
+// Order-B attention core over the paged cache (generic), one WG per (segment, head).
+hipError_t attn_decode_generic(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+                               const int32_t* page_table, int max_pages, const PlanPtrs& plan,
+                               int max_segs, float* part_o, float* part_ml, void* lat_out,
+                               hipStream_t s);
+
+// Merge split partials; sequences with one segment were written directly.
+hipError_t combine_partials(const Geo& g, const PlanPtrs& plan, int B, const float* part_o,
+                            const float* part_ml, void* lat_out, hipStream_t s);
+
+// Append: rotate + round + scatter rows of y [T][row] fp32.
+hipError_t append_finish(const Geo& g, const float* y, const int32_t* positions,
+                         const int32_t* slots, int T, const float* rope, int rope_len,
+                         void* cache, int num_pages, hipStream_t s);
+
+// Prefill helpers (generic, fp32 intermediates).
+hipError_t gather_rows_f32(const Geo& g, const void* cache, int num_pages, const int32_t* page_table,
+                           int max_pages, int kv_len, float* rows, hipStream_t s);
+hipError_t broadcast_kr(const Geo& g, const float* rows, int kv_len, float* kbuf, hipStream_t s);
+hipError_t rope_inplace_heads(const Geo& g, float* q, int T, long ld_row, int off,
+                              const int32_t* positions, const float* rope, int rope_len,
+                              hipStream_t s);
+hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
+                                const float* vbuf, const int32_t* positions, int T, int kv_len,
+                                int rope_len, float* o, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// MFMA kernels for the V2 bf16 shape
+// ---------------------------------------------------------------------------
+hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+                          const int32_t* page_table, int max_pages, const PlanPtrs& plan,
+                          int n_wg_launch, float* part_o, float* part_ml, void* lat_out,
+                          hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_15_amd import inputs, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        from mla_latent_kv_15_amd import build
+        build.build()
+    return lib.load()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _header_functions()
+    assert "mla_decode" in names and "mla_append_kv" in names and "mla_prefill" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib._SIGS)
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.status_string(code)
+    assert lib.status_string(7) == "unknown status"
+    assert L.mla_version() >= 100
+
+
+def _cfg(shape=inputs.V2, dtype="bf16", page=64):
+    return lib.make_config(shape, page, dtype)
+
+
+def test_workspace_sizes(L):
+    c = _cfg()
+    assert lib.workspace_size(c, lib.OP_APPEND, 10) == ((10 * 576 * 4 + 255) // 256) * 256
+    d1 = lib.workspace_size(c, lib.OP_DECODE, 64, 8193, 0)
+    d2 = lib.workspace_size(c, lib.OP_DECODE, 64, 8193, 4)
+    assert d1 > 0 and d2 > 0
+    assert lib.workspace_size(c, lib.OP_DECODE_QUERY, 1) > 0
+    assert lib.workspace_size(c, lib.OP_PREFILL, 4096, 4096) > 4096 * 128 * 192 * 4
+    bad = _cfg()
+    bad.d_r = 63
+    assert lib.workspace_size(bad, lib.OP_DECODE, 1, 1, 0) == 0
+    assert lib.workspace_size(c, 99, 1, 1, 0) == 0
+
+
+def test_invalid_arguments_rejected_before_launch(L):
+    c = _cfg()
+    w = lib.Weights(*([None] * 8))
+    z = ctypes.c_void_p(0)
+    # null config / null weights
+    assert L.mla_decode(None, None, z, z, z, 1, z, 1, z, 1, 1, z, 1, 0, z, 0, z, z) == lib.MLA_ERR_INVALID_ARG
+    assert L.mla_decode(ctypes.byref(c), ctypes.byref(w), z, z, z, 1, z, 1, z, 1, 1, z, 1, 0, z, 0,
+                        z, z) == lib.MLA_ERR_INVALID_ARG
+    # bad geometry
+    for field, val in (("d_r", 7), ("n_h", 0), ("page_size", 0), ("dtype", 5)):
+        b = _cfg()
+        setattr(b, field, val)
+        assert L.mla_rope_table_init(ctypes.byref(b), 10, ctypes.c_void_p(256), None) == lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_table_init(ctypes.byref(c), 0, ctypes.c_void_p(256), None) == lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_table_init(ctypes.byref(c), 10, None, None) == lib.MLA_ERR_INVALID_ARG
+    # fake non-null device pointers: validation must fail before they are used
+    p = ctypes.c_void_p(4096)
+    # max_kv_len beyond the page table's reach
+    assert L.mla_decode_attention(ctypes.byref(c), p, p, 4, p, 2, p, 1, 129, 0, p, 1 << 30, p,
+                                  None) == lib.MLA_ERR_INVALID_ARG
+    # negative sizes
+    assert L.mla_decode_attention(ctypes.byref(c), p, p, 4, p, 2, p, -1, 10, 0, p, 1 << 30, p,
+                                  None) == lib.MLA_ERR_INVALID_ARG
+    # workspace too small / misaligned
+    assert L.mla_decode_attention(ctypes.byref(c), p, p, 4, p, 2, p, 1, 100, 0, p, 16, p,
+                                  None) == lib.MLA_ERR_WORKSPACE
+    assert L.mla_decode_attention(ctypes.byref(c), p, p, 4, p, 2, p, 1, 100, 0,
+                                  ctypes.c_void_p(4096 + 8), 1 << 40, p, None) == lib.MLA_ERR_WORKSPACE
+    # unsupported: a latent too wide for the generic kernels
+    u = lib.make_config(inputs.Shape(d=64, n_h=4, d_h=16, d_c=2048, d_cq=48, d_r=8), 64, "f32")
+    assert L.mla_decode_attention(ctypes.byref(u), p, p, 4, p, 2, p, 1, 100, 0, p, 1 << 40, p,
+                                  None) == lib.MLA_ERR_UNSUPPORTED
+    # append: missing weights, zero pages
+    assert L.mla_append_kv(ctypes.byref(c), ctypes.byref(w), p, p, p, 3, p, 10, p, 1, p, 1 << 30,
+                           None) == lib.MLA_ERR_INVALID_ARG
+    wf = lib.Weights(*([4096] * 8))
+    assert L.mla_append_kv(ctypes.byref(c), ctypes.byref(wf), p, p, p, 3, p, 10, p, 0, p, 1 << 30,
+                           None) == lib.MLA_ERR_INVALID_ARG
+    # prefill: kv_len beyond the page table
+    assert L.mla_prefill(ctypes.byref(c), ctypes.byref(wf), p, p, p, 8, p, 1, 65, 4, p, 100, p,
+                         1 << 40, p, None) == lib.MLA_ERR_INVALID_ARG
+
+
+def test_empty_batches_are_noops(L):
+    c = _cfg()
+    wf = lib.Weights(*([4096] * 8))
+    z = None
+    assert L.mla_append_kv(ctypes.byref(c), ctypes.byref(wf), z, z, z, 0, z, 0, z, 0, z, 0, z) == 0
+    assert L.mla_decode_attention(ctypes.byref(c), z, z, 0, z, 0, z, 0, 0, 0, z, 0, z, z) == 0
+    assert L.mla_decode_output(ctypes.byref(c), ctypes.byref(wf), z, 0, z, 0, z, z) == 0
+    assert L.mla_prefill(ctypes.byref(c), ctypes.byref(wf), z, z, z, 0, z, 0, 0, 0, z, 0, z, 0, z,
+                         z) == 0

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Inputs are seeded and synthetic (hidden states N(0,1), weights N(0,1/fan_in),
+cache rows N(0,1)); the oracle receives the same values widened to fp64.
+Tolerance: max relative error per output vector (oracle.max_rel_error),
+1e-4 for fp32 storage and 2e-2 for bf16 storage with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_15_amd import device, inputs
+from tests.gpu_helpers import BASE, TOL, Layer, cache_from_rows, log, require_lib
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_lib()
+
+
+def _append_sequence(layer, H: inputs.Array, paged: inputs.Paged, rope):
+    """Append one sequence's rows at positions 0..N-1 through mla_append_kv."""
+    N = H.shape[0]
+    cache = layer.empty_cache(paged.num_pages)
+    layer.append(device.tensor(H), np.arange(N), paged.slots(0), cache, rope)
+    return cache
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 layer: append + decode against order A and the brute force
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("page,shuffle", [(64, False), (4, True)])
+def test_tiny_fp32_append_decode(page, shuffle):
+    s = inputs.TINY
+    layer = Layer(s, 1, "f32", page=page)
+    N = 17
+    H = inputs.make_hidden(N, s, 1, "f32")
+    paged = inputs.make_paged([N], page, 1, shuffle=shuffle)
+    rope = layer.rope(64)
+    log(f"tiny fp32 page={page}")
+    cache = _append_sequence(layer, H, paged, rope)
+    out = layer.decode(device.tensor(inputs.Array(H.f32[-1:], "f32")), [N - 1], cache,
+                       paged.page_table, [N], N, rope)
+    torch.cuda.synchronize()
+    u = device.to_f64(out)[0]
+    ref = oracle.decode_from_hidden(H.f64(), layer.W64, s.n_h, BASE, order="A")
+    bf = oracle.decode_bruteforce(H.f64(), layer.W64, s.n_h, BASE, oracle.default_scale(s.d_h, s.d_r))
+    assert oracle.max_rel_error(u, ref) < TOL["f32"]
+    assert oracle.max_rel_error(u, bf) < TOL["f32"]
+    # the cached rows themselves
+    c, kr = oracle.latent_rows(H.f64(), layer.W64["W_DKV"], layer.W64["W_KR"], np.arange(N), BASE)
+    rows = device.to_f64(cache).reshape(-1, s.row)[paged.slots(0)]
+    assert oracle.max_rel_error(rows, np.concatenate([c, kr], 1)) < 1e-5
+
+
+def test_tiny_fp32_steps():
+    """Each decode step on its own, fed with synthetic inputs of its own."""
+    s = inputs.TINY
+    layer = Layer(s, 11, "f32", page=8)
+    B = 3
+    Hq = inputs.make_hidden(B, s, 11, "f32")
+    pos = np.array([0, 5, 40], np.int32)
+    rope = layer.rope(64)
+    log("tiny fp32 decode_query")
+    q = device.to_f64(layer.decode_query(device.tensor(Hq), pos, rope))
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    for b in range(B):
+        q_c, q_r = oracle.query(Hq.f64()[b], layer.W64["W_DQ"], layer.W64["W_UQ"], layer.W64["W_QR"],
+                                int(pos[b]), s.n_h, BASE)
+        ref = oracle.absorbed_query(q_c, q_r, layer.W64["W_UK"], sc)
+        assert oracle.max_rel_error(q[b], ref) < TOL["f32"]
+    log("tiny fp32 decode_attention")
+    lens = np.array([1, 9, 30], np.int32)
+    paged = inputs.make_paged(lens, 8, 11, shuffle=True)
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 11, "f32")
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    cache = cache_from_rows(layer, rows, paged, offs)
+    qa = inputs.Array(inputs.normal((B, s.n_h, s.row), 0.3, 11, inputs.STREAM_QUERY), "f32")
+    lat = device.to_f64(layer.decode_attention(device.tensor(qa), cache, paged.page_table, lens, 30))
+    for b in range(B):
+        r = rows.f64()[offs[b]:offs[b] + lens[b]]
+        assert oracle.max_rel_error(lat[b], oracle.latent_attention(qa.f64()[b], r, s.d_c)) < TOL["f32"]
+    log("tiny fp32 decode_output")
+    la = inputs.Array(inputs.normal((B, s.n_h, s.d_c), 1.0, 11, inputs.STREAM_QUERY, 1), "f32")
+    u = device.to_f64(layer.decode_output(device.tensor(la)))
+    for b in range(B):
+        ref = oracle.latent_output(la.f64()[b], layer.W64["W_UV"], layer.W64["W_O"])
+        assert oracle.max_rel_error(u[b], ref) < TOL["f32"]
+
+
+# ---------------------------------------------------------------------------
+# V2 layer, batch 1 over 4096 cached tokens, cache built by mla_append_kv
+# ---------------------------------------------------------------------------
+
+def test_v2_batch1_append_decode():
+    s = inputs.V2
+    layer = Layer(s, 2, "bf16")
+    L = 4096
+    N = L + 1
+    H = inputs.make_hidden(N, s, 2, "bf16")
+    paged = inputs.make_paged([N], 64, 2, shuffle=False)
+    rope = layer.rope(N)
+    log("v2 batch1: append 4097 rows")
+    cache = _append_sequence(layer, H, paged, rope)
+    log("v2 batch1: decode")
+    hq = device.tensor(inputs.Array(H.f32[-1:], "bf16"))
+    out = layer.decode(hq, [L], cache, paged.page_table, [N], N, rope)
+    torch.cuda.synchronize()
+    u = device.to_f64(out)[0]
+    log("v2 batch1: oracle order A")
+    ref = oracle.decode_from_hidden(H.f64(), layer.W64, s.n_h, BASE, order="A")
+    err = oracle.max_rel_error(u, ref)
+    log(f"v2 batch1 max rel err {err:.3e}")
+    assert err < TOL["bf16"]
+    # the appended rows (bf16 rounding of the exact rows)
+    c, kr = oracle.latent_rows(H.f64()[:256], layer.W64["W_DKV"], layer.W64["W_KR"], np.arange(256), BASE)
+    rows = device.to_f64(cache).reshape(-1, s.row)[paged.slots(0)[:256]]
+    assert oracle.max_rel_error(rows, np.concatenate([c, kr], 1)) < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# V2 layer, batch 64, lengths U[1024, 8192], shuffled 64-token pages
+# ---------------------------------------------------------------------------
+
+def _batch_case(cid, B, lo, hi, s=inputs.V2):
+    L = inputs.make_lengths(B, lo, hi, cid)
+    kv = (L + 1).astype(np.int32)
+    paged = inputs.make_paged(kv, 64, cid, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(kv)[:-1]]).astype(np.int64)
+    rows = inputs.make_cache_rows(int(kv.sum()), s, cid, "bf16")
+    return L, kv, paged, offs, rows
+
+
+def _oracle_order_b(layer, hq64, pos, rows64):
+    s = layer.shape
+    q_c, q_r = oracle.query(hq64, layer.W64["W_DQ"], layer.W64["W_UQ"], layer.W64["W_QR"], pos, s.n_h, BASE)
+    Qt = oracle.absorbed_query(q_c, q_r, layer.W64["W_UK"], oracle.default_scale(s.d_h, s.d_r))
+    lat = oracle.latent_attention(Qt, rows64, s.d_c)
+    return oracle.latent_output(lat, layer.W64["W_UV"], layer.W64["W_O"])
+
+
+def test_v2_batch64_paged():
+    s = inputs.V2
+    layer = Layer(s, 3, "bf16")
+    B = 64
+    L, kv, paged, offs, rows = _batch_case(3, B, 1024, 8192)
+    log(f"v2 batch64: {int(kv.sum())} cached rows, {paged.num_pages} pages")
+    cache = cache_from_rows(layer, rows, paged, offs)
+    Hq = inputs.make_hidden(B, s, 3, "bf16")
+    rope = layer.rope(int(kv.max()) + 1)
+    out = layer.decode(device.tensor(Hq), L, cache, paged.page_table, kv, int(kv.max()), rope)
+    torch.cuda.synchronize()
+    u = device.to_f64(out)
+    r64 = rows.f64()
+    worst = 0.0
+    for b in range(B):
+        ref = _oracle_order_b(layer, Hq.f64()[b], int(L[b]), r64[offs[b]:offs[b] + kv[b]])
+        worst = max(worst, oracle.max_rel_error(u[b], ref))
+    log(f"v2 batch64 worst rel err {worst:.3e}")
+    assert worst < TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# V2 layer, batch 4 at 131072 tokens: 4096-token prefix against order A,
+# full length against order B and the uniform-attention closed form
+# ---------------------------------------------------------------------------
+
+def test_v2_long_context():
+    s = inputs.V2
+    layer = Layer(s, 4, "bf16")
+    B, Lfull = 4, 131072
+    kv_full = np.full(B, Lfull + 1, np.int32)
+    paged = inputs.make_paged(kv_full, 64, 4, shuffle=True)
+    offs = np.arange(B, dtype=np.int64) * (Lfull + 1)
+    log("v2 long: generating 524292 cache rows")
+    rows = inputs.make_cache_rows(int(kv_full.sum()), s, 4, "bf16")
+    cache = cache_from_rows(layer, rows, paged, offs)
+    Hq = inputs.make_hidden(B, s, 4, "bf16")
+    pos = np.full(B, Lfull, np.int32)
+    rope = layer.rope(Lfull + 1)
+    hq = device.tensor(Hq)
+    # prefix: kv_lens clipped to 4096, positions left at 131072
+    log("v2 long: prefix decode")
+    pre = 4096
+    u = device.to_f64(layer.decode(hq, pos, cache, paged.page_table, np.full(B, pre, np.int32),
+                                   Lfull + 1, rope))
+    r64 = rows.f64()
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    for b in range(B):
+        r = r64[offs[b]:offs[b] + pre]
+        q_c, q_r = oracle.query(Hq.f64()[b], layer.W64["W_DQ"], layer.W64["W_UQ"], layer.W64["W_QR"],
+                                Lfull, s.n_h, BASE)
+        if b < 2:
+            o = oracle.attend_order_a(q_c, q_r, r[:, :s.d_c], r[:, s.d_c:], layer.W64["W_UK"],
+                                      layer.W64["W_UV"], sc)
+            ref = oracle.integrate(o, layer.W64["W_O"])
+        else:
+            ref = _oracle_order_b(layer, Hq.f64()[b], Lfull, r)
+        err = oracle.max_rel_error(u[b], ref)
+        log(f"v2 long prefix seq {b}: {err:.3e}")
+        assert err < TOL["bf16"]
+    # full length, attention core, order B
+    log("v2 long: full-length decode_attention")
+    qa = layer.decode_query(hq, pos, rope)
+    q64 = device.to_f64(qa)
+    for ns in (0, 37):
+        lat = device.to_f64(layer.decode_attention(qa, cache, paged.page_table, kv_full, Lfull + 1, ns))
+        for b in range(B):
+            ref = oracle.latent_attention(q64[b], r64[offs[b]:offs[b] + Lfull + 1], s.d_c)
+            err = oracle.max_rel_error(lat[b], ref)
+            log(f"v2 long full seq {b} splits {ns}: {err:.3e}")
+            assert err < TOL["bf16"]
+    # closed form: zero query -> uniform weights -> plain mean of the latents
+    zq = torch.zeros_like(qa)
+    lat = device.to_f64(layer.decode_attention(zq, cache, paged.page_table, kv_full, Lfull + 1))
+    for b in range(B):
+        mean = r64[offs[b]:offs[b] + Lfull + 1, :s.d_c].mean(axis=0)
+        assert oracle.max_rel_error(lat[b], np.broadcast_to(mean, lat[b].shape)) < TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# V2 causal prefill (order A) of 4096 tokens, rows against the oracle and the
+# last 64 rows against mla_decode (order B) at kv_len = p + 1
+# ---------------------------------------------------------------------------
+
+def test_v2_prefill_4096():
+    s = inputs.V2
+    layer = Layer(s, 5, "bf16")
+    T = 4096
+    H = inputs.make_hidden(T, s, 5, "bf16")
+    paged = inputs.make_paged([T], 64, 5, shuffle=True)
+    rope = layer.rope(T)
+    log("v2 prefill: append")
+    cache = _append_sequence(layer, H, paged, rope)
+    h = device.tensor(H)
+    log("v2 prefill: prefill")
+    out = layer.prefill(h, np.arange(T), cache, paged.page_table[0], T, rope)
+    u = device.to_f64(out)
+    log("v2 prefill: decode cross-check on the last 64 positions")
+    P = np.arange(T - 64, T)
+    dec = layer.decode(h[T - 64:], P, cache, np.repeat(paged.page_table, 64, 0), P + 1, T, rope)
+    ud = device.to_f64(dec)
+    xerr = oracle.max_rel_error(u[T - 64:], ud)
+    log(f"prefill vs decode: {xerr:.3e}")
+    assert xerr < 2 * TOL["bf16"]
+    log("v2 prefill: oracle rows")
+    H64 = H.f64()
+    c, kr = oracle.latent_rows(H64, layer.W64["W_DKV"], layer.W64["W_KR"], np.arange(T), BASE)
+    sel = [0, 1, 63, 64, 65, 700, T - 1]
+    ref = oracle.prefill_order_a(H64, np.arange(T), c, kr, layer.W64, s.n_h, BASE, rows=sel)
+    err = oracle.max_rel_error(u[sel], ref)
+    log(f"prefill vs oracle: {err:.3e}")
+    assert err < TOL["bf16"]

@@ -1,0 +1,121 @@
+"""GPU structural checks: paging and indexing bit-exact, kv_len edges, split
+invariance, append slot discipline, invalid device indices."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_15_amd import device, inputs
+from tests.gpu_helpers import TOL, Layer, cache_from_rows, log, require_lib
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_lib()
+
+
+@pytest.fixture(scope="module")
+def v2():
+    return Layer(inputs.V2, 21, "bf16")
+
+
+def _rand_q(B, s, cid, std=1.0):
+    # |q~| of order 1 per element scaled like the real absorbed query
+    return inputs.Array(inputs.normal((B, s.n_h, s.row), std * 0.05, cid, inputs.STREAM_QUERY), "bf16")
+
+
+EDGE_LENS = [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097]
+
+
+def test_kv_len_edges_against_oracle(v2):
+    s = inputs.V2
+    lens = np.array(EDGE_LENS, np.int32)
+    B = len(lens)
+    paged = inputs.make_paged(lens, 64, 22, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 22, "bf16")
+    cache = cache_from_rows(v2, rows, paged, offs)
+    qa = _rand_q(B, s, 22)
+    for ns in (0, 1, 2, 7):
+        log(f"edges: splits {ns}")
+        lat = device.to_f64(v2.decode_attention(device.tensor(qa), cache, paged.page_table, lens,
+                                                int(lens.max()), ns))
+        r64 = rows.f64()
+        for b in range(B):
+            ref = oracle.latent_attention(qa.f64()[b], r64[offs[b]:offs[b] + lens[b]], s.d_c)
+            err = oracle.max_rel_error(lat[b], ref)
+            assert err < TOL["bf16"], (lens[b], ns, err)
+
+
+def test_page_permutation_bit_exact(v2):
+    """Same rows, different physical pages: bit-identical outputs."""
+    s = inputs.V2
+    lens = np.array([1, 64, 65, 700, 3000], np.int32)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 23, "bf16")
+    qa = device.tensor(_rand_q(len(lens), s, 23))
+    outs = []
+    for shuffle, extra in ((False, 0), (True, 0), (True, 9)):
+        paged = inputs.make_paged(lens, 64, 23 + extra, shuffle=shuffle, extra_pages=extra)
+        cache = cache_from_rows(v2, rows, paged, offs)
+        outs.append(v2.decode_attention(qa, cache, paged.page_table, lens, int(lens.max()), 0))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_split_invariance(v2):
+    s = inputs.V2
+    lens = np.array([5000, 130, 4097, 64], np.int32)
+    paged = inputs.make_paged(lens, 64, 24, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 24, "bf16")
+    cache = cache_from_rows(v2, rows, paged, offs)
+    qa = device.tensor(_rand_q(len(lens), s, 24))
+    base = device.to_f64(v2.decode_attention(qa, cache, paged.page_table, lens, 5000, 1))
+    for ns in (2, 7, 64, 0):
+        o = device.to_f64(v2.decode_attention(qa, cache, paged.page_table, lens, 5000, ns))
+        assert oracle.max_rel_error(o, base) < 1e-2
+
+
+def test_append_writes_only_its_slots():
+    s = inputs.TINY
+    layer = Layer(s, 25, "f32", page=4)
+    T = 6
+    H = inputs.make_hidden(T, s, 25, "f32")
+    num_pages = 5
+    cache = layer.empty_cache(num_pages, fill=-7.0)
+    slots = np.array([3, 4, 17, -1, 19, 10_000], np.int32)   # -1 and 10000 are not written
+    rope = layer.rope(32)
+    layer.append(device.tensor(H), np.arange(T), slots, cache, rope)
+    flat = device.to_f64(cache).reshape(-1, s.row)
+    written = {3, 4, 17, 19}
+    for slot in range(num_pages * 4):
+        if slot not in written:
+            assert np.all(flat[slot] == -7.0), slot
+    c, kr = oracle.latent_rows(H.f64(), layer.W64["W_DKV"], layer.W64["W_KR"], np.arange(T), 10000.0)
+    ref = np.concatenate([c, kr], 1)
+    for t, slot in enumerate(slots):
+        if slot in written:
+            assert oracle.max_rel_error(flat[slot], ref[t]) < 1e-5
+
+
+def test_invalid_device_indices_give_nan_rows(v2):
+    s = inputs.V2
+    lens = np.array([100, 100, 100, 100], np.int32)
+    paged = inputs.make_paged(lens, 64, 26, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 26, "bf16")
+    cache = cache_from_rows(v2, rows, paged, offs)
+    qa = _rand_q(4, s, 26)
+    pt = paged.page_table.copy()
+    pt[1, 1] = paged.num_pages + 5        # page id out of range
+    bad_lens = lens.copy()
+    bad_lens[2] = 0                       # kv_len below 1
+    bad_lens[3] = 129                     # beyond the page table row (2 pages)
+    lat = device.to_f64(v2.decode_attention(device.tensor(qa), cache, pt, bad_lens, 128, 0))
+    assert np.all(np.isnan(lat[1])) and np.all(np.isnan(lat[2])) and np.all(np.isnan(lat[3]))
+    ref = oracle.latent_attention(qa.f64()[0], rows.f64()[:100], s.d_c)
+    assert oracle.max_rel_error(lat[0], ref) < TOL["bf16"]
