@@ -168,6 +168,16 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                 const float* rope_table, int rope_len, void* workspace, size_t ws_bytes,
                 void* out, void* stream);
 
+/* Kernel timing for measurement tools (not needed for computing).  While
+ * enabled, every mla_decode / mla_decode_attention call records a HIP event
+ * pair on its stream around its cache-streaming attention kernel.
+ * mla_profile_attention_ms waits for the recorded events, returns the summed
+ * kernel time in milliseconds and the number of launches, and clears the
+ * record.  Host-thread-unsafe; enable from one thread.  Returns MLA_ERR_HIP
+ * if an event call fails. */
+int mla_profile_enable(int enable);
+int mla_profile_attention_ms(double* total_ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

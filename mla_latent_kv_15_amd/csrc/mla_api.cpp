@@ -186,6 +186,30 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
   return MLA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// optional event pairs around the attention kernel (measurement only)
+// ---------------------------------------------------------------------------
+struct Profiler {
+  bool on = false;
+  int used = 0;
+  hipEvent_t ev[2 * 4096];
+  int created = 0;
+  hipError_t mark(int which, hipStream_t s) {
+    if (!on) return hipSuccess;
+    int idx = 2 * used + which;
+    if (idx >= 2 * 4096) return hipSuccess;
+    if (idx >= created) {
+      hipError_t e = hipEventCreate(&ev[idx]);
+      if (e != hipSuccess) return e;
+      created = idx + 1;
+    }
+    hipError_t e = hipEventRecord(ev[idx], s);
+    if (which == 1 && e == hipSuccess) ++used;
+    return e;
+  }
+};
+Profiler g_prof;
+
 int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                   const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
                   int max_kv_len, int num_splits, void* ws, void* lat, hipStream_t s) {
@@ -196,14 +220,19 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
   carve_plan(a.plan, B, num_splits, &plan);
   const bool fast = is_v2_fast(g);
   MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
+  MLA_TRY(g_prof.mark(0, s));
   if (fast) {
+    // the MFMA kernel writes every segment as a partial; its merge follows
     MLA_TRY(attn_decode_v2(g, q_abs, cache, num_pages, page_table, max_pages, plan, a.max_wg,
-                           a.part_o, a.part_ml, lat, s));
+                           a.part_o, a.part_ml, s));
+    MLA_TRY(g_prof.mark(1, s));
+    MLA_TRY(combine_decode_v2(plan, B, a.part_o, a.part_ml, lat, s));
   } else {
     MLA_TRY(attn_decode_generic(g, q_abs, cache, num_pages, page_table, max_pages, plan,
                                 a.max_segs, a.part_o, a.part_ml, lat, s));
+    MLA_TRY(g_prof.mark(1, s));
+    MLA_TRY(combine_partials(g, plan, B, a.part_o, a.part_ml, lat, s));
   }
-  MLA_TRY(combine_partials(g, plan, B, a.part_o, a.part_ml, lat, s));
   return MLA_OK;
 }
 
@@ -248,6 +277,28 @@ const char* mla_status_string(int status) {
 }
 
 int mla_version(void) { return 100; }
+
+int mla_profile_enable(int enable) {
+  g_prof.on = enable != 0;
+  g_prof.used = 0;
+  return MLA_OK;
+}
+
+int mla_profile_attention_ms(double* total_ms, int* launches) {
+  if (!total_ms || !launches) return MLA_ERR_INVALID_ARG;
+  double tot = 0.0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return MLA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
+      return MLA_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = g_prof.used;
+  g_prof.used = 0;
+  return MLA_OK;
+}
 
 int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void* stream) {
   Geo g;

@@ -20,7 +20,7 @@ struct Geo {
 };
 
 // The DeepSeek-V2 decode shape served by the MFMA kernels.
-constexpr bool kHaveV2Attention = false;
+constexpr bool kHaveV2Attention = true;
 inline bool is_v2_fast(const Geo& g) {
   return kHaveV2Attention && g.bf16 && g.n_h == 128 && g.d_c == 512 && g.d_r == 64 && g.d_h == 128 &&
          g.page % 64 == 0 && g.d % 256 == 0 && g.d_cq % 256 == 0;
@@ -105,7 +105,9 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
 // ---------------------------------------------------------------------------
 hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
-                          int n_wg_launch, float* part_o, float* part_ml, void* lat_out,
-                          hipStream_t s);
+                          int n_wg_launch, float* part_o, float* part_ml, hipStream_t s);
+// Merge of the register-order partials attn_decode_v2 writes.
+hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const float* part_o,
+                             const float* part_ml, void* lat_out, hipStream_t s);
 
 }  // namespace mla

@@ -68,6 +68,8 @@ _SIGS = {
     "mla_decode_attention": (c_int, [_P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, c_int, _P,
                                      c_size_t, _P, _P]),
     "mla_decode_output": (c_int, [_P, _P, _P, c_int, _P, c_size_t, _P, _P]),
+    "mla_profile_enable": (c_int, [c_int]),
+    "mla_profile_attention_ms": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
     "mla_prefill": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P, c_int, _P,
                             c_size_t, _P, _P]),
 }
@@ -188,3 +190,15 @@ def prefill(cfg, weights, h, positions, kv_cache, page_table, kv_len, rope_table
         ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), _ptr(positions), _ptr(kv_cache),
         kv_cache.shape[0], _ptr(page_table), page_table.shape[0], kv_len, h.shape[0],
         _ptr(rope_table), rope_table.shape[0], wp, wn, _ptr(out), _stream(stream)))
+
+
+def profile_enable(on: bool):
+    _check("mla_profile_enable", load().mla_profile_enable(1 if on else 0))
+
+
+def profile_attention_ms():
+    """(summed attention-kernel milliseconds, launches) since the last read."""
+    ms = c_double(0.0)
+    n = c_int(0)
+    _check("mla_profile_attention_ms", load().mla_profile_attention_ms(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

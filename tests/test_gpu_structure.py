@@ -119,3 +119,29 @@ def test_invalid_device_indices_give_nan_rows(v2):
     assert np.all(np.isnan(lat[1])) and np.all(np.isnan(lat[2])) and np.all(np.isnan(lat[3]))
     ref = oracle.latent_attention(qa.f64()[0], rows.f64()[:100], s.d_c)
     assert oracle.max_rel_error(lat[0], ref) < TOL["bf16"]
+
+
+def test_score_jump_redo_path(v2):
+    """A score far above the segment's first scores (beyond 2^64 in the
+    softmax numerator) takes the exact-max redo path; results still match."""
+    s = inputs.V2
+    lens = np.array([300, 5000], np.int32)
+    paged = inputs.make_paged(lens, 64, 27, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 27, "bf16")
+    qa = _rand_q(2, s, 27)
+    f32 = rows.f32.copy()
+    q = qa.f32
+    for b, t in ((0, 250), (1, 4321)):
+        # a row aligned with head 0's query: its score ~ +60 nats
+        f32[offs[b] + t] = np.sign(q[b][0]) * 60.0 / np.abs(q[b][0]).sum()
+    rows = inputs.Array(f32, "bf16")
+    cache = cache_from_rows(v2, rows, paged, offs)
+    r64 = rows.f64()
+    for ns in (0, 1):
+        lat = device.to_f64(v2.decode_attention(device.tensor(qa), cache, paged.page_table, lens, 5000, ns))
+        for b in range(2):
+            ref = oracle.latent_attention(qa.f64()[b], r64[offs[b]:offs[b] + lens[b]], s.d_c)
+            sc = qa.f64()[b][0] @ r64[offs[b]:offs[b] + lens[b]].T
+            assert sc.max() - sc[:32].max() > 50  # the jump is real (> 64 in log2 units)
+            assert oracle.max_rel_error(lat[b], ref) < TOL["bf16"]
