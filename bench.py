@@ -1,0 +1,214 @@
+#!/usr/bin/env python
+"""MLA decode benchmark on one MI355X.
+
+One step = one mla_decode call (query projections, absorption, paged-cache
+attention with split-KV merge, W_UV and W_O) for a batch of 64 sequences of
+the DeepSeek-V2 layer (d=5120, n_h=128, d_h=128, d_c=512, d_c'=1536, d_R=64),
+context lengths uniform on [1024, 8192], 64-token pages in shuffled order,
+bf16 weights/cache with fp32 accumulation, query positions equal to each
+sequence's length (kv_len = L + 1).  Inputs are seeded synthetic data resident
+in HBM; two full buffer sets (weights + cache) alternate between steps so
+that the 256 MB last-level cache cannot serve a step from the previous one.
+
+Prints one JSON line (see the keys below).  --gpus N with N > 1 exits: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + latent-cache HBM GB/s & MFMA% (n_h=128, d_c=512)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+BYTES_PER_TOKEN = 1152          # one cached row: (512 + 64) bf16
+FLOP_PER_TOKEN = 2 * 128 * 576 + 2 * 128 * 512   # scores + latent accumulation per head
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+WORKLOADS = {
+    # name: (batch, lo, hi, config id)
+    "batch64": (64, 1024, 8192, 3),
+    "batch1": (1, 4096, 4096, 2),
+    "long4": (4, 131072, 131072, 4),
+}
+
+
+def build_set(s, B, lo, hi, cid, sub, device, inputs, lib):
+    import numpy as np
+    import torch
+    L = inputs.make_lengths(B, lo, hi, cid)
+    kv = (L + 1).astype(np.int32)
+    paged = inputs.make_paged(kv, 64, cid + 100 * sub, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(kv)[:-1]]).astype(np.int64)
+    rows = inputs.make_cache_rows(int(kv.sum()), s, cid, "bf16", sub=sub)
+    cache = device.bits_tensor(inputs.scatter_rows(rows.bits, paged, offs, fill=0))
+    del rows
+    W = inputs.make_weights(s, cid + 100 * sub, "bf16")
+    Wd = device.weights(W)
+    del W
+    Hq = inputs.make_hidden(B, s, cid, "bf16", sub=sub)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
+    return dict(L=L, kv=kv, paged=paged, cache=cache, Wd=Wd, wts=lib.make_weights(Wd),
+                h=device.tensor(Hq), pos=i32(L), kv_d=i32(kv), pt=i32(paged.page_table),
+                Hq=Hq, offs=offs)
+
+
+def cpu_baseline(s, st, budget_s, cid):
+    """The fp64 oracle (order A, the reference) on a bounded sample of the
+    same workload: whole sequences until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from mla_latent_kv_15_amd import inputs
+    try:
+        import threadpoolctl
+        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:  # noqa: BLE001
+        threads = 1
+    W64 = {k: v.f64() for k, v in inputs.make_weights(s, cid, "bf16").items()}
+    t0 = time.perf_counter()
+    done = 0
+    toks = 0
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    for b in range(len(st["L"])):
+        n = int(st["kv"][b])
+        rows = inputs.make_cache_rows(n, s, 9000 + b, "bf16").f64()
+        q_c, q_r = oracle.query(st["Hq"].f64()[b], W64["W_DQ"], W64["W_UQ"], W64["W_QR"],
+                                int(st["L"][b]), s.n_h, 10000.0)
+        o = oracle.attend_order_a(q_c, q_r, rows[:, :s.d_c], rows[:, s.d_c:], W64["W_UK"],
+                                  W64["W_UV"], sc)
+        oracle.integrate(o, W64["W_O"])
+        done += 1
+        toks += n
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"order-A fp64 decode of the first {done} of the batch's sequences "
+                      f"({toks} cached rows) in {dt:.1f} s; each sequence yields one token"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU sharding is described "
+              "in DESIGN.md but not built (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_15_amd import device, inputs, lib
+
+    lib.load()
+    torch.cuda.set_device(0)
+    s = inputs.V2
+    B, lo, hi, cid = WORKLOADS[args.workload]
+    log(f"building {args.sets} buffer set(s) for workload {args.workload}")
+    sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib) for k in range(args.sets)]
+    st0 = sets[0]
+    max_kv = int(max(int(st["kv"].max()) for st in sets))
+    cfg = lib.make_config(s, 64, "bf16")
+    rope = torch.empty(max_kv + 1, s.d_r // 2, 2, dtype=torch.float32, device="cuda")
+    lib.rope_table_init(cfg, max_kv + 1, rope)
+    ws = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE, B, max_kv, args.splits))
+    outs = [torch.empty(B, s.d, dtype=torch.bfloat16, device="cuda") for _ in sets]
+
+    def step(i):
+        st = sets[i % len(sets)]
+        lib.decode(cfg, st["wts"], st["h"], st["pos"], st["cache"], st["pt"], st["kv_d"], max_kv,
+                   rope, args.splits, ws, outs[i % len(sets)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("timing")
+    lib.profile_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    attn_ms, launches = lib.profile_attention_ms()
+    lib.profile_enable(False)
+    ms_step = total_ms / args.steps
+    attn_avg = attn_ms / max(launches, 1)
+    # per-launch algorithmic work: the cached rows of the step's batch (sets alternate)
+    toks = [int(st["kv"].sum()) for st in sets]
+    toks_avg = sum(toks[i % len(sets)] for i in range(args.steps)) / args.steps
+    cache_bytes = toks_avg * BYTES_PER_TOKEN
+    achieved = cache_bytes / (attn_avg * 1e-3) / 1e9
+    mfma_tflops = toks_avg * FLOP_PER_TOKEN / (attn_avg * 1e-3) / 1e12
+    weight_bytes = sum(t.numel() * t.element_size() for t in st0["Wd"].values())
+    step_bytes = cache_bytes + weight_bytes
+
+    res = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mla_decode, DeepSeek-V2 layer, batch {B}, context U[{lo},{hi}], "
+                        f"64-token shuffled pages, kv_len = L + 1",
+            "batch": B, "context_lo": lo, "context_hi": hi, "page_size": 64,
+            "d": s.d, "n_h": s.n_h, "d_h": s.d_h, "d_c": s.d_c, "d_cq": s.d_cq, "d_r": s.d_r,
+            "num_splits": args.splits, "buffer_sets": len(sets),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "kernel": "attn_v2_kernel (paged latent-cache attention)",
+            "launch_ms": attn_avg,
+            "bytes_per_launch": cache_bytes,
+        },
+        "attention_mfma_tflops": mfma_tflops,
+        "attention_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
+        "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_bytes": step_bytes,
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(s, st0, args.cpu_seconds, cid)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
