@@ -28,12 +28,33 @@ CFLAGS = [
 ]
 
 
+# Kernels that must not touch scratch memory: their inner loops count
+# outstanding vector-memory operations by hand (a spill reload would both
+# break that count and stall on it), and their inline-asm MFMA chains rely on
+# the compiler never placing spill code between them.
+NO_SCRATCH = ("attn_v2_kernel",)
+
+
+def _check_scratch(src: str, remarks: str):
+    """Parse -Rpass-analysis=kernel-resource-usage remarks for NO_SCRATCH kernels."""
+    cur = None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            cur = line.split("Function Name:")[1].strip()
+        elif "ScratchSize [bytes/lane]:" in line and cur is not None:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size and any(k in cur for k in NO_SCRATCH):
+                raise RuntimeError(f"{os.path.basename(src)}: kernel {cur} uses {size} B of scratch "
+                                   f"per lane; its hand-counted memory waits require none")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_scratch(src, r.stderr)
     return obj
 
 

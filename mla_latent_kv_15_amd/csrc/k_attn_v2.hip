@@ -14,8 +14,11 @@
 //    accumulation registers (256 per lane).  All 128 heads read each cache
 //    row from LDS, so HBM sees every row exactly once.
 //  * 64-token tiles (one page slice, 72 KB contiguous in HBM) are streamed
-//    with 16-byte direct-to-LDS loads into a double buffer; LDS rows are
-//    padded to 73 x 16 B so the 32 rows of one score MFMA hit distinct banks.
+//    with 16-byte direct-to-LDS loads into a double buffer.  LDS rows are
+//    1152 B with the 16-byte chunks of row r XOR-permuted by a 3-bit function
+//    of r, chosen so that both read patterns below (32 rows at one chunk, and
+//    4 rows x 32 bytes per 16 lanes) are free of bank conflicts for 32- and
+//    64-bank LDS models.
 //  * scores: S^T[token][head] = C[token][dims] . Q~^T[dims][head] with
 //    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~ from VGPRs).
 //  * softmax numerators in the log2 domain against a per-segment reference:
@@ -29,8 +32,8 @@
 //  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T with the
 //    same MFMA.  The P operand comes straight from the score accumulators (the
 //    token order inside one K-step is permuted to match their layout); the
-//    C^T operand is an in-register 8x8 bf16 transpose of 8-byte LDS row reads,
-//    which maps lane m to dims {8m .. 8m+7} across eight MFMAs.
+//    C^T operand arrives already transposed from two ds_read_b64_tr_b16 per
+//    MFMA (each 16-lane group turns 4 rows x 16 dims into 16 lanes x 4 rows).
 //  * a work-group walks the segments the plan assigns to it and writes each
 //    segment's unnormalised (m, l, o~) straight from the accumulation
 //    registers, in register order; a merge kernel weighs the segments of each
@@ -52,42 +55,71 @@ constexpr int kHeads = 128;
 constexpr int kRow = 576;            // bf16 numbers per cached token
 constexpr int kDc = 512;
 constexpr int kChunks = kRow / 8;    // 72 x 16 B per row
-constexpr int kLdsStride = 73;       // padded LDS row, in 16-byte chunks
-constexpr int kTile = 64;            // tokens per tile
-constexpr int kTileChunks = kTile * kLdsStride;      // 4672
-constexpr int kLoadInsts = kTileChunks / 64;         // 73 wave-wide loads per tile
+constexpr int kRowBytes = kRow * 2;  // 1152
+constexpr int kSub = 32;             // tokens per sub-tile (one MFMA block)
+constexpr int kSlots = 4;            // LDS ring: one sub-tile computed, three in flight
+constexpr int kSubChunks = kSub * kChunks;           // 2304
+constexpr int kSubBytes = kSubChunks * 16;           // 36864
+constexpr int kSubInsts = kSubChunks / 64;           // 36 wave-wide loads per sub-tile
+constexpr int kInstsPerWave = kSubInsts / 4;         // 9
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKSteps = kRow / 16;   // 36 score K-steps of 16 dims
+constexpr int kKReg = kDc / 16;      // 32 K-steps whose Q~ slice stays in VGPRs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 64.0f;       // allowed score excess over the reference (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __shared__ __attribute__((aligned(16))) char g_tiles[2 * kTileChunks * 16];
+// one LDS object: the cache ring, then the query's RoPE slice
+constexpr int kQropeOff = kSlots * kSubBytes;        // 147456
+constexpr int kQropeBytes = kHeads * 64 * 2;         // 16384
+__device__ __shared__ __attribute__((aligned(16))) char g_tiles[kQropeOff + kQropeBytes];
+// rope part of the absorbed query (dims 512..575) for all 128 heads at
+// g_tiles + kQropeOff; chunk c of head i sits at chunk position c ^ swz(i)
 
-// Stream one 64-token tile (rows [0, nvalid) valid) into LDS buffer `buf`;
-// rows past nvalid are zero-filled so 0 * garbage never reaches an MFMA.
-__device__ inline void load_tile(const u32x4* __restrict__ gtile, int nvalid, char* buf,
-                                 int wave, int lane) {
-  for (int inst = wave; inst < kLoadInsts; inst += kWaves) {
-    const int p = inst * 64 + lane;
-    const int r = p / kLdsStride;
-    const int c = p - r * kLdsStride;
-    if (c < kChunks) {
-      if (r < nvalid) {
-        __builtin_amdgcn_global_load_lds((const void*)(gtile + r * kChunks + c),
-                                         (lds_void*)(buf + inst * 64 * 16), 16, 0, 0);
-      } else {
-        *(u32x4*)(buf + p * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
+// Work-group barrier without __syncthreads' release fence: that fence waits
+// for every outstanding vector memory operation, which would drain the
+// in-flight cache sub-tiles of the ring at each barrier.  LDS ordering is
+// established by the explicit s_waitcnt that precedes each use; the asm
+// memory clobbers keep the compiler from moving LDS accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+// 16-byte chunk c of tile row r sits at chunk position c ^ swz(r) of that row
+__device__ inline int swz(int r) {
+  return ((((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1)) & 7;
+}
+
+// Stream one 32-token sub-tile into LDS slot `buf`.  Rows at or past nvalid
+// re-read the last valid row (nvalid = 0: row 0 of the page passed in): their
+// scores are masked to zero weight, and the data stays finite, so
+// 0 * row never turns into NaN.  Every wave issues exactly kInstsPerWave loads
+// per sub-tile whatever nvalid is; the ring's vmcnt bookkeeping relies on it.
+__device__ inline void load_sub(const u32x4* __restrict__ gsub, int nvalid, char* buf, int wave,
+                                int lane) {
+  // recompute the per-lane addresses at every call instead of keeping nine
+  // loop-invariant offsets live across the compute loop (VGPRs are scarce)
+  asm volatile("" : "+v"(lane));
+  const int rmax = max(nvalid - 1, 0);
+  // wave w fills rows [8w, 8w+8): its i-th load covers chunks [64i, 64i+64)
+  // of those 576, i.e. rows k_i and k_i + 1 with the switch at lane b_i
+#pragma unroll
+  for (int i = 0; i < kInstsPerWave; ++i) {
+    const int k = (64 * i) / kChunks;
+    const int bnd = kChunks * (k + 1) - 64 * i;
+    const bool second = lane >= bnd;
+    const int r = 8 * wave + k + (second ? 1 : 0);
+    const int cp = 64 * i - kChunks * k + lane - (second ? kChunks : 0);
+    __builtin_amdgcn_global_load_lds((const void*)(gsub + min(r, rmax) * kChunks + (cp ^ swz(r))),
+                                     (lds_void*)(buf + (8 * wave * kChunks + 64 * i) * 16), 16, 0, 0);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
@@ -102,147 +134,212 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   const int m32 = lane & 31;
   const int head = wave * 32 + m32;
   const u32x4* cache16 = (const u32x4*)cache;
+  lds_char* const lds = (lds_char*)g_tiles;
+
+  // Per-lane LDS byte offsets inside a 32-token block (row 0 of the block is
+  // a multiple of 16, so the swizzle only sees the low 4 row bits).
+  // scores: row m32, chunk 2ks + h   -> qoff[ks & 3] + 128 * (ks >> 2)
+  int qoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qoff[j] = m32 * kRowBytes + (((2 * j + h) ^ swz(m32)) << 4);
+  // latent accumulation: element e = 4a + c of lane (m32, h) is token row
+  // 8a + 4h + c of the K-step; it reads 16-byte chunk m32 (+32 per quarter)
+  int voff[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = 8 * (e >> 2) + 4 * h + (e & 3);
+    voff[e] = row * kRowBytes + ((m32 ^ swz(row)) << 4);
+  }
 
   const int k_begin = plan.wg_seg_start[g];
   const int k_end = plan.wg_seg_start[g + 1];
   for (int k = k_begin; k < k_end; ++k) {
     const Seg sg = plan.segs[k];
     const int b = sg.b;
-    const int ntiles = (sg.t1 - sg.t0 + kTile - 1) / kTile;
 
     // absorbed query slice -> VGPRs (B operand: lane = head, 8 dims per K-step half)
-    bf16x8 qreg[kKSteps];
+    bf16x8 qreg[kKReg];
     {
-      const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + head) * kRow + 8 * h);
+      int hd = head, hh = h;
+      asm volatile("" : "+v"(hd), "+v"(hh));
+      const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qs[2 * ks];
+      for (int ks = 0; ks < kKReg; ++ks) qreg[ks] = qs[2 * ks];
     }
     f32x16 acc[16];
     float m_ref = -INFINITY;  // exponent reference (log2 units), fixed within a pass
     float l_run = 0.f;
     bool bad = false;
-    // mode 0: reference = max of the first 32 tokens; mode 1: exact max only;
-    // mode 2: full pass with the exact max (after a mode-0 overflow)
+    // pass 0: reference = max of the first 32 tokens; every sub-tile's max is
+    // tracked, so after a pass-0 overflow the exact segment max is known and
+    // pass 1 redoes the segment with it as the reference
     int mode = 0;
     for (;;) {
+      // opaque to the optimiser: one copy of the sub-tile loop serves both passes
+      asm volatile("" : "+v"(mode));
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[x] = f32x16{};
       l_run = 0.f;
       float m_seen = -INFINITY;
       bool over = false;
 
-      __syncthreads();  // every wave is done with both tile buffers
+      __syncthreads();  // every wave is done with the ring and the query buffer
       {
-        const int tt = sg.t0;
+        // rope part of Q~ for all heads -> LDS: 1024 chunks, 4 per thread
+        int tl = threadIdx.x;
+        asm volatile("" : "+v"(tl));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = tl + kThreads * u;
+          const int hd = e >> 3, c = e & 7;
+          const u32x4 v = *(const u32x4*)(q_abs + ((long)b * kHeads + hd) * kRow + kDc + 8 * c);
+          *(u32x4*)(g_tiles + kQropeOff + hd * 128 + ((c ^ swz(hd)) << 4)) = v;
+        }
+      }
+      const int nsub = (sg.t1 - sg.t0 + kSub - 1) / kSub;
+      // sub-tile j of the segment: tokens [t0 + 32j, ...) inside one page
+      auto issue = [&](int j) {
+        const int tt = sg.t0 + j * kSub;
         const int pg = page_table[(long)b * max_pages + tt / page];
         const bool ok = pg >= 0 && pg < num_pages;
         bad |= !ok;
         const long slot0 = ok ? (long)pg * page + tt % page : 0;
-        load_tile(cache16 + slot0 * kChunks, ok ? min(kTile, sg.t1 - tt) : 0, g_tiles, wave, lane);
-      }
+        load_sub(cache16 + slot0 * kChunks, ok ? min(kSub, sg.t1 - tt) : 0,
+                 g_tiles + (j % kSlots) * kSubBytes, wave, lane);
+      };
+      for (int j = 0; j < kSlots - 1 && j < nsub; ++j) issue(j);
 
-      for (int it = 0; it < ntiles; ++it) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // tile `it` landed everywhere; buffer (it+1)&1 is free
-        if (it + 1 < ntiles) {
-          const int tt = sg.t0 + (it + 1) * kTile;
-          const int pg = page_table[(long)b * max_pages + tt / page];
-          const bool ok = pg >= 0 && pg < num_pages;
-          bad |= !ok;
-          const long slot0 = ok ? (long)pg * page + tt % page : 0;
-          load_tile(cache16 + slot0 * kChunks, ok ? min(kTile, sg.t1 - tt) : 0,
-                    g_tiles + ((it + 1) & 1) * kTileChunks * 16, wave, lane);
+#pragma clang loop unroll(disable)
+      for (int j = 0; j < nsub; ++j) {
+        // sub-tile j is complete once at most the loads of the sub-tiles
+        // issued after it are outstanding
+        const int later = min(kSlots - 2, nsub - 1 - j);
+        static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
+        if (later >= 2)
+          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (later == 1)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the ring slot after the last sub-tile is free at the last iteration;
+        // it carries the work-group's redo flag
+        if (j == nsub - 1 && threadIdx.x == 0) {
+          *(int __attribute__((address_space(3)))*)(lds + (nsub % kSlots) * kSubBytes) = 0;
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        const char* buf = g_tiles + (it & 1) * kTileChunks * 16;
-        const int nvalid = min(kTile, sg.t1 - (sg.t0 + it * kTile));
-
+        lds_barrier();  // sub-tile j landed everywhere; slot (j+3)%4 is free
+        const int nvalid = min(kSub, sg.t1 - (sg.t0 + j * kSub));
+        lds_char* bb = lds + (j % kSlots) * kSubBytes;
+        {
+          // ---- scores for 32 tokens x 32 heads, A operand prefetched 4 deep.
+          // The MFMA chain is written as inline asm with a VGPR ("v")
+          // accumulator: with the builtin the compiler puts S in the
+          // accumulation registers, which the 32 x 512 o~ accumulator already
+          // fills, and then spills o~.  Back-to-back accumulation into the
+          // same registers needs no wait states; the s_nop after the chain
+          // covers the MFMA-result -> VALU-read hazard.
+          f32x16 S;
+          bf16x8 abuf[4];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          if (32 * blk >= nvalid) break;
-          // ---- scores for 32 tokens x 32 heads
-          f32x16 S = f32x16{};
-          const char* arow = buf + ((32 * blk + m32) * kLdsStride + h) * 16;
+          for (int ks = 0; ks < 4; ++ks) abuf[ks] = *(const bf16x8 __attribute__((address_space(3)))*)(bb + qoff[ks & 3] + 128 * (ks >> 2));
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks) {
-            const bf16x8 a = *(const bf16x8*)(arow + 2 * ks * 16);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], S, 0, 0, 0);
+            const bf16x8 a = abuf[ks & 3];
+            if (ks + 4 < kKSteps)
+              abuf[ks & 3] = *(const bf16x8 __attribute__((address_space(3)))*)(bb + qoff[(ks + 4) & 3] + 128 * ((ks + 4) >> 2));
+            const bf16x8 q = ks < kKReg
+                ? qreg[ks]
+                : *(const bf16x8 __attribute__((address_space(3)))*)(
+                      lds + kQropeOff + head * 128 + (((2 * (ks - kKReg) + h) ^ swz(head)) << 4));
+            if (ks == 0)
+              // early clobber: the destination must not overlap the A/B operands
+              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(q));
+            else
+              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(q));
           }
+          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
           // ---- softmax numerators (log2 domain), lane = head, 16 of the 32 tokens
+          if (nvalid < kSub) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int tok = 8 * (i >> 2) + 4 * h + (i & 3);
+              S[i] = tok < nvalid ? S[i] : -INFINITY;
+            }
+          }
           float bm = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tok = 32 * blk + 8 * (i >> 2) + 4 * h + (i & 3);
-            S[i] = tok < nvalid ? S[i] * kLog2e : -INFINITY;
-            bm = fmaxf(bm, S[i]);
-          }
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          for (int i = 0; i < 16; ++i) bm = fmaxf(bm, S[i]);
+          bm = fmaxf(bm, __shfl_xor(bm, 32)) * kLog2e;
           m_seen = fmaxf(m_seen, bm);
-          if (mode == 1) continue;
-          if (mode == 0 && it == 0 && blk == 0) m_ref = bm;
+          // pass 0 takes its reference from the first sub-tile (m_ref is -inf
+          // until then); the redo pass starts with the exact maximum
+          m_ref = (m_ref == -INFINITY) ? bm : m_ref;
           over |= bm > m_ref + kLazy;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            S[i] = __builtin_amdgcn_exp2f(S[i] - m_ref);
+            S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], kLog2e, -m_ref));
             l_run += S[i];
           }
-          // ---- latent accumulation, two K-steps of 16 tokens
+          // ---- latent accumulation: o~^T[dims][head] += C^T . P^T, two K-steps
+          // of 16 tokens.  Lane (m32, h) reads the 16-byte chunk m32 of each
+          // quarter-row for its eight token rows and transposes the 8 x 8 bf16
+          // block in registers: M-block (q, j) holds dims 256q + 8m + j.
+          bf16x8 pb[2];
 #pragma unroll
-          for (int kap = 0; kap < 2; ++kap) {
-            if (32 * blk + 16 * kap >= nvalid) break;
-            bf16x8 pb;
+          for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)S[8 * kap + e];
-            // token rows of this lane's K slots: 16kap + 8a + 4h + c (a = 0..1, c = 0..3)
-            const char* vrow = buf + ((32 * blk + 16 * kap + 4 * h) * kLdsStride + m32) * 16;
+            for (int e = 0; e < 8; ++e) pb[kap][e] = (__bf16)S[8 * kap + e];
+          // (a K-step past nvalid adds P = 0 times finite re-read rows)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+          for (int g8 = 0; g8 < 4; ++g8) {       // (kap, q) groups of 8 MFMAs
+            const int kap = g8 >> 1, q = g8 & 1;
+            u32x4 v[8];
 #pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                uint2 v[8];
+            for (int e = 0; e < 8; ++e)
+              v[e] = *(const u32x4 __attribute__((address_space(3)))*)(
+                  bb + 16 * kap * kRowBytes + voff[e] + 512 * q);
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+            for (int d = 0; d < 4; ++d) {
+              u32x4 lo, hi;
 #pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    v[4 * a + c] =
-                        *(const uint2*)(vrow + ((8 * a + c) * kLdsStride + 32 * q) * 16 + 8 * hh);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                  u32x4 lo, hi;
-#pragma unroll
-                  for (int f = 0; f < 4; ++f) {
-                    const uint32_t x0 = e ? v[2 * f].y : v[2 * f].x;
-                    const uint32_t x1 = e ? v[2 * f + 1].y : v[2 * f + 1].x;
-                    lo[f] = perm(x1, x0, 0x05040100u);
-                    hi[f] = perm(x1, x0, 0x07060302u);
-                  }
-                  const int j = 4 * hh + 2 * e;
-                  acc[8 * q + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                      __builtin_bit_cast(bf16x8, lo), pb, acc[8 * q + j], 0, 0, 0);
-                  acc[8 * q + j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                      __builtin_bit_cast(bf16x8, hi), pb, acc[8 * q + j + 1], 0, 0, 0);
-                }
+              for (int f = 0; f < 4; ++f) {
+                lo[f] = __builtin_amdgcn_perm(v[2 * f + 1][d], v[2 * f][d], 0x05040100u);
+                hi[f] = __builtin_amdgcn_perm(v[2 * f + 1][d], v[2 * f][d], 0x07060302u);
               }
+              acc[8 * q + 2 * d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, lo), pb[kap], acc[8 * q + 2 * d], 0, 0, 0);
+              acc[8 * q + 2 * d + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, hi), pb[kap], acc[8 * q + 2 * d + 1], 0, 0, 0);
             }
           }
+          // refill the ring after this iteration's last LDS read (the
+          // compiler places a full vmcnt wait before LDS reads that follow a
+          // direct-to-LDS load in program order)
+          if (j + kSlots - 1 < nsub) issue(j + kSlots - 1);
         }
       }
-      if (mode == 1) {
-        m_ref = m_seen;
-        mode = 2;
-        continue;
-      }
       // a score more than kLazy above the reference anywhere in the work-group:
-      // find the exact maximum and redo the segment with it (rare)
-      if (mode == 0 && __syncthreads_or(over ? 1 : 0)) {
-        mode = 1;
-        continue;
+      // redo the segment with the exact maximum seen in this pass (rare)
+      if (mode == 0) {
+        int __attribute__((address_space(3)))* flag =
+            (int __attribute__((address_space(3)))*)(lds + (nsub % kSlots) * kSubBytes);
+        if (over) *flag = 1;
+        __syncthreads();
+        const int redo = *flag;
+        if (redo) {
+          m_ref = m_seen;
+          mode = 1;
+          continue;
+        }
       }
       break;
     }
 
     // ---- unnormalised partial (m, l, o~) in register order; merged later
     {
-      f32x4* dst = (f32x4*)(part_o + (long)k * kHeads * kDc) + wave * 64 + lane;
+      int tl = threadIdx.x;
+      asm volatile("" : "+v"(tl));  // form the per-lane address here, not at kernel entry
+      f32x4* dst = (f32x4*)(part_o + (long)k * kHeads * kDc) + tl;
 #pragma unroll
       for (int x = 0; x < 16; ++x)
 #pragma unroll
@@ -251,8 +348,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
               f32x4{acc[x][4 * a], acc[x][4 * a + 1], acc[x][4 * a + 2], acc[x][4 * a + 3]};
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       if (h == 0) {
-        part_ml[((long)k * kHeads + head) * 2] = m_ref * kLn2;
-        part_ml[((long)k * kHeads + head) * 2 + 1] = bad ? __builtin_nanf("") : l_tot;
+        int hd = head;
+        asm volatile("" : "+v"(hd));
+        float2* ml = (float2*)(part_ml + ((long)k * kHeads + hd) * 2);
+        *ml = float2{m_ref * kLn2, bad ? __builtin_nanf("") : l_tot};
       }
     }
   }
@@ -315,7 +414,8 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
       for (int r = 0; r < 16; ++r) acc[r] += ws * src[(r0 + 4 * r) * kThreads];
     }
   }
-  // register order -> [head][dim]: x = 8q + j, i = 4a + c, row m' = 8a + 4h + c
+  // register order -> [head][dim]: accumulator x = 8q + j holds dims
+  // 256q + 8m + j with row m = 8a + 4h + c for element i = 4a + c
   const int hf = lane >> 5;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -323,10 +423,8 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     const int x = xa >> 2, a = xa & 3;
     const int q = x >> 3, j = x & 7;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int dim = 256 * q + 8 * (8 * a + 4 * hf + c) + j;
-      stage[hd_l][dim] = (__bf16)acc[r][c];
-    }
+    for (int c = 0; c < 4; ++c)
+      stage[hd_l][256 * q + 8 * (8 * a + 4 * hf + c) + j] = (__bf16)acc[r][c];
   }
   __syncthreads();
   for (int e = t; e < 32 * (kDc / 8); e += 256) {

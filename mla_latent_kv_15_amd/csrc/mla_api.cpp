@@ -70,13 +70,37 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 // ---------------------------------------------------------------------------
 // workspace layouts
 // ---------------------------------------------------------------------------
+// split-K factors of the MFMA decode GEMMs (W_DQ over d, W_O over n_h*d_h)
+int split_dq(const Geo& g) {
+  for (int sk = 10; sk > 1; --sk)
+    if (g.d % (sk * 128) == 0) return sk;
+  return 1;
+}
+int split_o(const Geo& g) {
+  for (int sk = 8; sk > 1; --sk)
+    if ((g.n_h * g.d_h) % (sk * 128) == 0) return sk;
+  return 1;
+}
+
 struct QueryWs {
-  float *cq, *qc, *qr;
+  float *cq, *qc, *qr;   // generic: fp32 intermediates
+  float* cq_part;        // MFMA path: split-K partials of c^Q
+  void *cq16, *qc16;     // MFMA path: bf16 c^Q and q^C
 };
 void carve_query(Carver& c, const Geo& g, int B, QueryWs* w) {
+  if (is_v2_fast(g)) {
+    w->cq_part = (float*)c.take(sizeof(float) * (size_t)split_dq(g) * B * g.d_cq);
+    w->cq16 = c.take(2 * (size_t)B * g.d_cq);
+    w->qc16 = c.take(2 * (size_t)B * g.n_h * g.d_h);
+    w->qr = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_r);
+    w->cq = w->qc = nullptr;
+    return;
+  }
   w->cq = (float*)c.take(sizeof(float) * (size_t)B * g.d_cq);
   w->qc = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_h);
   w->qr = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_r);
+  w->cq_part = nullptr;
+  w->cq16 = w->qc16 = nullptr;
 }
 
 struct AttnWs {
@@ -94,10 +118,20 @@ void carve_attn(Carver& c, const Geo& g, int B, int num_splits, AttnWs* w) {
 }
 
 struct OutWs {
-  float* o;
+  float* o;        // generic: fp32 o
+  void* o16;       // MFMA path: bf16 o
+  float* u_part;   // MFMA path: split-K partials of u
 };
 void carve_out(Carver& c, const Geo& g, int B, OutWs* w) {
+  if (is_v2_fast(g)) {
+    w->o16 = c.take(2 * (size_t)B * g.n_h * g.d_h);
+    w->u_part = (float*)c.take(sizeof(float) * (size_t)split_o(g) * B * g.d);
+    w->o = nullptr;
+    return;
+  }
   w->o = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_h);
+  w->o16 = nullptr;
+  w->u_part = nullptr;
 }
 
 struct DecodeWs {
@@ -168,6 +202,23 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
   Carver c(ws);
   QueryWs q;
   carve_query(c, g, B, &q);
+  if (is_v2_fast(g)) {
+    const int sk = split_dq(g);
+    const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
+    // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16
+    MLA_TRY(wgemm(B, g.d_cq, g.d, sk, h, g.d, 0, g.d_cq, w->W_DQ, q.cq_part, g.d_cq,
+                  (long)B * g.d_cq, true, 1.f, s));
+    MLA_TRY(splitk_reduce(B, g.d_cq, sk, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s));
+    // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
+    MLA_TRY(wgemm(B, (int)nq, g.d_cq, 1, q.cq16, g.d_cq, 0, (int)nq, w->W_UQ, q.qc16, nq, 0,
+                  false, 1.f, s));
+    MLA_TRY(wgemm(B, (int)nr, g.d_cq, 1, q.cq16, g.d_cq, 0, (int)nr, w->W_QR, q.qr, nr, 0, true,
+                  1.f, s));
+    // absorbed query q~_i = W_UK,i^T q^C_i, scaled (order B)
+    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, s));
+    MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
+    return MLA_OK;
+  }
   const GType T = st(g);
   // c^Q = W_DQ h  (eq. (12))
   MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, q.cq,
@@ -241,6 +292,18 @@ int run_output(const Geo& g, const mla_weights* w, const void* lat, int B, void*
   Carver c(ws);
   OutWs o;
   carve_out(c, g, B, &o);
+  if (is_v2_fast(g)) {
+    const long nq = (long)g.n_h * g.d_h;
+    const int sk = split_o(g);
+    // o_i = W_UV,i o~_i: weight rows of head i read the latent row of head i
+    MLA_TRY(wgemm(B, (int)nq, g.d_c, 1, lat, (long)g.n_h * g.d_c, g.d_c, g.d_h, w->W_UV, o.o16,
+                  nq, 0, false, 1.f, s));
+    // u = W_O [o_0 | ... | o_{n_h-1}], split over n_h*d_h, reduced to bf16
+    MLA_TRY(wgemm(B, g.d, (int)nq, sk, o.o16, nq, 0, g.d, w->W_O, o.u_part, g.d, (long)B * g.d,
+                  true, 1.f, s));
+    MLA_TRY(splitk_reduce(B, g.d, sk, o.u_part, (long)B * g.d, out, g.d, s));
+    return MLA_OK;
+  }
   const GType T = st(g);
   // o_i = W_UV,i o~_i
   MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_h, g.d_c, lat, (long)g.n_h * g.d_c, g.d_c,

@@ -22,8 +22,8 @@ struct Geo {
 // The DeepSeek-V2 decode shape served by the MFMA kernels.
 constexpr bool kHaveV2Attention = true;
 inline bool is_v2_fast(const Geo& g) {
-  return kHaveV2Attention && g.bf16 && g.n_h == 128 && g.d_c == 512 && g.d_r == 64 && g.d_h == 128 &&
-         g.page % 64 == 0 && g.d % 256 == 0 && g.d_cq % 256 == 0;
+  return kHaveV2Attention && g.bf16 && g.n_h == 128 && g.d_c == 512 && g.d_r == 64 &&
+         g.d_h == 128 && g.page % 64 == 0 && g.d % 128 == 0 && g.d_cq % 128 == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -106,6 +106,18 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
 hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
                           int n_wg_launch, float* part_o, float* part_ml, hipStream_t s);
+// Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, X bf16 rows);
+// X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx.
+// out_f32: Y is fp32 partials [k_split][M][ldy]; else bf16 [M][ldy].
+bool wgemm_shape_ok(int N, int K, int k_split);
+hipError_t wgemm(int M, int N, int K, int k_split, const void* X, long ldx, long x_group_stride,
+                 int n_group, const void* W, void* Y, long ldy, long y_split_stride, bool out_f32,
+                 float alpha, hipStream_t s);
+hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
+                         long ldo, hipStream_t s);
+// q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16).
+hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
+                     hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
 hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const float* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);
