@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--sets", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (a known-size "
+                         "reference for the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU sharding is described "
@@ -120,8 +123,17 @@ def main():
 
     from mla_latent_kv_15_amd import device, inputs, lib
 
-    lib.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return
+    lib.load()
     s = inputs.V2
     B, lo, hi, cid = WORKLOADS[args.workload]
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")

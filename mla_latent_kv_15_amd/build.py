@@ -28,24 +28,56 @@ CFLAGS = [
 ]
 
 
-# Kernels that must not touch scratch memory: their inner loops count
-# outstanding vector-memory operations by hand (a spill reload would both
-# break that count and stall on it), and their inline-asm MFMA chains rely on
-# the compiler never placing spill code between them.
-NO_SCRATCH = ("attn_v2_kernel",)
+# Kernels whose MFMA blocks must be free of spill code.  Their inner loops
+# count outstanding vector-memory operations by hand and chain inline-asm
+# MFMAs whose hazards the compiler does not see, so no scratch access and no
+# accumulation-register copy may land in a basic block that issues MFMAs.
+# Spills elsewhere in the kernel (at entry, around a segment's epilogue) are
+# allowed up to a small cap.
+HOT_KERNELS = {"k_attn_v2.hip": "attn_v2_kernel"}
+MAX_SCRATCH = 256   # bytes per lane
+_SPILL_OPS = ("scratch_", "buffer_store", "buffer_load", "v_accvgpr_read", "v_accvgpr_write",
+              "v_accvgpr_mov")
 
 
 def _check_scratch(src: str, remarks: str):
-    """Parse -Rpass-analysis=kernel-resource-usage remarks for NO_SCRATCH kernels."""
+    """Parse -Rpass-analysis=kernel-resource-usage remarks of the hot kernels."""
+    kernel = HOT_KERNELS.get(os.path.basename(src))
+    if kernel is None:
+        return
     cur = None
     for line in remarks.splitlines():
         if "Function Name:" in line:
             cur = line.split("Function Name:")[1].strip()
-        elif "ScratchSize [bytes/lane]:" in line and cur is not None:
+        elif "ScratchSize [bytes/lane]:" in line and cur is not None and kernel in cur:
             size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
-            if size and any(k in cur for k in NO_SCRATCH):
-                raise RuntimeError(f"{os.path.basename(src)}: kernel {cur} uses {size} B of scratch "
-                                   f"per lane; its hand-counted memory waits require none")
+            if size > MAX_SCRATCH:
+                raise RuntimeError(f"{os.path.basename(src)}: {kernel} uses {size} B of scratch "
+                                   f"per lane (cap {MAX_SCRATCH})")
+
+
+def _check_hot_blocks(src: str, asm: str):
+    """No spill code inside a basic block of the hot kernel that issues MFMAs."""
+    kernel = HOT_KERNELS[os.path.basename(src)]
+    lines = asm.splitlines()
+    code = [l.split(";")[0].rstrip() for l in lines]   # drop the assembler's comments
+    begin = next(i for i, c in enumerate(code)
+                 if c.endswith(":") and kernel in c and not c.startswith((".", "\t")))
+    block, label, bad = [], lines[begin], []
+    for l, c in zip(lines[begin + 1:], code[begin + 1:]):
+        if c.startswith(".Lfunc_end"):
+            break
+        is_label = (c.endswith(":") and c.startswith(".LBB")) or l.startswith("; %bb.")
+        if is_label:
+            if any("v_mfma" in x for x in block):
+                bad += [f"{label.split()[0]} {x.strip()}" for x in block
+                        if any(op in x for op in _SPILL_OPS)]
+            block, label = [], l
+        else:
+            block.append(l)
+    if bad:
+        raise RuntimeError(f"{os.path.basename(src)}: spill code in MFMA blocks of {kernel}:\n  "
+                           + "\n  ".join(bad[:10]))
 
 
 def _compile(src: str) -> str:
@@ -55,6 +87,14 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     _check_scratch(src, r.stderr)
+    if os.path.basename(src) in HOT_KERNELS:
+        s_file = os.path.join(BUILD, os.path.basename(src) + ".s")
+        cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-S", src, "-o", s_file]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        with open(s_file) as f:
+            _check_hot_blocks(src, f.read())
     return obj
 
 

@@ -9,34 +9,35 @@
 //
 // Design (gfx950):
 //  * one work-group per compute unit (4 waves, one per SIMD); wave w owns
-//    heads [32w, 32w+32).  Its slice of Q~ stays in VGPRs for the whole
-//    segment (36 x 16 B per lane) and its 32 x 512 fp32 accumulator o~ in the
-//    accumulation registers (256 per lane).  All 128 heads read each cache
-//    row from LDS, so HBM sees every row exactly once.
-//  * 64-token tiles (one page slice, 72 KB contiguous in HBM) are streamed
-//    with 16-byte direct-to-LDS loads into a double buffer.  LDS rows are
-//    1152 B with the 16-byte chunks of row r XOR-permuted by a 3-bit function
-//    of r, chosen so that both read patterns below (32 rows at one chunk, and
-//    4 rows x 32 bytes per 16 lanes) are free of bank conflicts for 32- and
-//    64-bank LDS models.
+//    heads [32w, 32w+32).  Its slice of Q~ stays in registers for the whole
+//    segment (the 512 latent dims: 32 x 16 B per lane; the 64 RoPE dims of all
+//    heads sit in LDS) and its 32 x 512 fp32 accumulator o~ fills the
+//    accumulation registers (256 per lane).  All 128 heads read each cache row
+//    from LDS, so HBM sees every row once.
+//  * 32-token sub-tiles (36 KB, contiguous inside a page) stream through a
+//    four-slot LDS ring with 16-byte direct-to-LDS loads, three sub-tiles in
+//    flight.  Every wave issues the same number of loads per sub-tile, so the
+//    waits are static vmcnt counts; barriers skip __syncthreads' fence, which
+//    would drain the ring.  LDS rows are 1152 B with the 16-byte chunks of row
+//    r XOR-permuted by a 3-bit function of r, which makes both read patterns
+//    below free of bank conflicts.
 //  * scores: S^T[token][head] = C[token][dims] . Q~^T[dims][head] with
-//    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~ from VGPRs).
+//    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~), 36 K-steps.
 //  * softmax numerators in the log2 domain against a per-segment reference:
 //    the max of the segment's first 32 scores.  Later scores may exceed it by
 //    up to 64 (P <= 2^64, harmless in fp32/bf16), so the 256-register
 //    accumulator is never rescaled - VALU work on it would push the kernel
 //    out of its 512-register budget.  If any score in the work-group exceeds
-//    the reference by more than 64, the segment is redone: a scores-only pass
-//    finds the exact max, then a full pass uses it (correct for any input,
-//    essentially never taken).
+//    the reference by more than 64, the segment is redone once with the exact
+//    maximum, which the first pass tracks (correct for any input, essentially
+//    never taken).
 //  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T with the
-//    same MFMA.  The P operand comes straight from the score accumulators (the
-//    token order inside one K-step is permuted to match their layout); the
-//    C^T operand arrives already transposed from two ds_read_b64_tr_b16 per
-//    MFMA (each 16-lane group turns 4 rows x 16 dims into 16 lanes x 4 rows).
+//    same MFMA.  P comes straight from the score accumulators (rounded to
+//    bf16); C^T is read from the same LDS tile with ds_read_b128 and
+//    transposed in registers with v_perm_b32.
 //  * a work-group walks the segments the plan assigns to it and writes each
-//    segment's unnormalised (m, l, o~) straight from the accumulation
-//    registers, in register order; a merge kernel weighs the segments of each
+//    segment's unnormalised (m, l, o~) from the accumulation registers, o~ as
+//    bf16 in register order; a merge kernel weighs the segments of each
 //    sequence by e^(m_s - M) / sum_s l_s e^(m_s - M) and writes o~ as bf16.
 #include <math.h>
 
@@ -125,8 +126,13 @@ __device__ inline void load_sub(const u32x4* __restrict__ gsub, int nvalid, char
 __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ cache, int num_pages,
     const int32_t* __restrict__ page_table, int max_pages, int page, PlanPtrs plan,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  const int g = blockIdx.x;
+    __bf16* __restrict__ part_o, float* __restrict__ part_ml) {
+  // Work-groups are dispatched round-robin over the eight XCDs.  Give the
+  // work-groups of one XCD consecutive plan slots: consecutive slots share
+  // sequences, so a sequence's absorbed query is fetched into one L2.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int g = xcd * (G >> 3) + min(xcd, G & 7) + (blockIdx.x >> 3);
   if (g >= plan.counts[1]) return;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -335,17 +341,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       break;
     }
 
-    // ---- unnormalised partial (m, l, o~) in register order; merged later
+    // ---- unnormalised partial (m, l, o~): o~ rounded to bf16, in register
+    // order (8-byte piece 4x + a of a lane holds elements 4a .. 4a + 3 of
+    // accumulator x); merged later
     {
       int tl = threadIdx.x;
       asm volatile("" : "+v"(tl));  // form the per-lane address here, not at kernel entry
-      f32x4* dst = (f32x4*)(part_o + (long)k * kHeads * kDc) + tl;
+      uint2* dst = (uint2*)(part_o + (long)k * kHeads * kDc) + tl;
 #pragma unroll
       for (int x = 0; x < 16; ++x)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+          const float f0 = acc[x][4 * a], f1 = acc[x][4 * a + 1];
+          const float f2 = acc[x][4 * a + 2], f3 = acc[x][4 * a + 3];
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 p0 = {(__bf16)f0, (__bf16)f1}, p1 = {(__bf16)f2, (__bf16)f3};
           dst[(x * 4 + a) * kThreads] =
-              f32x4{acc[x][4 * a], acc[x][4 * a + 1], acc[x][4 * a + 2], acc[x][4 * a + 3]};
+              uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        }
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       if (h == 0) {
         int hd = head;
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
 constexpr int kCombSegs = 64;   // segments weighed per pass
 
 __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
-                                                         const float* __restrict__ part_o,
+                                                         const __bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          __bf16* __restrict__ lat_out) {
   __shared__ float w[kCombSegs][32];
@@ -393,7 +406,7 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
   }
   __syncthreads();
   const int lane = t & 63;
-  const int r0 = t >> 6;              // (x, a) combos r0 + 4r, r = 0..15
+  const int r0 = t >> 6;              // 8-byte pieces p = 4x + a = r0 + 4r, r = 0..15
   const int hd_l = lane & 31;
   f32x4 acc[16];
 #pragma unroll
@@ -409,9 +422,13 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     __syncthreads();
     for (int s = 0; s < nc; ++s) {
       const float ws = w[s][hd_l];
-      const f32x4* src = (const f32x4*)(part_o + (long)(k0 + c0 + s) * kHeads * kDc) + wv * 64 + lane;
+      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s) * kHeads * kDc) + wv * 64 + lane;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] += ws * src[(r0 + 4 * r) * kThreads];
+      for (int r = 0; r < 16; ++r) {
+        const uint2 v = src[(r0 + 4 * r) * kThreads];
+        acc[r] += ws * f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+      }
     }
   }
   // register order -> [head][dim]: accumulator x = 8q + j holds dims
@@ -437,19 +454,19 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
 
 hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
-                          int n_wg_launch, float* part_o, float* part_ml, hipStream_t s) {
+                          int n_wg_launch, void* part_o, float* part_ml, hipStream_t s) {
   if (n_wg_launch <= 0) return hipSuccess;
   hipLaunchKernelGGL(attn_v2_kernel, dim3(n_wg_launch), dim3(kThreads), 0, s,
                      (const __bf16*)q_abs, (const __bf16*)cache, num_pages, page_table, max_pages,
-                     g.page, plan, part_o, part_ml);
+                     g.page, plan, (__bf16*)part_o, part_ml);
   return hipGetLastError();
 }
 
-hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const float* part_o,
+hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan, part_o,
-                     part_ml, (__bf16*)lat_out);
+  hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan,
+                     (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   return hipGetLastError();
 }
 

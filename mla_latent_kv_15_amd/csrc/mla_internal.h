@@ -105,7 +105,9 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
 // ---------------------------------------------------------------------------
 hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
-                          int n_wg_launch, float* part_o, float* part_ml, hipStream_t s);
+                          int n_wg_launch, void* part_o, float* part_ml, hipStream_t s);
+// (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
+//  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
 // Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, X bf16 rows);
 // X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx.
 // out_f32: Y is fp32 partials [k_split][M][ldy]; else bf16 [M][ldy].
@@ -119,7 +121,7 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
                      hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
-hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const float* part_o,
+hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);
 
 }  // namespace mla

@@ -1,0 +1,47 @@
+"""The build's guard against spill code inside the attention kernel's MFMA
+blocks (host-side text check of the compiler's assembly)."""
+import pytest
+
+from mla_latent_kv_15_amd import build
+
+KERNEL = build.HOT_KERNELS["k_attn_v2.hip"]
+
+
+def _asm(body):
+    return "\n".join([f"_Z{KERNEL}v:                 ; @_Z{KERNEL}v", *body, ".Lfunc_end0:"])
+
+
+CLEAN = [
+    "\tscratch_store_dword off, v5, off offset:12 ; 4-byte Folded Spill",
+    ".LBB0_1:                    ;   in Loop: Header=BB0_1 Depth=1",
+    "\tds_read_b128 v[190:193], v148",
+    "\tv_mfma_f32_32x32x16_bf16 v[2:17], v[190:193], v[18:21], 0",
+    "\ts_cbranch_scc1 .LBB0_1",
+    ".LBB0_2:",
+    "\tscratch_load_dword v6, off, off offset:12 ; 4-byte Folded Reload",
+    "\ts_endpgm",
+]
+
+
+def test_spills_outside_mfma_blocks_pass():
+    build._check_hot_blocks("k_attn_v2.hip", _asm(CLEAN))
+
+
+@pytest.mark.parametrize("spill", [
+    "\tscratch_load_dword v6, off, off offset:12 ; 4-byte Folded Reload",
+    "\tv_accvgpr_read_b32 v2, a240",
+    "\tv_accvgpr_write_b32 a3, v7",
+])
+def test_spill_inside_an_mfma_block_fails(spill):
+    body = list(CLEAN)
+    body.insert(3, spill)
+    with pytest.raises(RuntimeError, match="spill code in MFMA blocks"):
+        build._check_hot_blocks("k_attn_v2.hip", _asm(body))
+
+
+def test_scratch_cap():
+    remarks = (f"remark: x.hip:1:0: Function Name: _Z{KERNEL}v\n"
+               f"remark: x.hip:1:0:     ScratchSize [bytes/lane]: {build.MAX_SCRATCH + 4}\n")
+    with pytest.raises(RuntimeError, match="scratch"):
+        build._check_scratch("k_attn_v2.hip", remarks)
+    build._check_scratch("k_attn_v2.hip", remarks.replace(str(build.MAX_SCRATCH + 4), "24"))
