@@ -8,19 +8,21 @@
 // sum of the latents o~_i = sum_j p_ij c^KV_j in 512-d latent space.
 //
 // Design (gfx950):
-//  * one work-group per compute unit (4 waves, one per SIMD); wave w owns
-//    heads [32w, 32w+32).  Its slice of Q~ stays in registers for the whole
-//    segment (the 512 latent dims: 32 x 16 B per lane; the 64 RoPE dims of all
-//    heads sit in LDS) and its 32 x 512 fp32 accumulator o~ fills the
-//    accumulation registers (256 per lane).  All 128 heads read each cache row
-//    from LDS, so HBM sees every row once.
-//  * 32-token sub-tiles (36 KB, contiguous inside a page) stream through a
-//    four-slot LDS ring with 16-byte direct-to-LDS loads, three sub-tiles in
-//    flight.  Every wave issues the same number of loads per sub-tile, so the
-//    waits are static vmcnt counts; barriers skip __syncthreads' fence, which
-//    would drain the ring.  LDS rows are 1152 B with the 16-byte chunks of row
-//    r XOR-permuted by a 3-bit function of r, which makes both read patterns
-//    below free of bank conflicts.
+//  * one work-group per compute unit (4 waves, one per SIMD).  For the scores
+//    wave w owns heads [32w, 32w+32) and keeps their whole absorbed query in
+//    registers (36 x 16 B per lane).  For the latent accumulation it owns
+//    latent dims [128w, 128w+128) of all 128 heads: a 128 x 128 fp32
+//    accumulator that fills the 256 accumulation registers.  The waves swap
+//    their softmax numerators P through LDS, so each wave reads only its
+//    quarter of the latent tile for the second contraction.
+//  * 32-token sub-tiles stream through a four-slot LDS ring with 16-byte
+//    direct-to-LDS buffer loads, two sub-tiles in flight while the scores of
+//    sub-tile j and the accumulation of sub-tile j-1 run.  A slot holds the
+//    32 latent parts (1024 B each) and then the 32 RoPE parts (128 B each);
+//    16-byte pieces are XOR-permuted per row so that every LDS read pattern
+//    below is free of bank conflicts, and each ring load covers exactly one
+//    row's latent part (or the RoPE parts of eight rows), which keeps its
+//    address arithmetic to one or two instructions.
 //  * scores: S^T[token][head] = C[token][dims] . Q~^T[dims][head] with
 //    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~), 36 K-steps.
 //  * softmax numerators in the log2 domain against a per-segment reference:
@@ -31,10 +33,11 @@
 //    the reference by more than 64, the segment is redone once with the exact
 //    maximum, which the first pass tracks (correct for any input, essentially
 //    never taken).
-//  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T with the
-//    same MFMA.  P comes straight from the score accumulators (rounded to
-//    bf16); C^T is read from the same LDS tile with ds_read_b128 and
-//    transposed in registers with v_perm_b32.
+//  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T.  Each
+//    lane reads 4 dims of 8 tokens (ds_read_b64) and transposes them with
+//    v_perm_b32 into the A operand; P^T comes from LDS.
+//  * the MFMA stream of an iteration interleaves the 36 score steps with the
+//    32 accumulation steps and the ring refill; sched_barrier pins the order.
 //  * a work-group walks the segments the plan assigns to it and writes each
 //    segment's unnormalised (m, l, o~) from the accumulation registers, o~ as
 //    bf16 in register order; a merge kernel weighs the segments of each
@@ -51,36 +54,34 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeads = 128;
-constexpr int kRow = 576;            // bf16 numbers per cached token
+constexpr int kRow = 576;             // bf16 numbers per cached token
 constexpr int kDc = 512;
-constexpr int kChunks = kRow / 8;    // 72 x 16 B per row
-constexpr int kRowBytes = kRow * 2;  // 1152
-constexpr int kSub = 32;             // tokens per sub-tile (one MFMA block)
-constexpr int kSlots = 4;            // LDS ring: one sub-tile computed, three in flight
-constexpr int kSubChunks = kSub * kChunks;           // 2304
-constexpr int kSubBytes = kSubChunks * 16;           // 36864
-constexpr int kSubInsts = kSubChunks / 64;           // 36 wave-wide loads per sub-tile
-constexpr int kInstsPerWave = kSubInsts / 4;         // 9
+constexpr int kRowBytes = kRow * 2;   // 1152: one cached row in HBM
+constexpr int kSub = 32;              // tokens per sub-tile (one MFMA block)
+constexpr int kSlots = 4;             // LDS ring slots
+constexpr int kLatBytes = 1024;       // LDS row of the latent part
+constexpr int kRopeBytes = 128;       // LDS row of the RoPE part
+constexpr int kRopeOff = kSub * kLatBytes;                 // 32768
+constexpr int kSubBytes = kRopeOff + kSub * kRopeBytes;    // 36864
+constexpr int kPBufOff = kSlots * kSubBytes;               // 147456
+constexpr int kPBufBytes = 4 * 2 * 64 * 16;                // [wave][K-step][lane][16 B]
+constexpr int kLdsBytes = kPBufOff + 2 * kPBufBytes;       // 163840 = 160 KB
+constexpr int kInstsPerWave = 9;      // ring loads per wave per sub-tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKSteps = kRow / 16;   // 36 score K-steps of 16 dims
-constexpr int kKReg = kDc / 16;      // 32 K-steps whose Q~ slice stays in VGPRs
+constexpr int kKSteps = kRow / 16;    // 36 score K-steps of 16 dims
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 64.0f;       // allowed score excess over the reference (log2 units)
+constexpr float kLazy = 64.0f;        // allowed score excess over the reference (log2 units)
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// one LDS object: the cache ring, then the query's RoPE slice
-constexpr int kQropeOff = kSlots * kSubBytes;        // 147456
-constexpr int kQropeBytes = kHeads * 64 * 2;         // 16384
-__device__ __shared__ __attribute__((aligned(16))) char g_tiles[kQropeOff + kQropeBytes];
-// rope part of the absorbed query (dims 512..575) for all 128 heads at
-// g_tiles + kQropeOff; chunk c of head i sits at chunk position c ^ swz(i)
+__device__ __shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
 
 // Work-group barrier without __syncthreads' release fence: that fence waits
 // for every outstanding vector memory operation, which would drain the
@@ -93,33 +94,51 @@ __device__ inline void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte chunk c of tile row r sits at chunk position c ^ swz(r) of that row
-__device__ inline int swz(int r) {
-  return ((((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1)) & 7;
+// 16-byte piece c of a row's RoPE part (8 pieces) sits at position
+// c ^ swz_rope(r) of LDS RoPE row r; piece c of the latent part (64 pieces)
+// sits at position c ^ (r & 15).
+__device__ inline int swz_rope(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+template <typename T>
+__device__ inline T lds_load(int byte) {
+  return *(const T __attribute__((address_space(3)))*)((lds_char*)g_lds + byte);
+}
+template <typename T>
+__device__ inline void lds_store(int byte, T v) {
+  *(T __attribute__((address_space(3)))*)((lds_char*)g_lds + byte) = v;
 }
 
-// Stream one 32-token sub-tile into LDS slot `buf`.  Rows at or past nvalid
-// re-read the last valid row (nvalid = 0: row 0 of the page passed in): their
-// scores are masked to zero weight, and the data stays finite, so
-// 0 * row never turns into NaN.  Every wave issues exactly kInstsPerWave loads
+// One 32-token sub-tile in flight: rows [0, 32) of a page run starting at
+// the resource's base go to LDS slot `slot`.  Rows at or past nvalid
+// (rmax = nvalid - 1) re-read row rmax: their scores are masked to zero
+// weight and the data stays finite, so 0 * row never turns into NaN.  Wave w
+// moves rows [8w, 8w+8): loads 0..7 the latent part of one row each, load 8
+// the RoPE parts of all eight.  Every wave issues exactly kInstsPerWave loads
 // per sub-tile whatever nvalid is; the ring's vmcnt bookkeeping relies on it.
-__device__ inline void load_sub(const u32x4* __restrict__ gsub, int nvalid, char* buf, int wave,
-                                int lane) {
-  // recompute the per-lane addresses at every call instead of keeping nine
-  // loop-invariant offsets live across the compute loop (VGPRs are scarce)
-  asm volatile("" : "+v"(lane));
-  const int rmax = max(nvalid - 1, 0);
-  // wave w fills rows [8w, 8w+8): its i-th load covers chunks [64i, 64i+64)
-  // of those 576, i.e. rows k_i and k_i + 1 with the switch at lane b_i
-#pragma unroll
-  for (int i = 0; i < kInstsPerWave; ++i) {
-    const int k = (64 * i) / kChunks;
-    const int bnd = kChunks * (k + 1) - 64 * i;
-    const bool second = lane >= bnd;
-    const int r = 8 * wave + k + (second ? 1 : 0);
-    const int cp = 64 * i - kChunks * k + lane - (second ? kChunks : 0);
-    __builtin_amdgcn_global_load_lds((const void*)(gsub + min(r, rmax) * kChunks + (cp ^ swz(r))),
-                                     (lds_void*)(buf + (8 * wave * kChunks + 64 * i) * 16), 16, 0, 0);
+//
+// The loads are MUBUF (buffer_load ... lds) rather than global_load_lds: the
+// compiler treats an outstanding FLAT-encoded LDS load as an LDS access of
+// unknown order and then waits for every LDS read with lgkmcnt(0), which
+// would serialise the operand prefetch of the compute loop.
+struct Refill {
+  __amdgpu_buffer_rsrc_t rs;
+  int slot;   // LDS byte offset of the ring slot
+  int rmax;
+};
+
+__device__ inline void ring_load(const Refill& rf, int i, int wave, int lane) {
+  int w = wave, l = lane;
+  asm volatile("" : "+s"(w), "+v"(l));  // recompute per call: no live per-load state
+  if (i < 8) {
+    const int r = 8 * w + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rf.rs, (lds_void*)((lds_char*)g_lds + rf.slot + r * kLatBytes), 16,
+        (l << 4) ^ ((r & 15) << 4), min(r, rf.rmax) * kRowBytes, 0, 0);
+  } else {
+    const int r = 8 * w + (l >> 3);   // this lane's row; piece l & 7 of its RoPE part
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rf.rs, (lds_void*)((lds_char*)g_lds + rf.slot + kRopeOff + 8 * w * kRopeBytes), 16,
+        min(r, rf.rmax) * kRowBytes + kLatBytes + (((l & 7) ^ swz_rope(r)) << 4), 0, 0, 0);
   }
 }
 
@@ -134,48 +153,77 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   const int xcd = blockIdx.x & 7;
   const int g = xcd * (G >> 3) + min(xcd, G & 7) + (blockIdx.x >> 3);
   if (g >= plan.counts[1]) return;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform: a scalar register, so the LDS destinations of the ring
+  // loads (M0) are scalar arithmetic rather than per-lane values
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;     // lane half
   const int m32 = lane & 31;
   const int head = wave * 32 + m32;
-  const u32x4* cache16 = (const u32x4*)cache;
-  lds_char* const lds = (lds_char*)g_tiles;
 
-  // Per-lane LDS byte offsets inside a 32-token block (row 0 of the block is
-  // a multiple of 16, so the swizzle only sees the low 4 row bits).
-  // scores: row m32, chunk 2ks + h   -> qoff[ks & 3] + 128 * (ks >> 2)
-  int qoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qoff[j] = m32 * kRowBytes + (((2 * j + h) ^ swz(m32)) << 4);
-  // latent accumulation: element e = 4a + c of lane (m32, h) is token row
-  // 8a + 4h + c of the K-step; it reads 16-byte chunk m32 (+32 per quarter)
-  int voff[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-    voff[e] = row * kRowBytes + ((m32 ^ swz(row)) << 4);
-  }
+  // Per-lane LDS byte offsets (slot base added per iteration; it is a
+  // multiple of 4096, so it never meets the XOR-ed bits 4..7).
+  // scores, latent K-step ks: row m32, piece 2ks + h at position
+  // (2ks + h) ^ (m32 & 15)  ->  (qa ^ ((ks & 7) << 5)) + 256 (ks >> 3)
+  const int qa = m32 * kLatBytes + ((h ^ (m32 & 15)) << 4);
+  // scores, RoPE K-step 32 + r: row m32, RoPE piece 2r + h -> qra ^ (r << 5)
+  const int qra = kRopeOff + m32 * kRopeBytes + ((h ^ swz_rope(m32)) << 4);
+  // accumulation, element e = 4a + c of the 8 tokens of lane (m32, h): token
+  // row R = 16 kap + 8a + 4h + c, dims 4 m32 .. 4 m32 + 3 of this wave's 128,
+  // i.e. latent piece 16w + (m32 >> 1), half m32 & 1:
+  // (pa ^ ((8a + c) << 4)) + (16 kap + 8a + c) * 1024
+  const int pa = 4 * h * kLatBytes + 256 * wave + (((m32 >> 1) ^ (4 * h)) << 4) + 8 * (m32 & 1);
 
   const int k_begin = plan.wg_seg_start[g];
   const int k_end = plan.wg_seg_start[g + 1];
   for (int k = k_begin; k < k_end; ++k) {
     const Seg sg = plan.segs[k];
     const int b = sg.b;
-
-    // absorbed query slice -> VGPRs (B operand: lane = head, 8 dims per K-step half)
-    bf16x8 qreg[kKReg];
-    {
-      int hd = head, hh = h;
-      asm volatile("" : "+v"(hd), "+v"(hh));
-      const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
-#pragma unroll
-      for (int ks = 0; ks < kKReg; ++ks) qreg[ks] = qs[2 * ks];
-    }
-    f32x16 acc[16];
-    float m_ref = -INFINITY;  // exponent reference (log2 units), fixed within a pass
-    float l_run = 0.f;
+    const int nsub = (sg.t1 - sg.t0 + kSub - 1) / kSub;
     bool bad = false;
+
+    // Page ids of the segment, 64 pages per window: lane i holds the id of
+    // page wb + i (-1 past the table row).  A vector register instead of
+    // scalar loads: an outstanding scalar load would force a full LDS wait
+    // (lgkmcnt(0)) at every use of an LDS read in the loop below.
+    int wb = 0;
+    auto load_window = [&]() {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int p = wb + ln;
+      const int v = p < max_pages ? page_table[(long)b * max_pages + p] : -1;
+      // consume the load here: a page-id load left in flight into the loop
+      // would make the compiler wait for all vector memory operations
+      // (vmcnt(0)) before each later page lookup, draining the ring
+      asm volatile("" ::"v"(v));
+      return v;
+    };
+    int pid = 0;
+    // sub-tile jj of the segment: tokens [t0 + 32 jj, ...) inside one page;
+    // a pass refills in increasing jj from the window set at its start
+    auto refill = [&](int jj) {
+      const int tt = sg.t0 + jj * kSub;
+      const int pi = tt / page;
+      if (pi - wb >= 64) {  // next window (segments longer than 64 pages)
+        wb += 64 * ((pi - wb) >> 6);
+        pid = load_window();
+      }
+      const int pg = __builtin_amdgcn_readlane(pid, pi - wb);
+      const bool ok = pg >= 0 && pg < num_pages;
+      bad |= !ok;
+      const long row0 = ok ? (long)pg * page + tt % page : 0;
+      Refill rf;
+      rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
+                                                kRsrcWord3);
+      rf.slot = (jj % kSlots) * kSubBytes;
+      rf.rmax = ok ? min(kSub, sg.t1 - tt) - 1 : 0;
+      return rf;
+    };
+
+    f32x16 acc[16];          // acc[4 mb + n]: dims block mb of this wave x head block n
+    bf16x8 qreg[kKSteps];    // absorbed query, B operand (lane = head, 8 dims per K-step half)
+    float m_ref = -INFINITY; // exponent reference (log2 units), fixed within a pass
+    float l_run = 0.f;
     // pass 0: reference = max of the first 32 tokens; every sub-tile's max is
     // tracked, so after a pass-0 overflow the exact segment max is known and
     // pass 1 redoes the segment with it as the reference
@@ -189,149 +237,208 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       float m_seen = -INFINITY;
       bool over = false;
 
-      __syncthreads();  // every wave is done with the ring and the query buffer
+      __syncthreads();  // every wave is done with the ring and the P buffers
       {
-        // rope part of Q~ for all heads -> LDS: 1024 chunks, 4 per thread
+        // P buffer 1 reads as the P of sub-tile -1 in iteration 0: zero it
+        const u32x4 z = {};
         int tl = threadIdx.x;
         asm volatile("" : "+v"(tl));
+        lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * tl, z);
+        lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * (tl + kThreads), z);
+      }
+      {
+        int hd = head, hh = h;
+        asm volatile("" : "+v"(hd), "+v"(hh));
+        const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int e = tl + kThreads * u;
-          const int hd = e >> 3, c = e & 7;
-          const u32x4 v = *(const u32x4*)(q_abs + ((long)b * kHeads + hd) * kRow + kDc + 8 * c);
-          *(u32x4*)(g_tiles + kQropeOff + hd * 128 + ((c ^ swz(hd)) << 4)) = v;
+        for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qs[2 * ks];
+      }
+      // page window of the segment's first 64 pages (a redo pass starts over)
+      wb = sg.t0 / page;
+      pid = load_window();
+      {
+        const Refill r0 = refill(0);
+#pragma unroll
+        for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
+        if (nsub > 1) {
+          const Refill r1 = refill(1);
+#pragma unroll
+          for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
         }
       }
-      const int nsub = (sg.t1 - sg.t0 + kSub - 1) / kSub;
-      // sub-tile j of the segment: tokens [t0 + 32j, ...) inside one page
-      auto issue = [&](int j) {
-        const int tt = sg.t0 + j * kSub;
-        const int pg = page_table[(long)b * max_pages + tt / page];
-        const bool ok = pg >= 0 && pg < num_pages;
-        bad |= !ok;
-        const long slot0 = ok ? (long)pg * page + tt % page : 0;
-        load_sub(cache16 + slot0 * kChunks, ok ? min(kSub, sg.t1 - tt) : 0,
-                 g_tiles + (j % kSlots) * kSubBytes, wave, lane);
-      };
-      for (int j = 0; j < kSlots - 1 && j < nsub; ++j) issue(j);
+      // the query must have landed before the loop: a query load left in
+      // flight would make the compiler wait inside the loop behind ring loads
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qreg[ks]));
 
+      // Software pipeline over sub-tiles: iteration j computes the scores of
+      // sub-tile j interleaved with the latent accumulation of sub-tile j-1
+      // (its P, written to LDS at the end of iteration j-1) and with the ring
+      // loads of sub-tile j+2; the softmax of j overlaps the last quarter of
+      // j-1's accumulation.  Iteration 0 accumulates P = 0 over sub-tile 0;
+      // iteration nsub only drains (its scores are fully masked).
 #pragma clang loop unroll(disable)
-      for (int j = 0; j < nsub; ++j) {
-        // sub-tile j is complete once at most the loads of the sub-tiles
-        // issued after it are outstanding
-        const int later = min(kSlots - 2, nsub - 1 - j);
+      for (int j = 0; j <= nsub; ++j) {
         static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
-        if (later >= 2)
-          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (later == 1)
+        if (j + 1 < nsub)
           asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
         else
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // the ring slot after the last sub-tile is free at the last iteration;
-        // it carries the work-group's redo flag
-        if (j == nsub - 1 && threadIdx.x == 0) {
-          *(int __attribute__((address_space(3)))*)(lds + (nsub % kSlots) * kSubBytes) = 0;
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // the ring slot of sub-tile nsub is free from iteration nsub - 1 on
+        // (its previous sub-tile, nsub - 4, was last read in iteration
+        // nsub - 3); it carries the work-group's redo flag
+        if (j == nsub - 1 && threadIdx.x == 0) lds_store<int>((nsub % kSlots) * kSubBytes, 0);
+        // this wave's P of sub-tile j-1 (and the flag) are in LDS before the barrier
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();  // sub-tile j landed everywhere; sub-tile j-2's slot is free
+
+        const int nvalid = j < nsub ? min(kSub, sg.t1 - (sg.t0 + j * kSub)) : 0;
+        const bool more = j + 2 < nsub;
+        Refill rf{};
+        if (more) rf = refill(j + 2);
+        const int sq = (j % kSlots) * kSubBytes;                     // scores tile
+        const int sv = ((j == 0 ? 0 : j - 1) % kSlots) * kSubBytes;  // accumulation tile
+        const int prd = kPBufOff + ((j + 1) & 1) * kPBufBytes;       // P of sub-tile j-1
+        const int pwr = kPBufOff + (j & 1) * kPBufBytes;             // P of sub-tile j
+
+        // ---- scores for 32 tokens x 32 heads (inline asm with a VGPR
+        // accumulator: with the builtin the compiler puts S in the
+        // accumulation registers, which o~ already fills, and spills).
+        // Back-to-back accumulation into the same registers needs no wait
+        // states; the s_nop before the softmax covers MFMA-result -> VALU.
+        f32x16 S;
+        bf16x8 abuf[2];
+        const int qab = sq + qa, qrb = sq + qra;
+        auto a_read = [&](int ks) {
+          return ks < 32 ? lds_load<bf16x8>((qab ^ ((ks & 7) << 5)) + 256 * (ks >> 3))
+                         : lds_load<bf16x8>(qrb ^ ((ks - 32) << 5));
+        };
+        abuf[0] = a_read(0);
+        abuf[1] = a_read(1);
+        auto qk = [&](int ks) {
+          // take this K-step's operand before its buffer slot is refilled
+          const bf16x8 a = abuf[ks & 1];
+          if (ks + 2 < kKSteps) abuf[ks & 1] = a_read(ks + 2);
+          if (ks == 0)
+            // early clobber: the destination must not overlap the A/B operands
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(qreg[ks]));
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(qreg[ks]));
+        };
+
+        // ---- latent accumulation of sub-tile j-1, K-step kap (16 tokens):
+        // 8 x ds_read_b64 -> 16 v_perm_b32 -> A operands of the 4 dims blocks
+        const int pvb = sv + pa;
+        u32x2 raw[8];
+        bf16x8 A[4];
+        auto pv_read = [&](int kap) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int a = e >> 2, c = e & 3;
+            raw[e] = lds_load<u32x2>((pvb ^ ((8 * a + c) << 4)) + (16 * kap + 8 * a + c) * kLatBytes);
+          }
+        };
+        auto pv_build = [&]() {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            u32x4 t;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+              t[f] = __builtin_amdgcn_perm(raw[2 * f + 1][mb >> 1], raw[2 * f][mb >> 1],
+                                           (mb & 1) ? 0x07060302u : 0x05040100u);
+            A[mb] = __builtin_bit_cast(bf16x8, t);
+          }
+        };
+        // P^T of head block n, K-step kap (written by wave n)
+        auto p_read = [&](int kap, int n) {
+          int l = lane;
+          asm volatile("" : "+v"(l));
+          return lds_load<bf16x8>(prd + (2 * n + kap) * 1024 + 16 * l);
+        };
+        bf16x8 B[2];
+        auto pv_mfma = [&](int mb, int n) {
+          acc[4 * mb + n] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb], B[n & 1], acc[4 * mb + n], 0, 0, 0);
+        };
+
+        pv_read(0);
+        B[0] = p_read(0, 0);
+        // 36 regions, one score MFMA each; sched_barrier pins the interleave
+        // (left alone, the scheduler clusters the builtin MFMAs away from the
+        // inline-asm ones).  Regions 0..8 also issue the ring loads of
+        // sub-tile j+2; K-step 0 of the accumulation runs in regions 3..18,
+        // the first half of K-step 1 in regions 20..27, its second half after
+        // the score chain, beside the softmax.
+#pragma unroll
+        for (int r = 0; r < kKSteps; ++r) {
+          qk(r);
+          if (r < kInstsPerWave && more) ring_load(rf, r, wave, lane);
+          if (r == 2 || r == 19) pv_build();
+          if (r == 14) pv_read(1);
+          if (r >= 3 && r < 19) {
+            const int idx = r - 3, n = idx >> 2, mb = idx & 3;
+            if (mb == 0) B[(n + 1) & 1] = n < 3 ? p_read(0, n + 1) : p_read(1, 0);
+            pv_mfma(mb, n);
+          }
+          if (r >= 20 && r < 28) {
+            const int idx = r - 20, n = idx >> 2, mb = idx & 3;
+            if (mb == 0) B[(n + 1) & 1] = p_read(1, n + 1);
+            pv_mfma(mb, n);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        lds_barrier();  // sub-tile j landed everywhere; slot (j+3)%4 is free
-        const int nvalid = min(kSub, sg.t1 - (sg.t0 + j * kSub));
-        lds_char* bb = lds + (j % kSlots) * kSubBytes;
-        {
-          // ---- scores for 32 tokens x 32 heads, A operand prefetched 4 deep.
-          // The MFMA chain is written as inline asm with a VGPR ("v")
-          // accumulator: with the builtin the compiler puts S in the
-          // accumulation registers, which the 32 x 512 o~ accumulator already
-          // fills, and then spills o~.  Back-to-back accumulation into the
-          // same registers needs no wait states; the s_nop after the chain
-          // covers the MFMA-result -> VALU-read hazard.
-          f32x16 S;
-          bf16x8 abuf[4];
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) abuf[ks] = *(const bf16x8 __attribute__((address_space(3)))*)(bb + qoff[ks & 3] + 128 * (ks >> 2));
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            const bf16x8 a = abuf[ks & 3];
-            if (ks + 4 < kKSteps)
-              abuf[ks & 3] = *(const bf16x8 __attribute__((address_space(3)))*)(bb + qoff[(ks + 4) & 3] + 128 * ((ks + 4) >> 2));
-            const bf16x8 q = ks < kKReg
-                ? qreg[ks]
-                : *(const bf16x8 __attribute__((address_space(3)))*)(
-                      lds + kQropeOff + head * 128 + (((2 * (ks - kKReg) + h) ^ swz(head)) << 4));
-            if (ks == 0)
-              // early clobber: the destination must not overlap the A/B operands
-              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(q));
-            else
-              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(q));
-          }
-          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
-          // ---- softmax numerators (log2 domain), lane = head, 16 of the 32 tokens
-          if (nvalid < kSub) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int tok = 8 * (i >> 2) + 4 * h + (i & 3);
-              S[i] = tok < nvalid ? S[i] : -INFINITY;
-            }
-          }
-          float bm = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) bm = fmaxf(bm, S[i]);
-          bm = fmaxf(bm, __shfl_xor(bm, 32)) * kLog2e;
-          m_seen = fmaxf(m_seen, bm);
-          // pass 0 takes its reference from the first sub-tile (m_ref is -inf
-          // until then); the redo pass starts with the exact maximum
-          m_ref = (m_ref == -INFINITY) ? bm : m_ref;
-          over |= bm > m_ref + kLazy;
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
+
+        // ---- softmax numerators of sub-tile j (log2 domain), lane = head, 16
+        // of the 32 tokens; overlaps the rest of j-1's accumulation
+        if (nvalid < kSub) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], kLog2e, -m_ref));
-            l_run += S[i];
+            const int tok = 8 * (i >> 2) + 4 * h + (i & 3);
+            S[i] = tok < nvalid ? S[i] : -INFINITY;
           }
-          // ---- latent accumulation: o~^T[dims][head] += C^T . P^T, two K-steps
-          // of 16 tokens.  Lane (m32, h) reads the 16-byte chunk m32 of each
-          // quarter-row for its eight token rows and transposes the 8 x 8 bf16
-          // block in registers: M-block (q, j) holds dims 256q + 8m + j.
-          bf16x8 pb[2];
+        }
+        float bm = -INFINITY;
 #pragma unroll
-          for (int kap = 0; kap < 2; ++kap)
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, S[i]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                           false, false);
+          bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * kLog2e;
+        }
+        m_seen = fmaxf(m_seen, bm);
+        // pass 0 takes its reference from the first sub-tile (m_ref is -inf
+        // until then); the redo pass starts with the exact maximum
+        m_ref = (m_ref == -INFINITY) ? bm : m_ref;
+        over |= bm > m_ref + kLazy;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kap][e] = (__bf16)S[8 * kap + e];
-          // (a K-step past nvalid adds P = 0 times finite re-read rows)
+        for (int idx = 8; idx < 16; ++idx) {
+          const int n = idx >> 2, mb = idx & 3;
+          if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
+          pv_mfma(mb, n);
+        }
 #pragma unroll
-          for (int g8 = 0; g8 < 4; ++g8) {       // (kap, q) groups of 8 MFMAs
-            const int kap = g8 >> 1, q = g8 & 1;
-            u32x4 v[8];
+        for (int i = 0; i < 16; ++i) {
+          S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], kLog2e, -m_ref));
+          l_run += S[i];
+        }
+        // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
+        // half) for all four waves
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              v[e] = *(const u32x4 __attribute__((address_space(3)))*)(
-                  bb + 16 * kap * kRowBytes + voff[e] + 512 * q);
+        for (int kap = 0; kap < 2; ++kap) {
+          bf16x8 p;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              u32x4 lo, hi;
-#pragma unroll
-              for (int f = 0; f < 4; ++f) {
-                lo[f] = __builtin_amdgcn_perm(v[2 * f + 1][d], v[2 * f][d], 0x05040100u);
-                hi[f] = __builtin_amdgcn_perm(v[2 * f + 1][d], v[2 * f][d], 0x07060302u);
-              }
-              acc[8 * q + 2 * d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, lo), pb[kap], acc[8 * q + 2 * d], 0, 0, 0);
-              acc[8 * q + 2 * d + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, hi), pb[kap], acc[8 * q + 2 * d + 1], 0, 0, 0);
-            }
-          }
-          // refill the ring after this iteration's last LDS read (the
-          // compiler places a full vmcnt wait before LDS reads that follow a
-          // direct-to-LDS load in program order)
-          if (j + kSlots - 1 < nsub) issue(j + kSlots - 1);
+          for (int e = 0; e < 8; ++e) p[e] = (__bf16)S[8 * kap + e];
+          lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024 + 16 * lane, p);
         }
       }
       // a score more than kLazy above the reference anywhere in the work-group:
       // redo the segment with the exact maximum seen in this pass (rare)
       if (mode == 0) {
-        int __attribute__((address_space(3)))* flag =
-            (int __attribute__((address_space(3)))*)(lds + (nsub % kSlots) * kSubBytes);
-        if (over) *flag = 1;
+        const int flag = (nsub % kSlots) * kSubBytes;
+        if (over) lds_store<int>(flag, 1);
         __syncthreads();
-        const int redo = *flag;
+        const int redo = lds_load<int>(flag);
         if (redo) {
           m_ref = m_seen;
           mode = 1;
@@ -371,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// merge of the register-order partials: one work-group per (sequence, wave
-// slice of 32 heads).  o~ = sum_s e^(m_s - M) o~_s / sum_s e^(m_s - M) l_s.
+// merge of the register-order partials: one work-group per (sequence, head
+// block of 32).  o~ = sum_s e^(m_s - M) o~_s / sum_s e^(m_s - M) l_s.
 // ---------------------------------------------------------------------------
 constexpr int kCombSegs = 64;   // segments weighed per pass
 
@@ -383,17 +490,17 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
   __shared__ float w[kCombSegs][32];
   __shared__ float s_M[32], s_inv[32];
   __shared__ __bf16 stage[32][kDc + 8];
-  const int b = blockIdx.x, wv = blockIdx.y, t = threadIdx.x;
+  const int b = blockIdx.x, n = blockIdx.y, t = threadIdx.x;
   const int cnt = plan.seq_seg_count[b];
   const int k0 = plan.seq_seg_start[b];
-  __bf16* out = lat_out + ((long)b * kHeads + wv * 32) * kDc;
+  __bf16* out = lat_out + ((long)b * kHeads + n * 32) * kDc;
   if (cnt == 0) {
     for (int e = t; e < 32 * kDc; e += 256) out[e] = (__bf16)__builtin_nanf("");
     return;
   }
   // per-head max and normaliser
   if (t < 32) {
-    const int hd = wv * 32 + t;
+    const int hd = n * 32 + t;
     float M = -INFINITY;
     for (int s = 0; s < cnt; ++s) M = fmaxf(M, part_ml[((long)(k0 + s) * kHeads + hd) * 2]);
     float L = 0.f;
@@ -405,10 +512,11 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     s_inv[t] = 1.f / L;
   }
   __syncthreads();
-  const int lane = t & 63;
-  const int r0 = t >> 6;              // 8-byte pieces p = 4x + a = r0 + 4r, r = 0..15
+  // thread t takes lane t & 63 of the attention kernel's wave wo = t >> 6,
+  // whose accumulators x = 4 mb + n hold latent dims [128 wo, 128 wo + 128)
+  const int lane = t & 63, wo = t >> 6;
   const int hd_l = lane & 31;
-  f32x4 acc[16];
+  f32x4 acc[16];   // [4 mb + a]
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = f32x4{};
   for (int c0 = 0; c0 < cnt; c0 += kCombSegs) {
@@ -416,33 +524,33 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     __syncthreads();
     for (int e = t; e < nc * 32; e += 256) {
       const int s = e >> 5, hh = e & 31;
-      const float* ml = part_ml + ((long)(k0 + c0 + s) * kHeads + wv * 32 + hh) * 2;
+      const float* ml = part_ml + ((long)(k0 + c0 + s) * kHeads + n * 32 + hh) * 2;
       w[s][hh] = __expf(ml[0] - s_M[hh]) * s_inv[hh];
     }
     __syncthreads();
     for (int s = 0; s < nc; ++s) {
       const float ws = w[s][hd_l];
-      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s) * kHeads * kDc) + wv * 64 + lane;
+      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s) * kHeads * kDc) + t;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint2 v = src[(r0 + 4 * r) * kThreads];
-        acc[r] += ws * f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-      }
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint2 v = src[((4 * mb + n) * 4 + a) * kThreads];
+          acc[4 * mb + a] += ws * f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+        }
     }
   }
-  // register order -> [head][dim]: accumulator x = 8q + j holds dims
-  // 256q + 8m + j with row m = 8a + 4h + c for element i = 4a + c
+  // register order -> [head][dim]: element i = 4a + c of accumulator (mb, n)
+  // at lane (m32, hf) is head 32n + m32, dim 128 wo + 4 (8a + 4 hf + c) + mb
   const int hf = lane >> 5;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int xa = r0 + 4 * r;
-    const int x = xa >> 2, a = xa & 3;
-    const int q = x >> 3, j = x & 7;
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      stage[hd_l][256 * q + 8 * (8 * a + 4 * hf + c) + j] = (__bf16)acc[r][c];
-  }
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        stage[hd_l][128 * wo + 4 * (8 * a + 4 * hf + c) + mb] = (__bf16)acc[4 * mb + a][c];
   __syncthreads();
   for (int e = t; e < 32 * (kDc / 8); e += 256) {
     const int hh = e / (kDc / 8), c8 = e % (kDc / 8);
