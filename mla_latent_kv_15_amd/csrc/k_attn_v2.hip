@@ -199,24 +199,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       return v;
     };
     int pid = 0;
-    // sub-tile jj of the segment: tokens [t0 + 32 jj, ...) inside one page;
-    // a pass refills in increasing jj from the window set at its start
-    auto refill = [&](int jj) {
-      const int tt = sg.t0 + jj * kSub;
-      const int pi = tt / page;
-      if (pi - wb >= 64) {  // next window (segments longer than 64 pages)
-        wb += 64 * ((pi - wb) >> 6);
+    // Refill position: the next sub-tile to load is jj, tokens [tt, tt + 32)
+    // at offset po of page pi (sub-tiles never straddle a page: page is a
+    // multiple of 64 and segments start on 64-token boundaries or at 0).
+    // A pass refills jj = 0, 1, 2, ... in order from the window set at its start.
+    int rj = 0, rt = 0, rpi = 0, rpo = 0;
+    auto refill = [&]() {
+      if (rpi - wb >= 64) {  // next window (segments longer than 64 pages)
+        wb += 64 * ((rpi - wb) >> 6);
         pid = load_window();
       }
-      const int pg = __builtin_amdgcn_readlane(pid, pi - wb);
+      const int pg = __builtin_amdgcn_readlane(pid, rpi - wb);
       const bool ok = pg >= 0 && pg < num_pages;
       bad |= !ok;
-      const long row0 = ok ? (long)pg * page + tt % page : 0;
+      const long row0 = ok ? (long)pg * page + rpo : 0;
       Refill rf;
       rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
                                                 kRsrcWord3);
-      rf.slot = (jj % kSlots) * kSubBytes;
-      rf.rmax = ok ? min(kSub, sg.t1 - tt) - 1 : 0;
+      rf.slot = (rj % kSlots) * kSubBytes;
+      rf.rmax = ok ? min(kSub, sg.t1 - rt) - 1 : 0;
+      ++rj;
+      rt += kSub;
+      rpo += kSub;
+      if (rpo == page) {
+        rpo = 0;
+        ++rpi;
+      }
       return rf;
     };
 
@@ -256,12 +264,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       // page window of the segment's first 64 pages (a redo pass starts over)
       wb = sg.t0 / page;
       pid = load_window();
+      rj = 0;
+      rt = sg.t0;
+      rpi = wb;
+      rpo = sg.t0 - wb * page;
       {
-        const Refill r0 = refill(0);
+        const Refill r0 = refill();
 #pragma unroll
         for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
         if (nsub > 1) {
-          const Refill r1 = refill(1);
+          const Refill r1 = refill();
 #pragma unroll
           for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
         }
@@ -279,6 +291,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       // iteration nsub only drains (its scores are fully masked).
 #pragma clang loop unroll(disable)
       for (int j = 0; j <= nsub; ++j) {
+        // scalar set-up of the ring loads of sub-tile j+2 (issued below),
+        // ahead of the waits
+        const bool more = j + 2 < nsub;
+        Refill rf{};
+        if (more) rf = refill();
         static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
         if (j + 1 < nsub)
           asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
@@ -293,9 +310,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         lds_barrier();  // sub-tile j landed everywhere; sub-tile j-2's slot is free
 
         const int nvalid = j < nsub ? min(kSub, sg.t1 - (sg.t0 + j * kSub)) : 0;
-        const bool more = j + 2 < nsub;
-        Refill rf{};
-        if (more) rf = refill(j + 2);
         const int sq = (j % kSlots) * kSubBytes;                     // scores tile
         const int sv = ((j == 0 ? 0 : j - 1) % kSlots) * kSubBytes;  // accumulation tile
         const int prd = kPBufOff + ((j + 1) & 1) * kPBufBytes;       // P of sub-tile j-1
@@ -367,8 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // (left alone, the scheduler clusters the builtin MFMAs away from the
         // inline-asm ones).  Regions 0..8 also issue the ring loads of
         // sub-tile j+2; K-step 0 of the accumulation runs in regions 3..18,
-        // the first half of K-step 1 in regions 20..27, its second half after
-        // the score chain, beside the softmax.
+        // K-step 1 after the score chain, beside the softmax.
 #pragma unroll
         for (int r = 0; r < kKSteps; ++r) {
           qk(r);
@@ -378,11 +391,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           if (r >= 3 && r < 19) {
             const int idx = r - 3, n = idx >> 2, mb = idx & 3;
             if (mb == 0) B[(n + 1) & 1] = n < 3 ? p_read(0, n + 1) : p_read(1, 0);
-            pv_mfma(mb, n);
-          }
-          if (r >= 20 && r < 28) {
-            const int idx = r - 20, n = idx >> 2, mb = idx & 3;
-            if (mb == 0) B[(n + 1) & 1] = p_read(1, n + 1);
             pv_mfma(mb, n);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -398,9 +406,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
             S[i] = tok < nvalid ? S[i] : -INFINITY;
           }
         }
-        float bm = -INFINITY;
+        float mx[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, S[i]);
+        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(S[i], S[i + 8]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], mx[i + 4]);
+        float bm = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
                                                            false, false);
@@ -412,15 +423,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         m_ref = (m_ref == -INFINITY) ? bm : m_ref;
         over |= bm > m_ref + kLazy;
 #pragma unroll
-        for (int idx = 8; idx < 16; ++idx) {
+        for (int idx = 0; idx < 16; ++idx) {
           const int n = idx >> 2, mb = idx & 3;
           if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
           pv_mfma(mb, n);
+          if (idx < 8) {
+            S[2 * idx] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx], kLog2e, -m_ref));
+            S[2 * idx + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx + 1], kLog2e, -m_ref));
+          }
         }
+        {
+          float sm[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], kLog2e, -m_ref));
-          l_run += S[i];
+          for (int i = 0; i < 8; ++i) sm[i] = S[i] + S[i + 8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm[i] += sm[i + 4];
+          l_run += (sm[0] + sm[1]) + (sm[2] + sm[3]);
         }
         // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
         // half) for all four waves
