@@ -9,11 +9,13 @@
 //   o_i = W_UV,i o~_i             walkthrough §3 顺序 B (decompress once)
 //   u = W_O [o_0 | ... | o_127]   walkthrough step 5
 //
-// wgemm: a work-group owns 64 weight rows and a K slice; its four waves split
-// that slice four ways, each streaming 16-byte pieces of W straight into the
-// B operand of v_mfma_f32_16x16x32_bf16 (lane = weight row, 8 consecutive k),
-// with the activation rows as the A operand, then the four partial tiles are
-// summed in LDS in a fixed order.  Split-K across work-groups writes fp32
+// wgemm: one work-group per compute unit streams an equal share of W: 16 RB
+// weight rows times a K chunk, with RB and the chunk chosen per shape so that
+// the work-groups fill the GPU exactly (wgemm_tile).  Its four waves split the
+// chunk four ways; each streams 16-byte pieces of W straight into the B
+// operand of v_mfma_f32_16x16x32_bf16 (lane = weight row, 8 consecutive k) and
+// reuses each activation piece (A operand) for all RB row blocks.  The four
+// partial tiles are summed in LDS in a fixed order.  Split-K chunks write fp32
 // partials that a small kernel reduces in a fixed order (deterministic).
 #include "mla_internal.h"
 
@@ -25,85 +27,151 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kNT = 64;   // weight rows per work-group
 constexpr int kMT = 64;   // activation rows per work-group (4 MFMA blocks of 16)
+
+// "Blocked" activation layout [M / 64][K / 32][4][64][8]: the 16 x 32 A operand
+// of one MFMA (rows 16 mb .. 16 mb + 15 of a 64-row group, K-step t) is 1 KB
+// contiguous in lane order (lane 16 g + r holds row r, k = 32 t + 8 g .. + 7),
+// so a wave fetches it with one fully contiguous load instead of touching 16
+// rows.  Producers of GEMM inputs write it; rows past M are padding.
+__device__ inline long blk_index(int m, int k, int K) {
+  return ((((long)(m >> 6) * (K >> 5) + (k >> 5)) * 4 + ((m >> 4) & 3)) * 64 +
+          (((k >> 3) & 3) << 4) + (m & 15)) * 8 + (k & 7);
+}
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Y = alpha * X . W^T over one K split.  X row m of the n-th weight-row group
-// lives at X + (n / n_group) * x_group_stride + m * ldx.
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void wgemm_kernel(int M, int N, int K, int k_split,
+// Y = alpha * X . W^T over one K chunk.  Work-group (row group ng, chunk sp)
+// = blockIdx.x (ng fastest), activation block = blockIdx.y.  X row m of the
+// weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx.
+// NS > 0: each wave runs exactly NS K-steps of 32, fully unrolled (the
+// decode shapes); NS == 0: a loop over the steps, DEPTH dividing their count.
+template <int RB, int NS, int DEPTH, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int n_groups,
                                                        const __bf16* __restrict__ X, long ldx,
                                                        long x_group_stride, int n_group,
                                                        const __bf16* __restrict__ W,
                                                        void* __restrict__ Y, long ldy,
-                                                       long y_split_stride, float alpha) {
-  __shared__ f32x4 red[4][4][4][64];  // [wave][mb][nb][lane]
-  const int n0 = blockIdx.x * kNT;
-  const int split = blockIdx.y;
-  const int m0 = blockIdx.z * kMT;
+                                                       long y_split_stride, float alpha,
+                                                       int x_blocked, int y_blocked) {
+  __shared__ f32x4 red[4][RB][4][64];  // [wave][rb][mb][lane]
+  const int ng = blockIdx.x % n_groups, sp = blockIdx.x / n_groups;
+  const int n0 = ng * 16 * RB;
+  const int m0 = blockIdx.y * kMT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int kt = K / k_split;
-  const int kw = kt >> 2;
-  const int kbeg = split * kt + wave * kw + 8 * g;
+  const int kw = kc >> 2;                       // this wave's share of the chunk
+  const int kbeg = sp * kc + wave * kw + 8 * g;
   const int nmb = min(4, (M - m0 + 15) >> 4);
   const __bf16* xb = X + (long)(n0 / n_group) * x_group_stride;
   const bf16x8* xr[4];
+  int xstep;   // bf16x8 units from one K-step of an A operand to the next
+  if (x_blocked) {
+    const long blk = ((long)(m0 >> 6) * (K >> 5) + ((kbeg - 8 * g) >> 5)) * 4;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int m = min(m0 + mb * 16 + r16, M - 1);
-    xr[mb] = (const bf16x8*)(xb + (long)m * ldx + kbeg);
-  }
-  const bf16x8* wr[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) wr[nb] = (const bf16x8*)(W + (long)(n0 + nb * 16 + r16) * K + kbeg);
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{};
-
-#pragma unroll 4
-  for (int k = 0; k < kw; k += 32) {
-    bf16x8 b[4], a[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) b[nb] = wr[nb][k >> 3];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) a[mb] = xr[mb][k >> 3];
+    for (int mb = 0; mb < 4; ++mb) xr[mb] = (const bf16x8*)(xb + ((blk + mb) * 64 + lane) * 8);
+    xstep = 4 * 64;
+  } else {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      if (mb < nmb) {
+      const int m = min(m0 + mb * 16 + r16, M - 1);
+      xr[mb] = (const bf16x8*)(xb + (long)m * ldx + kbeg);
+    }
+    xstep = 4;
+  }
+  const bf16x8* wr[RB];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb], b[nb], acc[mb][nb]);
+  for (int rb = 0; rb < RB; ++rb) wr[rb] = (const bf16x8*)(W + (long)(n0 + rb * 16 + r16) * K + kbeg);
+
+  f32x4 acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[rb][mb] = f32x4{};
+
+  // Register ring of DEPTH K-steps of operands: step st + DEPTH is loaded
+  // while step st is multiplied, so DEPTH steps of W stay in flight.  All
+  // four activation blocks are multiplied (rows past M repeat row M-1; only
+  // rows < M are stored), which keeps the step free of branches.
+  bf16x8 bq[DEPTH][RB], aq[DEPTH][4];
+  auto load = [&](int d, int st) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) bq[d][rb] = wr[rb][4 * st];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) aq[d][mb] = xr[mb][xstep * st];
+  };
+  // inline asm with the accumulator tied in its accumulation registers: with
+  // the builtin, the register allocator renames the accumulators across the
+  // ring's phases and copies them back every iteration
+  auto step = [&](int d) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                     : "+a"(acc[rb][mb])
+                     : "v"(aq[d][mb]), "v"(bq[d][rb]));
+    // the refill of slot d stays after the MFMAs that read it: hoisted above
+    // them, it would need fresh registers and copies, and copying a load in
+    // flight waits for it
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load(d, d);
+  if constexpr (NS > 0) {
+    // straight-line code: the compiler waits for exactly the step it needs
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      step(st % DEPTH);
+      if (st + DEPTH < NS) load(st % DEPTH, st + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // generic shapes: the loads are unconditional (the last round re-reads
+    // the final step, unused); across the loop's back edge the compiler
+    // drains them at the top of each round
+    const int nsteps = kw >> 5;
+#pragma clang loop unroll(disable)
+    for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        step(d);
+        load(d, min(s0 + d + DEPTH, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
+  // MFMA result -> read by other instructions: wait states the compiler
+  // cannot see for inline-asm MFMAs
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int rb = 0; rb < RB; ++rb)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[rb][0]), "+a"(acc[rb][1]), "+a"(acc[rb][2]), "+a"(acc[rb][3]));
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) red[wave][mb][nb][lane] = acc[mb][nb];
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) red[wave][rb][mb][lane] = acc[rb][mb];
   __syncthreads();
   // wave w finishes activation block w: fixed-order sum over the four waves
   const int mb = wave;
   if (mb >= nmb) return;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    f32x4 v = red[0][mb][nb][lane];
-    v += red[1][mb][nb][lane];
-    v += red[2][mb][nb][lane];
-    v += red[3][mb][nb][lane];
-    const int n = n0 + nb * 16 + r16;
+  for (int rb = 0; rb < RB; ++rb) {
+    f32x4 v = red[0][rb][mb][lane];
+    v += red[1][rb][mb][lane];
+    v += red[2][rb][mb][lane];
+    v += red[3][rb][mb][lane];
+    const int n = n0 + rb * 16 + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + mb * 16 + 4 * g + i;
       if (m < M) {
         if (OUT_F32)
-          ((float*)Y)[split * y_split_stride + (long)m * ldy + n] = alpha * v[i];
+          ((float*)Y)[sp * y_split_stride + (long)m * ldy + n] = alpha * v[i];
+        else if (y_blocked)
+          ((__bf16*)Y)[blk_index(m, n, n_groups * 16 * RB)] = (__bf16)(alpha * v[i]);
         else
           ((__bf16*)Y)[(long)m * ldy + n] = (__bf16)(alpha * v[i]);
       }
@@ -112,14 +180,16 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(int M, int N, int K, int 
 }
 
 // out[m][n] = sum_s part[s][m][n] (fixed order), as bf16
+// (blocked: out in the blocked activation layout with K = N)
 __global__ void splitk_reduce_kernel(int M, int N, int S, const float* __restrict__ part,
-                                     long split_stride, __bf16* __restrict__ out, long ldo) {
+                                     long split_stride, __bf16* __restrict__ out, long ldo,
+                                     int blocked) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)M * N) return;
   const int m = (int)(idx / N), n = (int)(idx % N);
   float v = 0.f;
   for (int s = 0; s < S; ++s) v += part[s * split_stride + (long)m * N + n];
-  out[(long)m * ldo + n] = (__bf16)v;
+  out[blocked ? blk_index(m, n, N) : (long)m * ldo + n] = (__bf16)v;
 }
 
 // q~_i = scale * W_UK,i^T q^C_i for one head i (grid.x) and 64 batch rows
@@ -187,32 +257,93 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(int M, const __bf16* __r
 
 }  // namespace
 
-bool wgemm_shape_ok(int N, int K, int k_split) {
-  return N % kNT == 0 && k_split > 0 && K % (k_split * 128) == 0;
+// Tile choice: the share of a work-group is 16 rb weight rows x K / splits.
+// Among the tilings that divide the shape, take the one that keeps the most
+// compute units busy (work-groups / (rounds x CUs)), then the fewest K splits
+// (fewer partials to reduce), then the most rows per work-group (each
+// activation piece serves more MFMAs).  A group of n_group weight rows reads
+// its own activation rows, so a work-group's rows must lie in one group.
+GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split) {
+  const int G = auto_wg_budget();
+  GemmTile best{0, 0};
+  double best_eff = -1.0;
+  for (int rb = 5; rb >= 1; --rb) {
+    const int R = 16 * rb;
+    if (N % R != 0 || (n_group > 0 && n_group % R != 0)) continue;
+    for (int sp = 1; sp <= (allow_split ? 64 : 1); ++sp) {
+      if (K % (128 * sp) != 0) continue;
+      const long units = (long)(N / R) * sp;
+      const long rounds = (units + G - 1) / G;
+      const double eff = (double)units / (double)(rounds * G);
+      const bool better = eff > best_eff + 1e-9 ||
+                          (eff > best_eff - 1e-9 && (sp < best.splits ||
+                                                     (sp == best.splits && rb > best.rb)));
+      if (better) {
+        best = GemmTile{rb, sp};
+        best_eff = eff;
+      }
+    }
+  }
+  return best;
 }
 
-hipError_t wgemm(int M, int N, int K, int k_split, const void* X, long ldx, long x_group_stride,
-                 int n_group, const void* W, void* Y, long ldy, long y_split_stride, bool out_f32,
-                 float alpha, hipStream_t s) {
+hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
+                 long x_group_stride, int n_group, const void* W, void* Y, long ldy,
+                 long y_split_stride, bool out_f32, float alpha, hipStream_t s, bool x_blocked,
+                 bool y_blocked) {
   if (M <= 0) return hipSuccess;
-  dim3 grid(N / kNT, k_split, (M + kMT - 1) / kMT);
-  if (out_f32)
-    hipLaunchKernelGGL(wgemm_kernel<true>, grid, dim3(256), 0, s, M, N, K, k_split,
-                       (const __bf16*)X, ldx, x_group_stride, n_group, (const __bf16*)W, Y, ldy,
-                       y_split_stride, alpha);
-  else
-    hipLaunchKernelGGL(wgemm_kernel<false>, grid, dim3(256), 0, s, M, N, K, k_split,
-                       (const __bf16*)X, ldx, x_group_stride, n_group, (const __bf16*)W, Y, ldy,
-                       y_split_stride, alpha);
+  if (t.rb < 1 || t.rb > 5 || t.splits < 1 || N % (16 * t.rb) != 0 || K % (128 * t.splits) != 0 ||
+      (t.splits > 1 && !out_f32) || (y_blocked && (out_f32 || N % 32 != 0)) ||
+      (x_blocked && n_group > 0 && n_group != N))
+    return hipErrorInvalidValue;
+  const int n_groups = N / (16 * t.rb);
+  const int kc = K / t.splits;
+  const int nsteps = kc / 128;   // K-steps of 32 per wave
+  const int depth = nsteps % 4 == 0 ? 4 : 1;
+  const int xb = x_blocked ? 1 : 0, yb = y_blocked ? 1 : 0;
+  const dim3 grid(n_groups * t.splits, (M + kMT - 1) / kMT);
+  if (n_group <= 0) n_group = N;
+#define MLA_WGEMM_LAUNCH(RB, NS, D)                                                           \
+  do {                                                                                        \
+    if (out_f32)                                                                              \
+      hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, true>), grid, dim3(256), 0, s, M, K, kc,    \
+                         n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
+                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb);            \
+    else                                                                                      \
+      hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, false>), grid, dim3(256), 0, s, M, K, kc,   \
+                         n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
+                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb);            \
+    return hipGetLastError();                                                                 \
+  } while (0)
+  // fully unrolled variants for the decode projections' tiles on 256 CUs
+  // (W_O, W_UQ / W_UV, W_QR, W_DQ of the DeepSeek-V2 layer)
+  if (t.rb == 5 && nsteps == 32) MLA_WGEMM_LAUNCH(5, 32, 4);
+  if (t.rb == 4 && nsteps == 12) MLA_WGEMM_LAUNCH(4, 12, 4);
+  if (t.rb == 4 && nsteps == 4) MLA_WGEMM_LAUNCH(4, 4, 4);
+  if (t.rb == 2 && nsteps == 12) MLA_WGEMM_LAUNCH(2, 12, 4);
+  if (t.rb == 3 && nsteps == 5) MLA_WGEMM_LAUNCH(3, 5, 5);
+#define MLA_WGEMM_CASE(RB)                                               \
+  case RB:                                                               \
+    if (depth == 4) MLA_WGEMM_LAUNCH(RB, 0, 4);                          \
+    MLA_WGEMM_LAUNCH(RB, 0, 1);
+  switch (t.rb) {
+    MLA_WGEMM_CASE(1)
+    MLA_WGEMM_CASE(2)
+    MLA_WGEMM_CASE(3)
+    MLA_WGEMM_CASE(4)
+    MLA_WGEMM_CASE(5)
+  }
+#undef MLA_WGEMM_CASE
+#undef MLA_WGEMM_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
-                         long ldo, hipStream_t s) {
+                         long ldo, hipStream_t s, bool blocked) {
   long n = (long)M * N;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
-                     N, S, part, split_stride, (__bf16*)out, ldo);
+                     N, S, part, split_stride, (__bf16*)out, ldo, blocked ? 1 : 0);
   return hipGetLastError();
 }
 

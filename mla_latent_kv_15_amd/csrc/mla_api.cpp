@@ -70,17 +70,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 // ---------------------------------------------------------------------------
 // workspace layouts
 // ---------------------------------------------------------------------------
-// split-K factors of the MFMA decode GEMMs (W_DQ over d, W_O over n_h*d_h)
-int split_dq(const Geo& g) {
-  for (int sk = 10; sk > 1; --sk)
-    if (g.d % (sk * 128) == 0) return sk;
-  return 1;
-}
-int split_o(const Geo& g) {
-  for (int sk = 8; sk > 1; --sk)
-    if ((g.n_h * g.d_h) % (sk * 128) == 0) return sk;
-  return 1;
-}
+// tiles of the MFMA decode GEMMs (the same choice sizes the workspace and runs)
+// rows of the blocked activation buffers (multiples of 64)
+size_t pad64(int B) { return ((size_t)B + 63) / 64 * 64; }
+GemmTile tile_dq(const Geo& g) { return wgemm_tile(g.d_cq, g.d, 0, true); }
+GemmTile tile_uq(const Geo& g) { return wgemm_tile(g.n_h * g.d_h, g.d_cq, 0, false); }
+GemmTile tile_qr(const Geo& g) { return wgemm_tile(g.n_h * g.d_r, g.d_cq, 0, false); }
+GemmTile tile_uv(const Geo& g) { return wgemm_tile(g.n_h * g.d_h, g.d_c, g.d_h, false); }
+GemmTile tile_o(const Geo& g) { return wgemm_tile(g.d, g.n_h * g.d_h, 0, true); }
 
 struct QueryWs {
   float *cq, *qc, *qr;   // generic: fp32 intermediates
@@ -89,8 +86,8 @@ struct QueryWs {
 };
 void carve_query(Carver& c, const Geo& g, int B, QueryWs* w) {
   if (is_v2_fast(g)) {
-    w->cq_part = (float*)c.take(sizeof(float) * (size_t)split_dq(g) * B * g.d_cq);
-    w->cq16 = c.take(2 * (size_t)B * g.d_cq);
+    w->cq_part = (float*)c.take(sizeof(float) * (size_t)tile_dq(g).splits * B * g.d_cq);
+    w->cq16 = c.take(2 * (size_t)pad64(B) * g.d_cq);   // blocked activation layout
     w->qc16 = c.take(2 * (size_t)B * g.n_h * g.d_h);
     w->qr = (float*)c.take(sizeof(float) * (size_t)B * g.n_h * g.d_r);
     w->cq = w->qc = nullptr;
@@ -124,8 +121,8 @@ struct OutWs {
 };
 void carve_out(Carver& c, const Geo& g, int B, OutWs* w) {
   if (is_v2_fast(g)) {
-    w->o16 = c.take(2 * (size_t)B * g.n_h * g.d_h);
-    w->u_part = (float*)c.take(sizeof(float) * (size_t)split_o(g) * B * g.d);
+    w->o16 = c.take(2 * (size_t)pad64(B) * g.n_h * g.d_h);   // blocked activation layout
+    w->u_part = (float*)c.take(sizeof(float) * (size_t)tile_o(g).splits * B * g.d);
     w->o = nullptr;
     return;
   }
@@ -203,17 +200,18 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
   QueryWs q;
   carve_query(c, g, B, &q);
   if (is_v2_fast(g)) {
-    const int sk = split_dq(g);
+    const GemmTile tdq = tile_dq(g);
     const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
     // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16
-    MLA_TRY(wgemm(B, g.d_cq, g.d, sk, h, g.d, 0, g.d_cq, w->W_DQ, q.cq_part, g.d_cq,
+    MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
                   (long)B * g.d_cq, true, 1.f, s));
-    MLA_TRY(splitk_reduce(B, g.d_cq, sk, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s));
+    MLA_TRY(splitk_reduce(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s,
+                          true));
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
-    MLA_TRY(wgemm(B, (int)nq, g.d_cq, 1, q.cq16, g.d_cq, 0, (int)nq, w->W_UQ, q.qc16, nq, 0,
-                  false, 1.f, s));
-    MLA_TRY(wgemm(B, (int)nr, g.d_cq, 1, q.cq16, g.d_cq, 0, (int)nr, w->W_QR, q.qr, nr, 0, true,
-                  1.f, s));
+    MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
+                  false, 1.f, s, true));
+    MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
+                  true, 1.f, s, true));
     // absorbed query q~_i = W_UK,i^T q^C_i, scaled (order B)
     MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, s));
     MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
@@ -294,14 +292,14 @@ int run_output(const Geo& g, const mla_weights* w, const void* lat, int B, void*
   carve_out(c, g, B, &o);
   if (is_v2_fast(g)) {
     const long nq = (long)g.n_h * g.d_h;
-    const int sk = split_o(g);
+    const GemmTile to = tile_o(g);
     // o_i = W_UV,i o~_i: weight rows of head i read the latent row of head i
-    MLA_TRY(wgemm(B, (int)nq, g.d_c, 1, lat, (long)g.n_h * g.d_c, g.d_c, g.d_h, w->W_UV, o.o16,
-                  nq, 0, false, 1.f, s));
+    MLA_TRY(wgemm(tile_uv(g), B, (int)nq, g.d_c, lat, (long)g.n_h * g.d_c, g.d_c, g.d_h, w->W_UV,
+                  o.o16, nq, 0, false, 1.f, s, false, true));
     // u = W_O [o_0 | ... | o_{n_h-1}], split over n_h*d_h, reduced to bf16
-    MLA_TRY(wgemm(B, g.d, (int)nq, sk, o.o16, nq, 0, g.d, w->W_O, o.u_part, g.d, (long)B * g.d,
-                  true, 1.f, s));
-    MLA_TRY(splitk_reduce(B, g.d, sk, o.u_part, (long)B * g.d, out, g.d, s));
+    MLA_TRY(wgemm(to, B, g.d, (int)nq, o.o16, nq, 0, 0, w->W_O, o.u_part, g.d, (long)B * g.d, true,
+                  1.f, s, true));
+    MLA_TRY(splitk_reduce(B, g.d, to.splits, o.u_part, (long)B * g.d, out, g.d, s));
     return MLA_OK;
   }
   const GType T = st(g);

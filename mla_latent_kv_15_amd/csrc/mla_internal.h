@@ -109,14 +109,23 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, in
 // (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
 //  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
 // Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, X bf16 rows);
-// X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx.
-// out_f32: Y is fp32 partials [k_split][M][ldy]; else bf16 [M][ldy].
-bool wgemm_shape_ok(int N, int K, int k_split);
-hipError_t wgemm(int M, int N, int K, int k_split, const void* X, long ldx, long x_group_stride,
-                 int n_group, const void* W, void* Y, long ldy, long y_split_stride, bool out_f32,
-                 float alpha, hipStream_t s);
+// X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx
+// (n_group <= 0: one group).  A work-group streams 16 rb rows x K / splits.
+// splits > 1 requires out_f32: Y is fp32 partials [splits][M][ldy]; else Y is
+// [M][ldy], bf16 or fp32.  x_blocked: X (ungrouped) is in the blocked
+// activation layout [ceil(M/64)][K/32][4][64][8] (1 KB per MFMA operand, rows
+// padded to 64); y_blocked: bf16 Y is written in that layout with K = N.
+struct GemmTile {
+  int rb;       // weight rows per work-group / 16 (1..5)
+  int splits;   // K chunks
+};
+GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split);
+hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
+                 long x_group_stride, int n_group, const void* W, void* Y, long ldy,
+                 long y_split_stride, bool out_f32, float alpha, hipStream_t s,
+                 bool x_blocked = false, bool y_blocked = false);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
-                         long ldo, hipStream_t s);
+                         long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16).
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
                      hipStream_t s);
