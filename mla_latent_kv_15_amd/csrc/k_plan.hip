@@ -17,152 +17,153 @@ namespace mla {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;   // one chunk of sequences per pass (4 waves)
 
-__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  // Hillis-Steele over 1024 threads in LDS.
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    int add = (t >= off) ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+// Exclusive prefix sum over the work-group (wave scans + 4 wave totals).
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int incl = tmp[t];
-  *total = tmp[kPlanThreads - 1];
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    base += i < w ? wsum[i] : 0;
+    tot += wsum[i];
+  }
+  __syncthreads();   // wsum is reused by the next scan
+  *total = tot;
+  return base + x - v;
 }
 
 __device__ inline bool len_valid(int len, int max_kv_len, int cap) {
   return len >= 1 && len <= max_kv_len && len <= cap;
 }
 
-// number of g in [0, G] with floor(g*T/G) <= y   (T >= G >= 1, y >= 0)
-__device__ inline long count_le(long y, long T, long G) {
-  long c = ((y + 1) * G + T - 1) / T;  // ceil((y+1)G/T) = #g with g*T < (y+1)*G
-  return c > G + 1 ? G + 1 : c;
-}
+// Work-group g (of G) owns tiles [w(g), w(g+1)), w(g) = floor(g T / G).
+__device__ inline long wg_first_tile(long g, long T, long G) { return g * T / G; }
+// the work-group owning tile x: the largest g with w(g) <= x, ceil((x+1) G / T) - 1
+__device__ inline long wg_of_tile(long x, long T, long G) { return ((x + 1) * G + T - 1) / T - 1; }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     PlanPtrs p, const int32_t* __restrict__ kv_lens, int B, int max_kv_len, int max_pages,
     int page, int tile, int num_splits, int max_wg) {
-  __shared__ int tmp[kPlanThreads];
-  __shared__ long s_tile_base;
-  __shared__ int s_seg_base;
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ int s_kseq[kPlanThreads + 1];   // first segment of each sequence of the chunk
+  __shared__ long s_sb[kPlanThreads];        // first tile (global) of each sequence
+  __shared__ int s_len[kPlanThreads], s_tiles[kPlanThreads];
+  __shared__ long s_g0[kPlanThreads];        // work-group owning each sequence's first tile
   const int t = threadIdx.x;
   const long cap = (long)max_pages * page;
   const int capi = cap > 0x7fffffffL ? 0x7fffffff : (int)cap;
+  auto tiles_of = [&](int b, int* len) {
+    int l = b < B ? kv_lens[b] : 0;
+    if (!len_valid(l, max_kv_len, capi)) l = 0;
+    *len = l;
+    return (l + tile - 1) / tile;
+  };
 
-  // ---- pass 1: total tiles over valid sequences
-  if (t == 0) s_tile_base = 0;
-  __syncthreads();
-  long total_tiles = 0;
+  // ---- total tiles over the valid sequences (one chunk: kept for pass 2)
+  const bool one_chunk = B <= kPlanThreads;
+  int len0 = 0, tiles0 = 0, off0 = 0;
+  long T = 0;
   for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
-    int b = c0 + t;
-    int tiles = 0;
-    if (b < B) {
-      int len = kv_lens[b];
-      if (len_valid(len, max_kv_len, capi)) tiles = (len + tile - 1) / tile;
+    int len, tot;
+    const int tl = tiles_of(c0 + t, &len);
+    const int off = block_exclusive_scan(tl, wsum, &tot);
+    if (one_chunk) {
+      len0 = len;
+      tiles0 = tl;
+      off0 = off;
     }
-    int tot;
-    block_exclusive_scan(tiles, tmp, &tot);
-    total_tiles += tot;
+    T += tot;
   }
+  const long G = num_splits == 0 ? (T < max_wg ? T : max_wg) : 0;
 
-  long G = 0;
-  if (num_splits == 0) {
-    G = max_wg;
-    if (G > total_tiles) G = total_tiles;
-  }
-
-  // ---- pass 2: segments per sequence, prefix sums, and the segment list
+  // ---- per chunk: segments per sequence, their prefix sums, then the list
   long tile_base = 0;
   int seg_base = 0;
   for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
-    int b = c0 + t;
-    int len = 0, tiles = 0;
-    if (b < B) {
-      len = kv_lens[b];
-      if (len_valid(len, max_kv_len, capi)) tiles = (len + tile - 1) / tile;
-      else len = 0;
+    const int b = c0 + t;
+    int len = len0, tiles = tiles0, off = off0, tot_tiles = (int)T;
+    if (!one_chunk) {
+      tiles = tiles_of(b, &len);
+      off = block_exclusive_scan(tiles, wsum, &tot_tiles);
     }
-    int tot_tiles;
-    int my_tile_off = block_exclusive_scan(tiles, tmp, &tot_tiles);
-    long s_b = tile_base + my_tile_off;
-    long e_b = s_b + tiles;
-    int nseg = 0;
-    long g_first = 0;
-    int per = 1;
+    const long s_b = tile_base + off;
+    int nseg = 0, per = 1;
+    long g0 = 0;
     if (tiles > 0) {
       if (num_splits == 0) {
-        // WG boundaries w_g = floor(g*T/G); interior ones cut the sequence.
-        g_first = count_le(s_b, total_tiles, G);  // first g with w_g > s_b
-        long g = g_first;
-        nseg = 1;
-        while (g < G && (g * total_tiles) / G < e_b) {
-          ++nseg;
-          ++g;
-        }
+        g0 = wg_of_tile(s_b, T, G);
+        nseg = (int)(wg_of_tile(s_b + tiles - 1, T, G) - g0) + 1;
       } else {
         per = (tiles + num_splits - 1) / num_splits;
         nseg = (tiles + per - 1) / per;
       }
     }
     int tot_segs;
-    int my_seg_off = block_exclusive_scan(nseg, tmp, &tot_segs);
-    int k0 = seg_base + my_seg_off;
+    const int k0 = seg_base + block_exclusive_scan(nseg, wsum, &tot_segs);
     if (b < B) {
       p.seq_seg_start[b] = k0;
       p.seq_seg_count[b] = nseg;
     }
-    if (nseg > 0) {
-      if (num_splits == 0) {
-        long cur = s_b;
-        long g = g_first;
-        long owner = g_first - 1;  // WG owning tile s_b
-        for (int k = 0; k < nseg; ++k) {
-          long nxt = e_b;
-          if (k + 1 < nseg) nxt = (g * total_tiles) / G;
-          Seg sg;
-          sg.b = b;
-          sg.t0 = (int)((cur - s_b) * tile);
-          long t1 = (nxt - s_b) * tile;
-          sg.t1 = (int)(t1 < len ? t1 : len);
-          sg.pad = (int)owner;
-          p.segs[k0 + k] = sg;
-          // a segment that starts exactly on a WG boundary opens that WG's list
-          if ((owner * total_tiles) / G == cur) p.wg_seg_start[owner] = k0 + k;
-          cur = nxt;
-          owner = g;
-          ++g;
-        }
-      } else {
-        for (int k = 0; k < nseg; ++k) {
-          Seg sg;
-          sg.b = b;
-          sg.t0 = k * per * tile;
-          int t1 = (k + 1) * per * tile;
-          sg.t1 = t1 < len ? t1 : len;
-          sg.pad = k0 + k;
-          p.segs[k0 + k] = sg;
-          p.wg_seg_start[k0 + k] = k0 + k;
-        }
+    s_kseq[t] = k0;
+    s_sb[t] = s_b;
+    s_len[t] = len;
+    s_tiles[t] = per;   // forced mode: tiles per segment
+    s_g0[t] = g0;
+    if (t == 0) s_kseq[kPlanThreads] = seg_base + tot_segs;
+    __syncthreads();
+    // emit the chunk's segments, spread over all threads
+    for (int k = seg_base + t; k < seg_base + tot_segs; k += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads;   // the sequence i with kseq[i] <= k < kseq[i+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_kseq[mid] <= k) lo = mid;
+        else hi = mid;
       }
+      while (lo + 1 < kPlanThreads && s_kseq[lo + 1] <= k) ++lo;   // skip empty sequences
+      const int i = lo, j = k - s_kseq[i];
+      const int slen = s_len[i];
+      Seg sg;
+      sg.b = c0 + i;
+      if (num_splits == 0) {
+        const long sb = s_sb[i], eb = sb + (slen + tile - 1) / tile;
+        const long g = s_g0[i] + j;
+        const long w0 = wg_first_tile(g, T, G), w1 = wg_first_tile(g + 1, T, G);
+        const long a = w0 > sb ? w0 : sb, e = w1 < eb ? w1 : eb;
+        sg.t0 = (int)((a - sb) * tile);
+        const long t1 = (e - sb) * tile;
+        sg.t1 = (int)(t1 < slen ? t1 : slen);
+        sg.pad = (int)g;
+        // the segment holding a work-group's first tile opens its list
+        if (a == w0) p.wg_seg_start[g] = k;
+      } else {
+        const int per_i = s_tiles[i];
+        sg.t0 = j * per_i * tile;
+        const int t1 = (j + 1) * per_i * tile;
+        sg.t1 = t1 < slen ? t1 : slen;
+        sg.pad = k;
+        p.wg_seg_start[k] = k;
+      }
+      p.segs[k] = sg;
     }
+    __syncthreads();   // the chunk's shared arrays are rewritten next
     tile_base += tot_tiles;
     seg_base += tot_segs;
   }
   if (t == 0) {
-    int n_wg = (num_splits == 0) ? (int)G : seg_base;
+    const int n_wg = num_splits == 0 ? (int)G : seg_base;
     p.wg_seg_start[n_wg] = seg_base;
     p.counts[0] = seg_base;
     p.counts[1] = n_wg;
   }
-  (void)s_tile_base;
-  (void)s_seg_base;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

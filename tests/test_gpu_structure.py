@@ -145,3 +145,36 @@ def test_score_jump_redo_path(v2):
             sc = qa.f64()[b][0] @ r64[offs[b]:offs[b] + lens[b]].T
             assert sc.max() - sc[:32].max() > 50  # the jump is real (> 64 in log2 units)
             assert oracle.max_rel_error(lat[b], ref) < TOL["bf16"]
+
+
+def test_many_sequences_mixed_lengths(v2):
+    """More sequences than the planner handles in one pass, with invalid
+    lengths mixed in: sampled rows match the oracle, invalid rows are NaN,
+    and the auto split agrees with one segment per sequence."""
+    s = inputs.V2
+    rng = np.random.default_rng(28)
+    B = 300
+    lens = rng.integers(1, 400, B).astype(np.int32)
+    lens[rng.choice(B, 40, replace=False)] = rng.integers(1, 8, 40)   # short ones
+    paged = inputs.make_paged(lens, 64, 28, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = inputs.make_cache_rows(int(lens.sum()), s, 28, "bf16")
+    cache = cache_from_rows(v2, rows, paged, offs)
+    qa = _rand_q(B, s, 28)
+    bad = lens.copy()
+    invalid = [7, 150, 257, 299]
+    bad[invalid] = 0
+    qd = device.tensor(qa)
+    lat0 = device.to_f64(v2.decode_attention(qd, cache, paged.page_table, bad, 400, 0))
+    lat1 = device.to_f64(v2.decode_attention(qd, cache, paged.page_table, bad, 400, 1))
+    for b in invalid:
+        assert np.all(np.isnan(lat0[b])) and np.all(np.isnan(lat1[b])), b
+    ok = np.setdiff1d(np.arange(B), invalid)
+    # both results round bf16 partials and outputs: they agree to the bf16 bar
+    assert oracle.max_rel_error(lat0[ok], lat1[ok]) < TOL["bf16"]
+    r64 = rows.f64()
+    for b in rng.choice(ok, 12, replace=False).tolist() + [0, 255, 256, 298]:
+        ref = oracle.latent_attention(qa.f64()[b], r64[offs[b]:offs[b] + lens[b]], s.d_c)
+        for lat in (lat0, lat1):
+            err = oracle.max_rel_error(lat[b], ref)
+            assert err < TOL["bf16"], (b, lens[b], err)
