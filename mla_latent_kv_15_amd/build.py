@@ -40,6 +40,15 @@ _SPILL_OPS = ("scratch_", "buffer_store", "buffer_load", "v_accvgpr_read", "v_ac
               "v_accvgpr_mov")
 
 
+def _is_spill(line: str) -> bool:
+    """A scratch access or accumulation-register copy.  MUBUF loads with the
+    lds modifier are the kernels' own direct-to-LDS loads, not spills."""
+    code = line.split(";")[0]
+    if code.split() and code.split()[-1] == "lds":
+        return False
+    return any(op in code for op in _SPILL_OPS)
+
+
 def _check_scratch(src: str, remarks: str):
     """Parse -Rpass-analysis=kernel-resource-usage remarks of the hot kernels."""
     kernel = HOT_KERNELS.get(os.path.basename(src))
@@ -70,8 +79,7 @@ def _check_hot_blocks(src: str, asm: str):
         is_label = (c.endswith(":") and c.startswith(".LBB")) or l.startswith("; %bb.")
         if is_label:
             if any("v_mfma" in x for x in block):
-                bad += [f"{label.split()[0]} {x.strip()}" for x in block
-                        if any(op in x for op in _SPILL_OPS)]
+                bad += [f"{label.split()[0]} {x.strip()}" for x in block if _is_spill(x)]
             block, label = [], l
         else:
             block.append(l)

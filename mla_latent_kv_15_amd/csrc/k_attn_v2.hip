@@ -44,6 +44,8 @@
 //    sequence by e^(m_s - M) / sum_s l_s e^(m_s - M) and writes o~ as bf16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -66,9 +68,13 @@ constexpr int kLatBytes = 1024;       // LDS row of the latent part
 constexpr int kRopeBytes = 128;       // LDS row of the RoPE part
 constexpr int kRopeOff = kSub * kLatBytes;                 // 32768
 constexpr int kSubBytes = kRopeOff + kSub * kRopeBytes;    // 36864
-constexpr int kPBufOff = kSlots * kSubBytes;               // 147456
 constexpr int kPBufBytes = 4 * 2 * 64 * 16;                // [wave][K-step][lane][16 B]
-constexpr int kLdsBytes = kPBufOff + 2 * kPBufBytes;       // 163840 = 160 KB
+// the two P buffers first (their offsets fit a ds_read immediate), then the
+// ring; every slot base is a multiple of 4096, so it never meets the XOR-ed
+// address bits 4..7
+constexpr int kPBufOff = 0;
+constexpr int kRingOff = 2 * kPBufBytes;                   // 16384
+constexpr int kLdsBytes = kRingOff + kSlots * kSubBytes;   // 163840 = 160 KB
 constexpr int kInstsPerWave = 9;      // ring loads per wave per sub-tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -98,6 +104,40 @@ __device__ inline void lds_barrier() {
 // c ^ swz_rope(r) of LDS RoPE row r; piece c of the latent part (64 pieces)
 // sits at position c ^ (r & 15).
 __device__ inline int swz_rope(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// x ^ c formed at the point of use.  Left to itself the compiler hoists every
+// swizzled LDS address of the loop body into its own register for the whole
+// loop, which the register budget of the attention kernel cannot afford.
+template <int C>
+__device__ inline int xor_here(int x) {
+  if constexpr (C == 0) {
+    return x;
+  } else {
+    int r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(C), "v"(x));
+    return r;
+  }
+}
+
+// f(integral_constant<int, I>) for I in [I0, N): unrolled with compile-time indices
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// score MFMAs with a VGPR accumulator (first K-step starts from zero; the
+// early clobber keeps its destination off the A/B operands)
+__device__ __forceinline__ void score_mfma_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_mfma(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
 
 template <typename T>
 __device__ inline T lds_load(int byte) {
@@ -144,15 +184,19 @@ __device__ inline void ring_load(const Refill& rf, int i, int wave, int lane) {
 
 __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ cache, int num_pages,
-    const int32_t* __restrict__ page_table, int max_pages, int page, PlanPtrs plan,
-    __bf16* __restrict__ part_o, float* __restrict__ part_ml) {
+    const int32_t* __restrict__ page_table, int max_pages, int page,
+    const int* __restrict__ counts, const int* __restrict__ wg_seg_start,
+    const Seg* __restrict__ segs, __bf16* __restrict__ part_o, float* __restrict__ part_ml) {
   // Work-groups are dispatched round-robin over the eight XCDs.  Give the
   // work-groups of one XCD consecutive plan slots: consecutive slots share
   // sequences, so a sequence's absorbed query is fetched into one L2.
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int g = xcd * (G >> 3) + min(xcd, G & 7) + (blockIdx.x >> 3);
-  if (g >= plan.counts[1]) return;
+  if (g >= counts[1]) return;
+  const int k_begin = wg_seg_start[g];
+  const int k_end = wg_seg_start[g + 1];
+  if (k_begin >= k_end) return;
   // wave-uniform: a scalar register, so the LDS destinations of the ring
   // loads (M0) are scalar arithmetic rather than per-lane values
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,8 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   const int m32 = lane & 31;
   const int head = wave * 32 + m32;
 
-  // Per-lane LDS byte offsets (slot base added per iteration; it is a
-  // multiple of 4096, so it never meets the XOR-ed bits 4..7).
+  // Per-lane LDS byte offsets within a ring slot.
   // scores, latent K-step ks: row m32, piece 2ks + h at position
   // (2ks + h) ^ (m32 & 15)  ->  (qa ^ ((ks & 7) << 5)) + 256 (ks >> 3)
   const int qa = m32 * kLatBytes + ((h ^ (m32 & 15)) << 4);
@@ -173,63 +216,204 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   // i.e. latent piece 16w + (m32 >> 1), half m32 & 1:
   // (pa ^ ((8a + c) << 4)) + (16 kap + 8a + c) * 1024
   const int pa = 4 * h * kLatBytes + 256 * wave + (((m32 >> 1) ^ (4 * h)) << 4) + 8 * (m32 & 1);
+  auto slot_off = [](int pos) { return kRingOff + (pos & (kSlots - 1)) * kSubBytes; };
 
-  const int k_begin = plan.wg_seg_start[g];
-  const int k_end = plan.wg_seg_start[g + 1];
-  for (int k = k_begin; k < k_end; ++k) {
-    const Seg sg = plan.segs[k];
-    const int b = sg.b;
-    const int nsub = (sg.t1 - sg.t0 + kSub - 1) / kSub;
-    bool bad = false;
+  // Page ids, 64 pages per window: lane i holds the id of page w0 + i of
+  // sequence b (-1 past the table row).  A vector register instead of scalar
+  // loads: an outstanding scalar load would force a full LDS wait
+  // (lgkmcnt(0)) at every use of an LDS read in the loop below.
+  auto load_window = [&](int b, int w0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int p = w0 + ln;
+    return p < max_pages ? page_table[(long)b * max_pages + p] : -1;
+  };
 
-    // Page ids of the segment, 64 pages per window: lane i holds the id of
-    // page wb + i (-1 past the table row).  A vector register instead of
-    // scalar loads: an outstanding scalar load would force a full LDS wait
-    // (lgkmcnt(0)) at every use of an LDS read in the loop below.
-    int wb = 0;
-    auto load_window = [&]() {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int p = wb + ln;
-      const int v = p < max_pages ? page_table[(long)b * max_pages + p] : -1;
-      // consume the load here: a page-id load left in flight into the loop
-      // would make the compiler wait for all vector memory operations
-      // (vmcnt(0)) before each later page lookup, draining the ring
-      asm volatile("" ::"v"(v));
-      return v;
-    };
-    int pid = 0;
-    // Refill position: the next sub-tile to load is jj, tokens [tt, tt + 32)
-    // at offset po of page pi (sub-tiles never straddle a page: page is a
-    // multiple of 64 and segments start on 64-token boundaries or at 0).
-    // A pass refills jj = 0, 1, 2, ... in order from the window set at its start.
-    int rj = 0, rt = 0, rpi = 0, rpo = 0;
-    auto refill = [&]() {
+  // ---- ring refill cursor.  The work-group's sub-tiles form one stream
+  // (segment after segment); ring position pos holds a stream sub-tile in
+  // slot pos mod 4.  Each computing iteration consumes one position and loads
+  // the one two ahead, so near a segment's end the cursor walks into the
+  // next segment and that segment's first sub-tiles arrive while this one is
+  // still computed.  Cursor: segment rk (sequence rb), next token rt, end rt1,
+  // rn sub-tiles left, at offset rpo of page rpi, page window wb / pid.
+  int rk = k_begin, rb = 0, rt = 0, rt1 = 0, rn = 0, rpi = 0, rpo = 0, wb = 0, pid = 0;
+  int k = k_begin;      // the segment being computed
+  int pid_next = 0;     // window of segment k + 1's first pages (loaded ahead)
+  unsigned badm = 0;    // bit s & 31: segment s met a page id out of range
+  // a segment descriptor, waited for here: a scalar load left in flight
+  // would turn every later LDS wait of the iteration into lgkmcnt(0)
+  auto seg_at = [&](int kk) {
+    Seg sg = segs[kk];
+    asm volatile("" :: "v"(sg.b), "v"(sg.t0), "v"(sg.t1));
+    return sg;
+  };
+  auto cursor_begin = [&](int kk, int w) {
+    const Seg sg = seg_at(kk);
+    rk = kk;
+    rb = sg.b;
+    rt = sg.t0;
+    rt1 = sg.t1;
+    rn = (sg.t1 - sg.t0 + kSub - 1) / kSub;
+    wb = sg.t0 / page;
+    rpi = wb;
+    rpo = sg.t0 - wb * page;
+    pid = w;
+  };
+  // the cursor's next sub-tile, for ring position pos (sub-tiles never
+  // straddle a page: page is a multiple of 64 and segments start on 64-token
+  // boundaries or at 0)
+  auto refill = [&](int pos) {
+    Refill rf;
+    rf.slot = slot_off(pos);
+    if (rn > 0) {
       if (rpi - wb >= 64) {  // next window (segments longer than 64 pages)
         wb += 64 * ((rpi - wb) >> 6);
-        pid = load_window();
+        pid = load_window(rb, wb);
+        // consume here: a page-id load left in flight into the loop would
+        // make the compiler wait for all vector memory operations (vmcnt(0))
+        // before each later page lookup, draining the ring
+        asm volatile("" ::"v"(pid));
       }
       const int pg = __builtin_amdgcn_readlane(pid, rpi - wb);
       const bool ok = pg >= 0 && pg < num_pages;
-      bad |= !ok;
+      badm |= (ok ? 0u : 1u) << (rk & 31);
       const long row0 = ok ? (long)pg * page + rpo : 0;
-      Refill rf;
       rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
                                                 kRsrcWord3);
-      rf.slot = (rj % kSlots) * kSubBytes;
-      rf.rmax = ok ? min(kSub, sg.t1 - rt) - 1 : 0;
-      ++rj;
+      rf.rmax = ok ? min(kSub, rt1 - rt) - 1 : 0;
+      --rn;
       rt += kSub;
       rpo += kSub;
       if (rpo == page) {
         rpo = 0;
         ++rpi;
       }
-      return rf;
-    };
+    } else {
+      rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, 0, kRsrcWord3);
+      rf.rmax = 0;
+    }
+    return rf;
+  };
+  // past the stream, or a position that must stay unloaded: a resource of zero
+  // bytes, so each of its loads is out of range and moves no data.  Issuing
+  // them keeps the count of ring loads per sub-tile fixed, which the vmcnt
+  // immediates below rely on.
+  // sub-tile i (0 or 1) of segment k + 1 (descriptor sn), from the window
+  // loaded ahead: a segment starts on a 64-token boundary, so both lie in
+  // its first page
+  auto refill_next = [&](int pos, const Seg& sn, int i) {
+    const int pg = __builtin_amdgcn_readfirstlane(pid_next);
+    const bool ok = pg >= 0 && pg < num_pages;
+    badm |= (ok ? 0u : 1u) << ((k + 1) & 31);
+    const long row0 = ok ? (long)pg * page + (sn.t0 % page) + kSub * i : 0;
+    Refill rf;
+    rf.slot = slot_off(pos);
+    rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
+                                              kRsrcWord3);
+    rf.rmax = ok ? min(kSub, sn.t1 - (sn.t0 + kSub * i)) - 1 : 0;
+    return rf;
+  };
+  auto no_refill = [&](int pos) {
+    Refill rf;
+    rf.slot = slot_off(pos);
+    rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, 0, kRsrcWord3);
+    rf.rmax = 0;
+    return rf;
+  };
+
+  bf16x8 qreg[kKSteps];    // absorbed query, B operand (lane = head, 8 dims per K-step half)
+  auto load_q = [&](int b) {
+    const int hd = wave * 32 + (lane & 31), hh = lane >> 5;   // head, lane half
+    const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qs[2 * ks];
+  };
+  // the query must have landed before the sub-tile loop: a query load left in
+  // flight would make the compiler wait inside the loop behind ring loads
+  auto consume_q = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qreg[ks]));
+  };
+  int base = 0;   // ring position of sub-tile 0 of the segment being computed
+  // a pass that loads its own first two positions (the work-group's first
+  // segment, or a redo): window, positions base and base + 1, then the query
+  auto start_pass = [&](int b) {
+    const Seg sg = seg_at(k);
+    int w = load_window(sg.b, sg.t0 / page);
+    asm volatile("" ::"v"(w));
+    cursor_begin(k, w);
+    badm &= ~(1u << (k & 31));
+    const Refill r0 = refill(base);
+#pragma unroll
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
+    const Refill r1 = refill(base + 1);
+#pragma unroll
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
+    load_q(b);
+    consume_q();
+  };
+
+  // the cursor of a segment whose sub-tiles 0 and 1 the previous one loaded
+  auto cursor_after_prefetch = [&]() {
+    cursor_begin(k, pid_next);
+    rn -= 2;
+    rt += 2 * kSub;
+    rpo += 2 * kSub;
+    if (rpo == page) {
+      rpo = 0;
+      ++rpi;
+    }
+  };
+  Seg cur = seg_at(k);
+  if (k + 1 < k_end) {
+    const Seg sn = seg_at(k + 1);
+    pid_next = load_window(sn.b, sn.t0 / page);
+    asm volatile("" ::"v"(pid_next));
+  }
+  start_pass(cur.b);
+
+  for (;;) {   // the work-group's segments
+    const bool has_next = k + 1 < k_end;
+    const Seg nxt = seg_at(has_next ? k + 1 : k);
+    const int nsub = (cur.t1 - cur.t0 + kSub - 1) / kSub;
+    // the last two iterations load the next segment's first two sub-tiles
+    // (when both segments have two or more)
+    const bool pf_next = has_next && nsub >= 2 && nxt.t1 - nxt.t0 > kSub;
 
     f32x16 acc[16];          // acc[4 mb + n]: dims block mb of this wave x head block n
-    bf16x8 qreg[kKSteps];    // absorbed query, B operand (lane = head, 8 dims per K-step half)
+    // ---- latent accumulation, K-step kap (16 tokens) of the tile at LDS
+    // offset pvb - pa: 8 x ds_read_b64 -> 16 v_perm_b32 -> A operands of the
+    // 4 dims blocks; P^T of head block n from the P buffer at prd
+    u32x2 raw[8];
+    bf16x8 A[4];
+    bf16x8 B[2];
+    auto pv_read_at = [&](int pvb, int kap) {
+      static_for<0, 8>([&](auto ec) {
+        constexpr int e = decltype(ec)::value, a = e >> 2, c = e & 3;
+        raw[e] = lds_load<u32x2>(xor_here<(8 * a + c) << 4>(pvb) + (16 * kap + 8 * a + c) * kLatBytes);
+      });
+    };
+    auto pv_build = [&]() {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        u32x4 t;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          t[f] = __builtin_amdgcn_perm(raw[2 * f + 1][mb >> 1], raw[2 * f][mb >> 1],
+                                       (mb & 1) ? 0x07060302u : 0x05040100u);
+        A[mb] = __builtin_bit_cast(bf16x8, t);
+      }
+    };
+    // P^T of head block n, K-step kap (written by wave n)
+    auto p_read_at = [&](int prd, int kap, int n) {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      return lds_load<bf16x8>(prd + (2 * n + kap) * 1024 + 16 * l);
+    };
+    auto pv_mfma = [&](int mb, int n) {
+      acc[4 * mb + n] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb], B[n & 1], acc[4 * mb + n], 0, 0, 0);
+    };
     float m_ref = -INFINITY; // exponent reference (log2 units), fixed within a pass
     float l_run = 0.f;
     // pass 0: reference = max of the first 32 tokens; every sub-tile's max is
@@ -237,83 +421,56 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     // pass 1 redoes the segment with it as the reference
     int mode = 0;
     for (;;) {
-      // opaque to the optimiser: one copy of the sub-tile loop serves both passes
-      asm volatile("" : "+v"(mode));
+      // opaque to the optimiser: one copy of the sub-tile loop serves both
+      // passes (a scalar: the pass decides uniform control flow)
+      asm volatile("" : "+s"(mode));
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[x] = f32x16{};
       l_run = 0.f;
       float m_seen = -INFINITY;
       bool over = false;
 
-      __syncthreads();  // every wave is done with the ring and the P buffers
+      // every wave is done with the previous pass's P buffers
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();
       {
         // P buffer 1 reads as the P of sub-tile -1 in iteration 0: zero it
         const u32x4 z = {};
-        int tl = threadIdx.x;
-        asm volatile("" : "+v"(tl));
+        int tl = wave * 64 + lane;   // (threadIdx.x is not kept live)
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * tl, z);
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * (tl + kThreads), z);
       }
-      {
-        int hd = head, hh = h;
-        asm volatile("" : "+v"(hd), "+v"(hh));
-        const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qs[2 * ks];
-      }
-      // page window of the segment's first 64 pages (a redo pass starts over)
-      wb = sg.t0 / page;
-      pid = load_window();
-      rj = 0;
-      rt = sg.t0;
-      rpi = wb;
-      rpo = sg.t0 - wb * page;
-      {
-        const Refill r0 = refill();
-#pragma unroll
-        for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
-        if (nsub > 1) {
-          const Refill r1 = refill();
-#pragma unroll
-          for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
-        }
-      }
-      // the query must have landed before the loop: a query load left in
-      // flight would make the compiler wait inside the loop behind ring loads
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qreg[ks]));
 
       // Software pipeline over sub-tiles: iteration j computes the scores of
       // sub-tile j interleaved with the latent accumulation of sub-tile j-1
       // (its P, written to LDS at the end of iteration j-1) and with the ring
-      // loads of sub-tile j+2; the softmax of j overlaps the last quarter of
-      // j-1's accumulation.  Iteration 0 accumulates P = 0 over sub-tile 0;
-      // iteration nsub only drains (its scores are fully masked).
+      // loads of position base + j + 2; the softmax of j overlaps the last
+      // quarter of j-1's accumulation.  Iteration 0 accumulates P = 0 over
+      // sub-tile 0; the drain after the loop accumulates the last sub-tile.
+      // Every pass starts with exactly two positions loaded ahead.
 #pragma clang loop unroll(disable)
-      for (int j = 0; j <= nsub; ++j) {
-        // scalar set-up of the ring loads of sub-tile j+2 (issued below),
-        // ahead of the waits
-        const bool more = j + 2 < nsub;
-        Refill rf{};
-        if (more) rf = refill();
-        static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
-        if (j + 1 < nsub)
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      for (int j = 0; j < nsub; ++j) {
+        // scalar set-up of the ring loads (issued below), ahead of the waits
+        Refill rf;
+        if (j + 2 < nsub)
+          rf = refill(base + j + 2);
+        else if (pf_next)
+          rf = refill_next(base + j + 2, nxt, j + 2 - nsub);
         else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // the ring slot of sub-tile nsub is free from iteration nsub - 1 on
-        // (its previous sub-tile, nsub - 4, was last read in iteration
-        // nsub - 3); it carries the work-group's redo flag
-        if (j == nsub - 1 && threadIdx.x == 0) lds_store<int>((nsub % kSlots) * kSubBytes, 0);
-        // this wave's P of sub-tile j-1 (and the flag) are in LDS before the barrier
+          rf = no_refill(base + j + 2);
+        static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
+        // positions base and base + 1 landed before the query did; from j = 1
+        // on, only the loads of position base + j + 1 may still fly
+        if (j > 0) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        // this wave's P of sub-tile j-1 is in LDS before the barrier
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_barrier();  // sub-tile j landed everywhere; sub-tile j-2's slot is free
+        lds_barrier();  // sub-tile j landed everywhere; position base+j-2's slot is free
 
-        const int nvalid = j < nsub ? min(kSub, sg.t1 - (sg.t0 + j * kSub)) : 0;
-        const int sq = (j % kSlots) * kSubBytes;                     // scores tile
-        const int sv = ((j == 0 ? 0 : j - 1) % kSlots) * kSubBytes;  // accumulation tile
-        const int prd = kPBufOff + ((j + 1) & 1) * kPBufBytes;       // P of sub-tile j-1
-        const int pwr = kPBufOff + (j & 1) * kPBufBytes;             // P of sub-tile j
+        const int nvalid = min(kSub, cur.t1 - (cur.t0 + j * kSub));
+        const int sq = slot_off(base + j);                       // scores tile
+        const int sv = j == 0 ? sq : slot_off(base + j - 1);     // accumulation tile
+        const int prd = kPBufOff + ((j + 1) & 1) * kPBufBytes;   // P of sub-tile j-1
+        const int pwr = kPBufOff + (j & 1) * kPBufBytes;         // P of sub-tile j
 
         // ---- scores for 32 tokens x 32 heads (inline asm with a VGPR
         // accumulator: with the builtin the compiler puts S in the
@@ -323,78 +480,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         f32x16 S;
         bf16x8 abuf[2];
         const int qab = sq + qa, qrb = sq + qra;
-        auto a_read = [&](int ks) {
-          return ks < 32 ? lds_load<bf16x8>((qab ^ ((ks & 7) << 5)) + 256 * (ks >> 3))
-                         : lds_load<bf16x8>(qrb ^ ((ks - 32) << 5));
+        auto a_read = [&](auto ksc) {
+          constexpr int ks = decltype(ksc)::value;
+          if constexpr (ks < 32)
+            return lds_load<bf16x8>(xor_here<(ks & 7) << 5>(qab) + 256 * (ks >> 3));
+          else
+            return lds_load<bf16x8>(xor_here<(ks - 32) << 5>(qrb));
         };
-        abuf[0] = a_read(0);
-        abuf[1] = a_read(1);
-        auto qk = [&](int ks) {
+        abuf[0] = a_read(ic<0>{});
+        abuf[1] = a_read(ic<1>{});
+        auto qk = [&](auto ksc) {
+          constexpr int ks = decltype(ksc)::value;
           // take this K-step's operand before its buffer slot is refilled
           const bf16x8 a = abuf[ks & 1];
-          if (ks + 2 < kKSteps) abuf[ks & 1] = a_read(ks + 2);
-          if (ks == 0)
-            // early clobber: the destination must not overlap the A/B operands
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(qreg[ks]));
+          if constexpr (ks + 2 < kKSteps) abuf[ks & 1] = a_read(ic<ks + 2>{});
+          if constexpr (ks == 0)
+            score_mfma_first(S, a, qreg[ks]);
           else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(qreg[ks]));
+            score_mfma(S, a, qreg[ks]);
         };
 
-        // ---- latent accumulation of sub-tile j-1, K-step kap (16 tokens):
-        // 8 x ds_read_b64 -> 16 v_perm_b32 -> A operands of the 4 dims blocks
+        // ---- latent accumulation of sub-tile j-1 (tile at sv, P at prd)
         const int pvb = sv + pa;
-        u32x2 raw[8];
-        bf16x8 A[4];
-        auto pv_read = [&](int kap) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int a = e >> 2, c = e & 3;
-            raw[e] = lds_load<u32x2>((pvb ^ ((8 * a + c) << 4)) + (16 * kap + 8 * a + c) * kLatBytes);
-          }
-        };
-        auto pv_build = [&]() {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            u32x4 t;
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-              t[f] = __builtin_amdgcn_perm(raw[2 * f + 1][mb >> 1], raw[2 * f][mb >> 1],
-                                           (mb & 1) ? 0x07060302u : 0x05040100u);
-            A[mb] = __builtin_bit_cast(bf16x8, t);
-          }
-        };
-        // P^T of head block n, K-step kap (written by wave n)
-        auto p_read = [&](int kap, int n) {
-          int l = lane;
-          asm volatile("" : "+v"(l));
-          return lds_load<bf16x8>(prd + (2 * n + kap) * 1024 + 16 * l);
-        };
-        bf16x8 B[2];
-        auto pv_mfma = [&](int mb, int n) {
-          acc[4 * mb + n] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb], B[n & 1], acc[4 * mb + n], 0, 0, 0);
-        };
+        auto pv_read = [&](int kap) { pv_read_at(pvb, kap); };
+        auto p_read = [&](int kap, int n) { return p_read_at(prd, kap, n); };
 
         pv_read(0);
         B[0] = p_read(0, 0);
         // 36 regions, one score MFMA each; sched_barrier pins the interleave
         // (left alone, the scheduler clusters the builtin MFMAs away from the
-        // inline-asm ones).  Regions 0..8 also issue the ring loads of
-        // sub-tile j+2; K-step 0 of the accumulation runs in regions 3..18,
-        // K-step 1 after the score chain, beside the softmax.
-#pragma unroll
-        for (int r = 0; r < kKSteps; ++r) {
-          qk(r);
-          if (r < kInstsPerWave && more) ring_load(rf, r, wave, lane);
-          if (r == 2 || r == 19) pv_build();
-          if (r == 14) pv_read(1);
-          if (r >= 3 && r < 19) {
-            const int idx = r - 3, n = idx >> 2, mb = idx & 3;
-            if (mb == 0) B[(n + 1) & 1] = n < 3 ? p_read(0, n + 1) : p_read(1, 0);
+        // inline-asm ones).  Regions 0..8 also issue the ring loads;
+        // K-step 0 of the accumulation runs in regions 3..18, K-step 1 after
+        // the score chain, beside the softmax.
+        static_for<0, kKSteps>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          qk(rc);
+          if constexpr (r < kInstsPerWave) ring_load(rf, r, wave, lane);
+          if constexpr (r == 2 || r == 19) pv_build();
+          if constexpr (r == 14) pv_read(1);
+          if constexpr (r >= 3 && r < 19) {
+            constexpr int idx = r - 3, n = idx >> 2, mb = idx & 3;
+            if constexpr (mb == 0) B[(n + 1) & 1] = n < 3 ? p_read(0, n + 1) : p_read(1, 0);
             pv_mfma(mb, n);
           }
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
 
         // ---- softmax numerators of sub-tile j (log2 domain), lane = head, 16
@@ -441,37 +571,90 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           l_run += (sm[0] + sm[1]) + (sm[2] + sm[3]);
         }
         // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
-        // half) for all four waves
+        // half) for all four waves.  The last sub-tile of a first pass
+        // carries the wave's redo vote in the sign bit of lane 0's first
+        // number: the numerators are never negative, and a redo discards
+        // everything they feed.
+        const bool vote = mode == 0 && j == nsub - 1 && over;
 #pragma unroll
         for (int kap = 0; kap < 2; ++kap) {
           bf16x8 p;
 #pragma unroll
           for (int e = 0; e < 8; ++e) p[e] = (__bf16)S[8 * kap + e];
+          if (kap == 0) {
+            u32x4 pb = __builtin_bit_cast(u32x4, p);
+            pb[0] |= (vote && lane == 0) ? 0x8000u : 0u;
+            p = __builtin_bit_cast(bf16x8, pb);
+          }
           lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024 + 16 * lane, p);
         }
       }
-      // a score more than kLazy above the reference anywhere in the work-group:
-      // redo the segment with the exact maximum seen in this pass (rare)
+      // ---- drain: the latent accumulation of the last sub-tile.  The query
+      // registers are free from here on: the next segment's query loads now,
+      // under the accumulation and the partial's write.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();  // P of the last sub-tile (with the votes) is visible
+      if (has_next) load_q(nxt.b);
+      {
+        const int pvb = slot_off(base + nsub - 1) + pa;
+        const int prd = kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
+        pv_read_at(pvb, 0);
+        B[0] = p_read_at(prd, 0, 0);
+        pv_build();
+        static_for<0, 16>([&](auto ic_) {
+          constexpr int idx = decltype(ic_)::value, n = idx >> 2, mb = idx & 3;
+          if constexpr (mb == 0)
+            B[(n + 1) & 1] = n < 3 ? p_read_at(prd, 0, n + 1) : p_read_at(prd, 1, 0);
+          if constexpr (idx == 4) pv_read_at(pvb, 1);
+          pv_mfma(mb, n);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        pv_build();
+        static_for<0, 16>([&](auto ic_) {
+          constexpr int idx = decltype(ic_)::value, n = idx >> 2, mb = idx & 3;
+          if constexpr (mb == 0 && n < 3) B[(n + 1) & 1] = p_read_at(prd, 1, n + 1);
+          pv_mfma(mb, n);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      // a score more than kLazy above the reference anywhere in the work-group
+      // (a vote in the P of the last sub-tile, visible since the drain's
+      // barrier): redo the segment with the exact maximum seen in
+      // this pass (rare).  The redo starts at the ring position after this
+      // pass, behind the loads in flight there (same slots, issued earlier by
+      // the same wave, so they land earlier).
       if (mode == 0) {
-        const int flag = (nsub % kSlots) * kSubBytes;
-        if (over) lds_store<int>(flag, 1);
-        __syncthreads();
-        const int redo = lds_load<int>(flag);
-        if (redo) {
+        const int pv = kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
+        uint32_t v = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v |= lds_load<uint32_t>(pv + 2 * w * 1024);
+        // the same word in every lane: a uniform decision
+        if (__builtin_amdgcn_readfirstlane(v) & 0x8000u) {
           m_ref = m_seen;
           mode = 1;
+          base += nsub;
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          start_pass(cur.b);
           continue;
         }
       }
       break;
+    }
+    base += nsub;
+
+    // the window of the segment after the next, issued before the partial's
+    // stores so that waiting for it does not wait for the stores
+    int pid_n2 = 0;
+    if (k + 2 < k_end) {
+      const Seg s2 = seg_at(k + 2);
+      pid_n2 = load_window(s2.b, s2.t0 / page);
     }
 
     // ---- unnormalised partial (m, l, o~): o~ rounded to bf16, in register
     // order (8-byte piece 4x + a of a lane holds elements 4a .. 4a + 3 of
     // accumulator x); merged later
     {
-      int tl = threadIdx.x;
-      asm volatile("" : "+v"(tl));  // form the per-lane address here, not at kernel entry
+      const int tl = wave * 64 + lane;   // (threadIdx.x is not kept live)
       uint2* dst = (uint2*)(part_o + (long)k * kHeads * kDc) + tl;
 #pragma unroll
       for (int x = 0; x < 16; ++x)
@@ -483,8 +666,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           const bf16x2 p0 = {(__bf16)f0, (__bf16)f1}, p1 = {(__bf16)f2, (__bf16)f3};
           dst[(x * 4 + a) * kThreads] =
               uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+          // one accumulator at a time: the next query is arriving in the
+          // VGPRs, and reading all accumulators ahead would not fit beside it
+          if (a == 3) __builtin_amdgcn_sched_barrier(0);
         }
       const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const bool bad = (badm >> (k & 31)) & 1u;
+      badm &= ~(1u << (k & 31));
       if (h == 0) {
         int hd = head;
         asm volatile("" : "+v"(hd));
@@ -492,6 +680,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         *ml = float2{m_ref * kLn2, bad ? __builtin_nanf("") : l_tot};
       }
     }
+    if (!has_next) break;
+    ++k;
+    cur = nxt;
+    if (!pf_next) {
+      // a short segment on either side: the next one loads its own start
+      consume_q();
+      asm volatile("" ::"v"(pid_n2));
+      pid_next = pid_n2;
+      start_pass(cur.b);
+      continue;
+    }
+    consume_q();
+    asm volatile("" ::"v"(pid_n2));
+    cursor_after_prefetch();   // from pid_next: the window of segment k
+    pid_next = pid_n2;
   }
 }
 
@@ -584,7 +787,8 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, in
   if (n_wg_launch <= 0) return hipSuccess;
   hipLaunchKernelGGL(attn_v2_kernel, dim3(n_wg_launch), dim3(kThreads), 0, s,
                      (const __bf16*)q_abs, (const __bf16*)cache, num_pages, page_table, max_pages,
-                     g.page, plan, (__bf16*)part_o, part_ml);
+                     g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
+                     (const Seg*)plan.segs, (__bf16*)part_o, part_ml);
   return hipGetLastError();
 }
 

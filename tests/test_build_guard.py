@@ -27,8 +27,15 @@ def test_spills_outside_mfma_blocks_pass():
     build._check_hot_blocks("k_attn_v2.hip", _asm(CLEAN))
 
 
+def test_direct_to_lds_loads_are_not_spills():
+    body = list(CLEAN)
+    body.insert(3, "\tbuffer_load_dwordx4 v184, s[20:23], s61 offen lds")
+    build._check_hot_blocks("k_attn_v2.hip", _asm(body))
+
+
 @pytest.mark.parametrize("spill", [
     "\tscratch_load_dword v6, off, off offset:12 ; 4-byte Folded Reload",
+    "\tbuffer_store_dword v6, off, s[0:3], 0 offset:12 ; 4-byte Folded Spill",
     "\tv_accvgpr_read_b32 v2, a240",
     "\tv_accvgpr_write_b32 a3, v7",
 ])
