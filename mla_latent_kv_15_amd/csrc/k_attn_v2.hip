@@ -364,13 +364,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       ++rpi;
     }
   };
-  Seg cur = seg_at(k);
-  if (k + 1 < k_end) {
-    const Seg sn = seg_at(k + 1);
+  // work-group start: both descriptors, both page windows and the query in
+  // flight together, then the first two sub-tiles (landing behind the query:
+  // the first iteration waits for them itself)
+  Seg cur = segs[k];
+  {
+    const Seg sn = segs[k + 1 < k_end ? k + 1 : k];
+    asm volatile("" ::"v"(cur.b), "v"(cur.t0), "v"(cur.t1), "v"(sn.b), "v"(sn.t0));
+    const int w = load_window(cur.b, cur.t0 / page);
     pid_next = load_window(sn.b, sn.t0 / page);
-    asm volatile("" ::"v"(pid_next));
+    load_q(cur.b);
+    asm volatile("" ::"v"(w), "v"(pid_next));
+    cursor_begin(k, w);
+    const Refill r0 = refill(base);
+#pragma unroll
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
+    const Refill r1 = refill(base + 1);
+#pragma unroll
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
+    consume_q();
   }
-  start_pass(cur.b);
+  bool first_wait = true;   // iteration 0 of the first pass waits for its sub-tile
 
   for (;;) {   // the work-group's segments
     const bool has_next = k + 1 < k_end;
@@ -459,9 +473,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         else
           rf = no_refill(base + j + 2);
         static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
-        // positions base and base + 1 landed before the query did; from j = 1
-        // on, only the loads of position base + j + 1 may still fly
-        if (j > 0) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        // positions base and base + 1 landed before the query did (except at
+        // the work-group start); from j = 1 on, only the loads of position
+        // base + j + 1 may still fly
+        if (j > 0 || first_wait) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        first_wait = false;
         // this wave's P of sub-tile j-1 is in LDS before the barrier
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();  // sub-tile j landed everywhere; position base+j-2's slot is free
@@ -552,23 +568,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // until then); the redo pass starts with the exact maximum
         m_ref = (m_ref == -INFINITY) ? bm : m_ref;
         over |= bm > m_ref + kLazy;
+        // the numerators beside the first eight accumulation MFMAs, their
+        // LDS write beside the last eight (which hides its latency before
+        // the next barrier)
 #pragma unroll
-        for (int idx = 0; idx < 16; ++idx) {
+        for (int idx = 0; idx < 8; ++idx) {
           const int n = idx >> 2, mb = idx & 3;
-          if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
+          if (mb == 0) B[(n + 1) & 1] = p_read(1, n + 1);
           pv_mfma(mb, n);
-          if (idx < 8) {
-            S[2 * idx] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx], kLog2e, -m_ref));
-            S[2 * idx + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx + 1], kLog2e, -m_ref));
-          }
-        }
-        {
-          float sm[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sm[i] = S[i] + S[i + 8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm[i] += sm[i + 4];
-          l_run += (sm[0] + sm[1]) + (sm[2] + sm[3]);
+          S[2 * idx] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx], kLog2e, -m_ref));
+          S[2 * idx + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx + 1], kLog2e, -m_ref));
         }
         // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
         // half) for all four waves.  The last sub-tile of a first pass
@@ -587,6 +596,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
             p = __builtin_bit_cast(bf16x8, pb);
           }
           lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024 + 16 * lane, p);
+        }
+#pragma unroll
+        for (int idx = 8; idx < 16; ++idx) {
+          const int n = idx >> 2, mb = idx & 3;
+          if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
+          pv_mfma(mb, n);
+        }
+        {
+          float sm[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sm[i] = S[i] + S[i + 8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm[i] += sm[i + 4];
+          l_run += (sm[0] + sm[1]) + (sm[2] + sm[3]);
         }
       }
       // ---- drain: the latent accumulation of the last sub-tile.  The query
