@@ -6,10 +6,13 @@
 // log-sum-exp afterwards.
 //
 // Auto mode (num_splits == 0): the tiles (tile = 64 tokens) of all valid
-// sequences are laid end to end and cut into G equal ranges, one per
-// work-group, so every work-group streams the same number of cache bytes
-// whatever the length mix.  A range that crosses a sequence boundary becomes
-// several segments.  Forced mode (num_splits = S): every sequence is cut into
+// sequences are laid end to end, each sequence preceded by kSegCost virtual
+// tiles that stand for the fixed cost of starting a segment (its query, its
+// partial write), and this line is cut into G equal ranges, one per
+// work-group: every work-group gets the same cache bytes plus segment
+// overheads, whatever the length mix.  A range that crosses a sequence
+// boundary becomes several segments; a cut that falls on a sequence's
+// virtual tiles moves to the sequence's first tile.  Forced mode (num_splits = S): every sequence is cut into
 // at most S ranges and each segment gets its own work-group.
 #include "mla_internal.h"
 
@@ -18,6 +21,8 @@ namespace mla {
 namespace {
 
 constexpr int kPlanThreads = 256;   // one chunk of sequences per pass (4 waves)
+constexpr int kSegCost = 1;         // virtual tiles per segment start
+constexpr int kMaxAutoWg = 1024;    // work-groups an auto plan may use
 
 // Exclusive prefix sum over the work-group (wave scans + 4 wave totals).
 __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
@@ -58,6 +63,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ long s_sb[kPlanThreads];        // first tile (global) of each sequence
   __shared__ int s_len[kPlanThreads], s_tiles[kPlanThreads];
   __shared__ long s_g0[kPlanThreads];        // work-group owning each sequence's first tile
+  __shared__ int s_wgs[kMaxAutoWg + 1];       // first segment of each work-group (auto mode)
   const int t = threadIdx.x;
   const long cap = (long)max_pages * page;
   const int capi = cap > 0x7fffffffL ? 0x7fffffff : (int)cap;
@@ -68,40 +74,53 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     return (l + tile - 1) / tile;
   };
 
-  // ---- total tiles over the valid sequences (one chunk: kept for pass 2)
+  // a valid sequence's length on the virtual line
+  auto vtiles = [](int tiles) { return tiles > 0 ? tiles + kSegCost : 0; };
+
+  // ---- total tiles and virtual tiles over the valid sequences (one chunk:
+  // kept for pass 2)
   const bool one_chunk = B <= kPlanThreads;
   int len0 = 0, tiles0 = 0, off0 = 0;
-  long T = 0;
+  long T = 0, V = 0;
   for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
-    int len, tot;
+    int len, tot, vtot;
     const int tl = tiles_of(c0 + t, &len);
-    const int off = block_exclusive_scan(tl, wsum, &tot);
+    block_exclusive_scan(tl, wsum, &tot);
+    const int off = block_exclusive_scan(vtiles(tl), wsum, &vtot);
     if (one_chunk) {
       len0 = len;
       tiles0 = tl;
       off0 = off;
     }
     T += tot;
+    V += vtot;
   }
-  const long G = num_splits == 0 ? (T < max_wg ? T : max_wg) : 0;
+  long G = 0;
+  if (num_splits == 0) {
+    G = T < max_wg ? T : max_wg;
+    if (G > kMaxAutoWg) G = kMaxAutoWg;
+    for (int g = t; g <= G; g += kPlanThreads) s_wgs[g] = -1;
+    __syncthreads();
+  }
 
   // ---- per chunk: segments per sequence, their prefix sums, then the list
   long tile_base = 0;
   int seg_base = 0;
   for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
     const int b = c0 + t;
-    int len = len0, tiles = tiles0, off = off0, tot_tiles = (int)T;
+    int len = len0, tiles = tiles0, off = off0, tot_vt = (int)V;
     if (!one_chunk) {
       tiles = tiles_of(b, &len);
-      off = block_exclusive_scan(tiles, wsum, &tot_tiles);
+      off = block_exclusive_scan(vtiles(tiles), wsum, &tot_vt);
     }
+    // the sequence's virtual tiles start at s_b, its real tiles at s_b + kSegCost
     const long s_b = tile_base + off;
     int nseg = 0, per = 1;
     long g0 = 0;
     if (tiles > 0) {
       if (num_splits == 0) {
-        g0 = wg_of_tile(s_b, T, G);
-        nseg = (int)(wg_of_tile(s_b + tiles - 1, T, G) - g0) + 1;
+        g0 = wg_of_tile(s_b + kSegCost, V, G);
+        nseg = (int)(wg_of_tile(s_b + kSegCost + tiles - 1, V, G) - g0) + 1;
       } else {
         per = (tiles + num_splits - 1) / num_splits;
         nseg = (tiles + per - 1) / per;
@@ -134,16 +153,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       Seg sg;
       sg.b = c0 + i;
       if (num_splits == 0) {
-        const long sb = s_sb[i], eb = sb + (slen + tile - 1) / tile;
+        const long vb = s_sb[i], sb = vb + kSegCost, eb = sb + (slen + tile - 1) / tile;
         const long g = s_g0[i] + j;
-        const long w0 = wg_first_tile(g, T, G), w1 = wg_first_tile(g + 1, T, G);
+        const long w0 = wg_first_tile(g, V, G), w1 = wg_first_tile(g + 1, V, G);
         const long a = w0 > sb ? w0 : sb, e = w1 < eb ? w1 : eb;
         sg.t0 = (int)((a - sb) * tile);
         const long t1 = (e - sb) * tile;
         sg.t1 = (int)(t1 < slen ? t1 : slen);
         sg.pad = (int)g;
-        // the segment holding a work-group's first tile opens its list
-        if (a == w0) p.wg_seg_start[g] = k;
+        // a work-group's first segment: every later segment of a sequence,
+        // and its first one when the work-group's range starts within the
+        // sequence's virtual tiles
+        if (j > 0 || w0 >= vb) s_wgs[g] = k;
       } else {
         const int per_i = s_tiles[i];
         sg.t0 = j * per_i * tile;
@@ -155,12 +176,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       p.segs[k] = sg;
     }
     __syncthreads();   // the chunk's shared arrays are rewritten next
-    tile_base += tot_tiles;
+    tile_base += tot_vt;
     seg_base += tot_segs;
+  }
+  if (num_splits == 0) {
+    // a work-group whose range holds only virtual tiles has no segment: its
+    // list is empty (it starts where the next one does)
+    if (t == 0) s_wgs[G] = seg_base;
+    __syncthreads();
+    for (int g = t; g <= G; g += kPlanThreads) {
+      int gg = g;
+      while (s_wgs[gg] < 0) ++gg;
+      p.wg_seg_start[g] = s_wgs[gg];
+    }
   }
   if (t == 0) {
     const int n_wg = num_splits == 0 ? (int)G : seg_base;
-    p.wg_seg_start[n_wg] = seg_base;
+    if (num_splits != 0) p.wg_seg_start[n_wg] = seg_base;
     p.counts[0] = seg_base;
     p.counts[1] = n_wg;
   }
