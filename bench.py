@@ -99,6 +99,31 @@ def cpu_baseline(s, st, budget_s, cid):
                       f"({toks} cached rows) in {dt:.1f} s; each sequence yields one token"}
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "attn_v2_traffic_batch64.txt")
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current attention and planner sources and on this
+    workload; otherwise None."""
+    if workload != "batch64" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    from mla_latent_kv_15_amd import profsum
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("sources_sha256") != profsum.sources_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,7 +229,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "kernel": "attn_v2_kernel (paged latent-cache attention)",
             "launch_ms": attn_avg,
             "bytes_per_launch": cache_bytes,
