@@ -192,54 +192,64 @@ __global__ void splitk_reduce_kernel(int M, int N, int S, const float* __restric
   out[blocked ? blk_index(m, n, N) : (long)m * ldo + n] = (__bf16)v;
 }
 
-// q~_i = scale * W_UK,i^T q^C_i for one head i (grid.x) and 64 batch rows
-// (grid.y).  W_UK,i is [128 d][512 c]; the contraction runs over its row index,
-// so each lane reads eight consecutive rows (d) of one 16-byte column chunk and
-// transposes them in registers into eight B operands: N block j covers
-// c = 128 * wave + 8 * r16 + j.
-__global__ __launch_bounds__(256, 1) void absorb_kernel(int M, const __bf16* __restrict__ qc,
-                                                        const __bf16* __restrict__ W_UK,
-                                                        __bf16* __restrict__ q_abs, float scale) {
-  const int head = blockIdx.x;
+// The absorbed query of one head i and 64 batch rows: q~_i = scale * W_UK,i^T
+// q^C_i (latent half ch of the 512 columns per work-group: grid.x = 2 i + ch,
+// grid.y = row block), and the RoPE part, scale * RoPE(q^R_i) at the query's
+// position, packed after q~_i (rows split between the two work-groups).
+// W_UK,i is [128 d][512 c]; the contraction runs over its row index, so each
+// lane reads eight consecutive rows (d) of one 8-byte column chunk and
+// transposes them in registers into four B operands: N block j covers
+// c = 256 ch + 64 wave + 4 r16 + j.  All loads are issued before the first
+// MFMA (one memory round trip).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__global__ __launch_bounds__(256, 1) void absorb_kernel(
+    int M, const __bf16* __restrict__ qc, const __bf16* __restrict__ W_UK,
+    __bf16* __restrict__ q_abs, float scale, const float* __restrict__ q_r,
+    const int32_t* __restrict__ positions, const float* __restrict__ rope, int rope_len) {
+  const int head = blockIdx.x >> 1, ch = blockIdx.x & 1;
   const int m0 = blockIdx.y * kMT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int nmb = min(4, (M - m0 + 15) >> 4);
-  const __bf16* w = W_UK + (long)head * 128 * 512 + 128 * wave + 8 * r16;
-  f32x4 acc[4][8];
+  const int c0 = 256 * ch + 64 * wave + 4 * r16;
+  const __bf16* w = W_UK + (long)head * 128 * 512 + c0;
+  u32x2 v[4][8];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[mb][j] = f32x4{};
+    for (int r = 0; r < 8; ++r) v[ks][r] = *(const u32x2*)(w + (long)(32 * ks + 8 * g + r) * 512);
+  bf16x8 a[4][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = *(const u32x4*)(w + (long)(32 * ks + 8 * g + r) * 512);
-    bf16x8 a[4];
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = min(m0 + mb * 16 + r16, M - 1);
-      a[mb] = *(const bf16x8*)(qc + (long)m * 16384 + head * 128 + 32 * ks + 8 * g);
+      a[ks][mb] = *(const bf16x8*)(qc + (long)m * 16384 + head * 128 + 32 * ks + 8 * g);
     }
+  f32x4 acc[4][4];   // [mb][j]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[mb][j] = f32x4{};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
       u32x4 lo, hi;
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        lo[f] = __builtin_amdgcn_perm(v[2 * f + 1][e], v[2 * f][e], 0x05040100u);
-        hi[f] = __builtin_amdgcn_perm(v[2 * f + 1][e], v[2 * f][e], 0x07060302u);
+        lo[f] = __builtin_amdgcn_perm(v[ks][2 * f + 1][e], v[ks][2 * f][e], 0x05040100u);
+        hi[f] = __builtin_amdgcn_perm(v[ks][2 * f + 1][e], v[ks][2 * f][e], 0x07060302u);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (mb < nmb) {
-          acc[mb][2 * e] = mfma16(a[mb], __builtin_bit_cast(bf16x8, lo), acc[mb][2 * e]);
-          acc[mb][2 * e + 1] = mfma16(a[mb], __builtin_bit_cast(bf16x8, hi), acc[mb][2 * e + 1]);
+          acc[mb][2 * e] = mfma16(a[ks][mb], __builtin_bit_cast(bf16x8, lo), acc[mb][2 * e]);
+          acc[mb][2 * e + 1] = mfma16(a[ks][mb], __builtin_bit_cast(bf16x8, hi), acc[mb][2 * e + 1]);
         }
       }
     }
-  }
-  // D: lane holds column r16 (c = 128 wave + 8 r16 + j) and rows 4g + i
+  // D: lane holds column r16 of each N block (c = c0 + j) and rows 4g + i
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (mb >= nmb) continue;
@@ -247,11 +257,39 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(int M, const __bf16* __r
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + mb * 16 + 4 * g + i;
       if (m >= M) continue;
-      bf16x8 o;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = (__bf16)(scale * acc[mb][j][i]);
-      *(bf16x8*)(q_abs + ((long)m * 128 + head) * 576 + 128 * wave + 8 * r16) = o;
+      for (int j = 0; j < 4; ++j) o[j] = (__bf16)(scale * acc[mb][j][i]);
+      *(bf16x4*)(q_abs + ((long)m * 128 + head) * 576 + c0) = o;
     }
+  }
+  // RoPE part, rows 32 ch .. 32 ch + 31 of the block: row m, rotation pair k
+  // of q^R_i (NaN for a position outside the table); four per thread, all
+  // loads issued before the first store
+  constexpr int kPer = 32 * 32 / 256;
+  float2 x[kPer], cs[kPer];
+  int mm[kPer];
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = threadIdx.x + 256 * it;
+    const int m = min(m0 + 32 * ch + (e >> 5), M - 1), k = e & 31;
+    mm[it] = m0 + 32 * ch + (e >> 5);
+    x[it] = *(const float2*)(q_r + ((long)m * 128 + head) * 64 + 2 * k);
+    const int pos = positions[m];
+    const bool ok = pos >= 0 && pos < rope_len;
+    cs[it] = *(const float2*)(rope + ((long)(ok ? pos : 0) * 32 + k) * 2);
+    if (!ok) cs[it] = float2{__builtin_nanf(""), __builtin_nanf("")};
+  }
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = threadIdx.x + 256 * it, k = e & 31;
+    if (mm[it] >= M) continue;
+    const float o0 = (x[it].x * cs[it].x - x[it].y * cs[it].y) * scale;
+    const float o1 = (x[it].x * cs[it].y + x[it].y * cs[it].x) * scale;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    *(bf16x2*)(q_abs + ((long)mm[it] * 128 + head) * 576 + 512 + 2 * k) =
+        bf16x2{(__bf16)o0, (__bf16)o1};
   }
 }
 
@@ -348,10 +386,12 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
 }
 
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
+                     const float* q_r, const int32_t* positions, const float* rope, int rope_len,
                      hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(absorb_kernel, dim3(128, (M + kMT - 1) / kMT), dim3(256), 0, s, M,
-                     (const __bf16*)qc, (const __bf16*)W_UK, (__bf16*)q_abs, scale);
+  hipLaunchKernelGGL(absorb_kernel, dim3(2 * 128, (M + kMT - 1) / kMT), dim3(256), 0, s, M,
+                     (const __bf16*)qc, (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions,
+                     rope, rope_len);
   return hipGetLastError();
 }
 

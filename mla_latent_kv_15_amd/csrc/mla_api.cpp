@@ -212,9 +212,9 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
                   false, 1.f, s, true));
     MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
                   true, 1.f, s, true));
-    // absorbed query q~_i = W_UK,i^T q^C_i, scaled (order B)
-    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, s));
-    MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
+    // absorbed query q~_i = W_UK,i^T q^C_i and RoPE(q^R_i), scaled and packed
+    // (order B)
+    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, q.qr, positions, rope, rope_len, s));
     return MLA_OK;
   }
   const GType T = st(g);

@@ -128,6 +128,7 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16).
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
+                     const float* q_r, const int32_t* positions, const float* rope, int rope_len,
                      hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
 hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,

@@ -255,3 +255,36 @@ def test_v2_prefill_4096():
     err = oracle.max_rel_error(u[sel], ref)
     log(f"prefill vs oracle: {err:.3e}")
     assert err < TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# V2 absorbed query alone: two 64-row blocks with a ragged tail, positions
+# outside the RoPE table
+# ---------------------------------------------------------------------------
+
+def test_v2_decode_query_rows_and_positions():
+    s = inputs.V2
+    layer = Layer(s, 4, "bf16")
+    B = 70
+    table = 512
+    rng = np.random.default_rng(4)
+    pos = rng.integers(0, table, B).astype(np.int32)
+    bad = [3, 64, 69]
+    pos[bad] = [-1, table, table + 7]
+    H = inputs.make_hidden(B, s, 4, "bf16")
+    rope = layer.rope(table)
+    q = device.to_f64(layer.decode_query(device.tensor(H), pos, rope))
+    ok = np.setdiff1d(np.arange(B), bad)
+    scale = oracle.default_scale(s.d_h, s.d_r)
+    ref = []
+    for b in ok:
+        q_c, q_r = oracle.query(H.f64()[b], layer.W64["W_DQ"], layer.W64["W_UQ"], layer.W64["W_QR"],
+                                int(pos[b]), s.n_h, BASE)
+        ref.append(oracle.absorbed_query(q_c, q_r, layer.W64["W_UK"], scale))
+    ref = np.stack(ref)
+    # the latent part and the RoPE part of every head, each to the bf16 bar
+    assert oracle.max_rel_error(q[ok][..., :s.d_c], ref[..., :s.d_c]) < TOL["bf16"]
+    assert oracle.max_rel_error(q[ok][..., s.d_c:], ref[..., s.d_c:]) < TOL["bf16"]
+    # a position outside the table: NaN RoPE part, the latent part unaffected
+    assert np.all(np.isnan(q[bad][..., s.d_c:]))
+    assert np.all(np.isfinite(q[bad][..., :s.d_c]))
