@@ -29,15 +29,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 64;   // activation rows per work-group (4 MFMA blocks of 16)
 
-// "Blocked" activation layout [M / 64][K / 32][4][64][8]: the 16 x 32 A operand
-// of one MFMA (rows 16 mb .. 16 mb + 15 of a 64-row group, K-step t) is 1 KB
-// contiguous in lane order (lane 16 g + r holds row r, k = 32 t + 8 g .. + 7),
-// so a wave fetches it with one fully contiguous load instead of touching 16
-// rows.  Producers of GEMM inputs write it; rows past M are padding.
-__device__ inline long blk_index(int m, int k, int K) {
-  return ((((long)(m >> 6) * (K >> 5) + (k >> 5)) * 4 + ((m >> 4) & 3)) * 64 +
-          (((k >> 3) & 3) << 4) + (m & 15)) * 8 + (k & 7);
-}
+// Activations may come in the "blocked" layout (blk_index): a wave then
+// fetches each 16 x 32 A operand with one fully contiguous 1 KB load instead
+// of touching 16 rows.  Producers of GEMM inputs write it; rows past M are
+// padding.
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -50,14 +50,27 @@ __device__ inline bool len_valid(int len, int max_kv_len, int cap) {
   return len >= 1 && len <= max_kv_len && len <= cap;
 }
 
+// floor(a / b) for 0 <= a < 2^53, b > 0: a double estimate, corrected to the
+// exact quotient (64-bit integer division is a long software routine here)
+__device__ inline long div_floor(long a, long b) {
+  long q = (long)((double)a / (double)b);
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
 // Work-group g (of G) owns tiles [w(g), w(g+1)), w(g) = floor(g T / G).
-__device__ inline long wg_first_tile(long g, long T, long G) { return g * T / G; }
+__device__ inline long wg_first_tile(long g, long T, long G) { return div_floor(g * T, G); }
 // the work-group owning tile x: the largest g with w(g) <= x, ceil((x+1) G / T) - 1
-__device__ inline long wg_of_tile(long x, long T, long G) { return ((x + 1) * G + T - 1) / T - 1; }
+__device__ inline long wg_of_tile(long x, long T, long G) {
+  return div_floor((x + 1) * G + T - 1, T) - 1;
+}
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    PlanPtrs p, const int32_t* __restrict__ kv_lens, int B, int max_kv_len, int max_pages,
-    int page, int tile, int num_splits, int max_wg) {
+// The plan, built by one work-group of kPlanThreads threads.
+__device__ void plan_build(const PlanJob& job) {
+  const PlanPtrs& p = job.p;
+  const int32_t* __restrict__ kv_lens = job.kv_lens;
+  const int B = job.B, max_kv_len = job.max_kv_len, max_pages = job.max_pages;
+  const int page = job.page, tile = job.tile, num_splits = job.num_splits, max_wg = job.max_wg;
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ int s_kseq[kPlanThreads + 1];   // first segment of each sequence of the chunk
   __shared__ long s_sb[kPlanThreads];        // first tile (global) of each sequence
@@ -198,6 +211,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanJob job) { plan_build(job); }
+
+// splitk reduction (one output element per thread) and, in work-group 0,
+// the plan
+__global__ __launch_bounds__(kPlanThreads) void reduce_plan_kernel(int M, int N, int S,
+                                                                   const float* __restrict__ part,
+                                                                   long split_stride,
+                                                                   __bf16* __restrict__ out,
+                                                                   long ldo, int blocked,
+                                                                   PlanJob job) {
+  // the plan in the first work-group (dispatched first), the reduction in the rest
+  if (blockIdx.x == 0) {
+    plan_build(job);
+    return;
+  }
+  const long idx = (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  if (idx >= (long)M * N) return;
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[s * split_stride + (long)m * N + n];
+  out[blocked ? blk_index(m, n, N) : (long)m * ldo + n] = (__bf16)v;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -249,11 +285,35 @@ void carve_plan(void* base, int B, int num_splits, PlanPtrs* p) {
   p->counts = (int*)c;
 }
 
+PlanJob plan_job(const PlanPtrs& p, const int32_t* kv_lens, int B, int max_kv_len, int max_pages,
+                 int page, int tile, int num_splits) {
+  PlanJob j;
+  j.p = p;
+  j.kv_lens = kv_lens;
+  j.B = B;
+  j.max_kv_len = max_kv_len;
+  j.max_pages = max_pages;
+  j.page = page;
+  j.tile = tile;
+  j.num_splits = num_splits;
+  j.max_wg = plan_dims(B, num_splits).max_wg;
+  return j;
+}
+
 hipError_t launch_plan(const PlanPtrs& p, const int32_t* kv_lens, int B, int max_kv_len,
                        int max_pages, int page, int tile, int num_splits, hipStream_t s) {
-  PlanDims d = plan_dims(B, num_splits);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, kv_lens, B, max_kv_len,
-                     max_pages, page, tile, num_splits, d.max_wg);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s,
+                     plan_job(p, kv_lens, B, max_kv_len, max_pages, page, tile, num_splits));
+  return hipGetLastError();
+}
+
+hipError_t splitk_reduce_with_plan(int M, int N, int S, const float* part, long split_stride,
+                                   void* out, long ldo, bool blocked, const PlanJob& job,
+                                   hipStream_t s) {
+  const long n = (long)M * N;
+  hipLaunchKernelGGL(reduce_plan_kernel, dim3((unsigned)((n + kPlanThreads - 1) / kPlanThreads) + 1),
+                     dim3(kPlanThreads), 0, s, M, N, S, part, split_stride, (__bf16*)out, ldo,
+                     blocked ? 1 : 0, job);
   return hipGetLastError();
 }
 

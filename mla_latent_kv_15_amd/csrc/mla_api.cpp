@@ -175,7 +175,8 @@ size_t ws_decode(const Geo& g, int B, int ns) {
   size_t a = ws_attn(g, B, ns), o = ws_out(g, B);
   if (a > sub) sub = a;
   if (o > sub) sub = o;
-  return ws_decode_head(g, B) + sub;
+  // the plan has a region of its own: it is built during the query
+  return ws_decode_head(g, B) + al(plan_bytes(B, ns)) + sub;
 }
 size_t ws_append(const Geo& g, int T) { return al(sizeof(float) * (size_t)T * g.row); }
 size_t ws_prefill(const Geo& g, int T, int kv_len) {
@@ -194,8 +195,11 @@ int check_ws(void* ws, size_t have, size_t need) {
 // ---------------------------------------------------------------------------
 // step implementations (arguments already checked)
 // ---------------------------------------------------------------------------
+// job: a split plan to build during the query (in the launch of the W_DQ
+// reduction on the fast path, which leaves it idle compute units)
 int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* positions, int B,
-              const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s) {
+              const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s,
+              const PlanJob* job = nullptr) {
   Carver c(ws);
   QueryWs q;
   carve_query(c, g, B, &q);
@@ -205,8 +209,12 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16
     MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
                   (long)B * g.d_cq, true, 1.f, s));
-    MLA_TRY(splitk_reduce(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s,
-                          true));
+    if (job)
+      MLA_TRY(splitk_reduce_with_plan(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16,
+                                      g.d_cq, true, *job, s));
+    else
+      MLA_TRY(splitk_reduce(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s,
+                            true));
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
     MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
                   false, 1.f, s, true));
@@ -218,6 +226,11 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     return MLA_OK;
   }
   const GType T = st(g);
+  if (job) {
+    const PlanJob& j = *job;
+    MLA_TRY(launch_plan(j.p, j.kv_lens, j.B, j.max_kv_len, j.max_pages, j.page, j.tile,
+                        j.num_splits, s));
+  }
   // c^Q = W_DQ h  (eq. (12))
   MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, q.cq,
                        g.d_cq, 0, 1, 1.f, s));
@@ -259,16 +272,22 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// pre: a plan already built, ordered before s, by the caller
 int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                   const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
-                  int max_kv_len, int num_splits, void* ws, void* lat, hipStream_t s) {
+                  int max_kv_len, int num_splits, void* ws, void* lat, hipStream_t s,
+                  const PlanPtrs* pre = nullptr) {
   Carver c(ws);
   AttnWs a;
   carve_attn(c, g, B, num_splits, &a);
   PlanPtrs plan;
-  carve_plan(a.plan, B, num_splits, &plan);
   const bool fast = is_v2_fast(g);
-  MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
+  if (pre) {
+    plan = *pre;
+  } else {
+    carve_plan(a.plan, B, num_splits, &plan);
+    MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
+  }
   MLA_TRY(g_prof.mark(0, s));
   if (fast) {
     // the MFMA kernel writes every segment as a partial; its merge follows
@@ -485,11 +504,14 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
   Carver c(workspace);
   void* q_abs = c.take((size_t)B * g.n_h * g.row * g.esize());
   void* lat = c.take((size_t)B * g.n_h * g.d_c * g.esize());
+  PlanPtrs plan;
+  carve_plan(c.take(plan_bytes(B, num_splits)), B, num_splits, &plan);
+  const PlanJob job = plan_job(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits);
   void* sub = c.base + c.used;
-  r = run_query(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s);
+  r = run_query(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s, &job);
   if (r) return r;
   r = run_attention(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
-                    num_splits, sub, lat, s);
+                    num_splits, sub, lat, s, &plan);
   if (r) return r;
   return run_output(g, w, lat, B, sub, out, s);
 }

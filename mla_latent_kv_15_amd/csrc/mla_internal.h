@@ -57,6 +57,30 @@ void carve_plan(void* base, int B, int num_splits, PlanPtrs* p);
 hipError_t launch_plan(const PlanPtrs& p, const int32_t* kv_lens, int B, int max_kv_len,
                        int max_pages, int page, int tile, int num_splits, hipStream_t s);
 
+// Everything the planner reads: a plan request that a launch of another kernel
+// can carry (the plan then runs in one extra work-group of that launch).
+struct PlanJob {
+  PlanPtrs p;
+  const int32_t* kv_lens;
+  int B, max_kv_len, max_pages, page, tile, num_splits, max_wg;
+};
+PlanJob plan_job(const PlanPtrs& p, const int32_t* kv_lens, int B, int max_kv_len, int max_pages,
+                 int page, int tile, int num_splits);
+// out = sum_s part[s] as bf16 (splitk_reduce below) in one launch with the
+// plan of `job`, built by one extra work-group beside the reduction's.
+hipError_t splitk_reduce_with_plan(int M, int N, int S, const float* part, long split_stride,
+                                   void* out, long ldo, bool blocked, const PlanJob& job,
+                                   hipStream_t s);
+
+// "Blocked" activation layout [M / 64][K / 32][4][64][8] of the GEMM inputs:
+// the 16 x 32 A operand of one MFMA (rows 16 mb .. 16 mb + 15 of a 64-row
+// group, K-step t) is 1 KB contiguous in lane order (lane 16 g + r holds row
+// r, k = 32 t + 8 g .. + 7).
+__device__ inline long blk_index(int m, int k, int K) {
+  return ((((long)(m >> 6) * (K >> 5) + (k >> 5)) * 4 + ((m >> 4) & 3)) * 64 +
+          (((k >> 3) & 3) << 4) + (m & 15)) * 8 + (k & 7);
+}
+
 // ---------------------------------------------------------------------------
 // generic kernels (any geometry, fp32 or bf16 storage)
 // ---------------------------------------------------------------------------
