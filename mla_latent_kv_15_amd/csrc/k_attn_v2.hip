@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // Back-to-back accumulation into the same registers needs no wait
         // states; the s_nop before the softmax covers MFMA-result -> VALU.
         f32x16 S;
-        bf16x8 abuf[2];
+        bf16x8 abuf[4];
         const int qab = sq + qa, qrb = sq + qra;
         auto a_read = [&](auto ksc) {
           constexpr int ks = decltype(ksc)::value;
@@ -505,11 +505,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         };
         abuf[0] = a_read(ic<0>{});
         abuf[1] = a_read(ic<1>{});
+        abuf[2] = a_read(ic<2>{});
+        abuf[3] = a_read(ic<3>{});
         auto qk = [&](auto ksc) {
           constexpr int ks = decltype(ksc)::value;
-          // take this K-step's operand before its buffer slot is refilled
-          const bf16x8 a = abuf[ks & 1];
-          if constexpr (ks + 2 < kKSteps) abuf[ks & 1] = a_read(ic<ks + 2>{});
+          // take this K-step's operand before its buffer slot is refilled (four
+          // K-steps ahead: the LDS latency under four waves of reads)
+          const bf16x8 a = abuf[ks % 4];
+          if constexpr (ks + 4 < kKSteps) abuf[ks % 4] = a_read(ic<ks + 4>{});
           if constexpr (ks == 0)
             score_mfma_first(S, a, qreg[ks]);
           else
