@@ -41,6 +41,9 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Y = alpha * X . W^T over one K chunk.  Work-group (row group ng, chunk sp)
 // = blockIdx.x (ng fastest), activation block = blockIdx.y.  X row m of the
 // weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx.
+// Weight rows n >= n2 come from a second matrix W2 (its row n - n2) and go to
+// Y2 as fp32 (row stride ldy2): two projections of the same input in one
+// launch.  n2 >= N leaves W2 unused.
 // NS > 0: each wave runs exactly NS K-steps of 32, fully unrolled (the
 // decode shapes); NS == 0: a loop over the steps, DEPTH dividing their count.
 template <int RB, int NS, int DEPTH, bool OUT_F32>
@@ -50,7 +53,9 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
                                                        const __bf16* __restrict__ W,
                                                        void* __restrict__ Y, long ldy,
                                                        long y_split_stride, float alpha,
-                                                       int x_blocked, int y_blocked) {
+                                                       int x_blocked, int y_blocked,
+                                                       const __bf16* __restrict__ W2, int n2,
+                                                       float* __restrict__ Y2, long ldy2) {
   __shared__ f32x4 red[4][RB][4][64];  // [wave][rb][mb][lane]
   const int ng = blockIdx.x % n_groups, sp = blockIdx.x / n_groups;
   const int n0 = ng * 16 * RB;
@@ -78,7 +83,11 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
   }
   const bf16x8* wr[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) wr[rb] = (const bf16x8*)(W + (long)(n0 + rb * 16 + r16) * K + kbeg);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int n = n0 + rb * 16 + r16;   // a 16-row block lies wholly on one side of n2
+    wr[rb] = n0 + rb * 16 >= n2 ? (const bf16x8*)(W2 + (long)(n - n2) * K + kbeg)
+                                : (const bf16x8*)(W + (long)n * K + kbeg);
+  }
 
   f32x4 acc[RB][4];
 #pragma unroll
@@ -159,11 +168,14 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
     v += red[2][rb][mb][lane];
     v += red[3][rb][mb][lane];
     const int n = n0 + rb * 16 + r16;
+    const bool second = n0 + rb * 16 >= n2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + mb * 16 + 4 * g + i;
       if (m < M) {
-        if (OUT_F32)
+        if (second)
+          Y2[(long)m * ldy2 + (n - n2)] = alpha * v[i];
+        else if (OUT_F32)
           ((float*)Y)[sp * y_split_stride + (long)m * ldy + n] = alpha * v[i];
         else if (y_blocked)
           ((__bf16*)Y)[blk_index(m, n, n_groups * 16 * RB)] = (__bf16)(alpha * v[i]);
@@ -341,11 +353,13 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
     if (out_f32)                                                                              \
       hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, true>), grid, dim3(256), 0, s, M, K, kc,    \
                          n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
-                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb);            \
+                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,             \
+                         (const __bf16*)nullptr, N, (float*)nullptr, 0L);                     \
     else                                                                                      \
       hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, false>), grid, dim3(256), 0, s, M, K, kc,   \
                          n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
-                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb);            \
+                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,             \
+                         (const __bf16*)nullptr, N, (float*)nullptr, 0L);                     \
     return hipGetLastError();                                                                 \
   } while (0)
   // fully unrolled variants for the decode projections' tiles on 256 CUs
@@ -368,6 +382,22 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
   }
 #undef MLA_WGEMM_CASE
 #undef MLA_WGEMM_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W1, int N1,
+                      void* Y1, long ldy1, const void* W2, int N2, float* Y2, long ldy2,
+                      hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  constexpr int RB = 6, NS = 12;
+  const int N = N1 + N2;
+  if (N1 % 16 != 0 || N % (16 * RB) != 0 || K != 4 * 32 * NS || N / (16 * RB) > auto_wg_budget())
+    return hipErrorNotSupported;
+  const int n_groups = N / (16 * RB);
+  const dim3 grid(n_groups, (M + kMT - 1) / kMT);
+  hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false>), grid, dim3(256), 0, s, M, K, K, n_groups,
+                     (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1, 0L, 1.f,
+                     x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
   return hipGetLastError();
 }
 

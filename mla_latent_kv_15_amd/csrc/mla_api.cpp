@@ -216,10 +216,17 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
       MLA_TRY(splitk_reduce(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s,
                             true));
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
-    MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
-                  false, 1.f, s, true));
-    MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
-                  true, 1.f, s, true));
+    // (one launch for both where the shape fits its tiling)
+    const hipError_t pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq,
+                                     w->W_QR, (int)nr, q.qr, nr, s);
+    if (pe == hipErrorNotSupported) {
+      MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
+                    false, 1.f, s, true));
+      MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
+                    true, 1.f, s, true));
+    } else {
+      MLA_TRY(pe);
+    }
     // absorbed query q~_i = W_UK,i^T q^C_i and RoPE(q^R_i), scaled and packed
     // (order B)
     MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, q.qr, positions, rope, rope_len, s));

@@ -144,6 +144,13 @@ struct GemmTile {
   int splits;   // K chunks
 };
 GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split);
+// Y1 = X . W1^T (bf16, N1 rows) and Y2 = X . W2^T (fp32, N2 rows) in one
+// launch of 96-row work-groups without a K split; hipErrorNotSupported when
+// the shape does not fit that tiling (K = 1536, N1 + N2 a multiple of 96
+// within the compute units).
+hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W1, int N1,
+                      void* Y1, long ldy1, const void* W2, int N2, float* Y2, long ldy2,
+                      hipStream_t s);
 hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
                  long x_group_stride, int n_group, const void* W, void* Y, long ldy,
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s,
