@@ -6,9 +6,11 @@ attention with split-KV merge, W_UV and W_O) for a batch of 64 sequences of
 the DeepSeek-V2 layer (d=5120, n_h=128, d_h=128, d_c=512, d_c'=1536, d_R=64),
 context lengths uniform on [1024, 8192], 64-token pages in shuffled order,
 bf16 weights/cache with fp32 accumulation, query positions equal to each
-sequence's length (kv_len = L + 1).  Inputs are seeded synthetic data resident
-in HBM; two full buffer sets (weights + cache) alternate between steps so
-that the 256 MB last-level cache cannot serve a step from the previous one.
+sequence's length (kv_len = L + 1).  The weights are packed once, before
+timing, into the tiled layout the decode GEMMs stream (--weights rows keeps
+them row-major).  Inputs are seeded synthetic data resident in HBM; two
+full buffer sets (weights + cache) alternate between steps so that the 256 MB
+last-level cache cannot serve a step from the previous one.
 
 Prints one JSON line (see the keys below).  --gpus N with N > 1 exits: this
 build runs on one GPU.
@@ -43,7 +45,7 @@ WORKLOADS = {
 }
 
 
-def build_set(s, B, lo, hi, cid, sub, device, inputs, lib):
+def build_set(s, B, lo, hi, cid, sub, device, inputs, lib, cfg, tiles):
     import numpy as np
     import torch
     L = inputs.make_lengths(B, lo, hi, cid)
@@ -56,9 +58,17 @@ def build_set(s, B, lo, hi, cid, sub, device, inputs, lib):
     W = inputs.make_weights(s, cid + 100 * sub, "bf16")
     Wd = device.weights(W)
     del W
+    wbytes = sum(t.numel() * t.element_size() for t in Wd.values())
+    wts, packed = lib.make_weights(Wd), None
+    if tiles:
+        # one-time layout change at load; the row-major copies are dropped
+        packed = device.workspace(lib.packed_weights_size(cfg))
+        wts = lib.pack_weights(cfg, wts, packed)
+        torch.cuda.synchronize()
+        Wd = None
     Hq = inputs.make_hidden(B, s, cid, "bf16", sub=sub)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
-    return dict(L=L, kv=kv, paged=paged, cache=cache, Wd=Wd, wts=lib.make_weights(Wd),
+    return dict(L=L, kv=kv, paged=paged, cache=cache, Wd=Wd, wts=wts, packed=packed, wbytes=wbytes,
                 h=device.tensor(Hq), pos=i32(L), kv_d=i32(kv), pt=i32(paged.page_table),
                 Hq=Hq, offs=offs)
 
@@ -132,6 +142,8 @@ def main():
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--sets", type=int, default=2)
+    ap.add_argument("--weights", default="tiles", choices=("tiles", "rows"),
+                    help="weight layout (default: packed into tiles before timing)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -161,11 +173,12 @@ def main():
     lib.load()
     s = inputs.V2
     B, lo, hi, cid = WORKLOADS[args.workload]
+    cfg = lib.make_config(s, 64, "bf16")
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")
-    sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib) for k in range(args.sets)]
+    sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib, cfg, args.weights == "tiles")
+            for k in range(args.sets)]
     st0 = sets[0]
     max_kv = int(max(int(st["kv"].max()) for st in sets))
-    cfg = lib.make_config(s, 64, "bf16")
     rope = torch.empty(max_kv + 1, s.d_r // 2, 2, dtype=torch.float32, device="cuda")
     lib.rope_table_init(cfg, max_kv + 1, rope)
     ws = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE, B, max_kv, args.splits))
@@ -200,7 +213,7 @@ def main():
     cache_bytes = toks_avg * BYTES_PER_TOKEN
     achieved = cache_bytes / (attn_avg * 1e-3) / 1e9
     mfma_tflops = toks_avg * FLOP_PER_TOKEN / (attn_avg * 1e-3) / 1e12
-    weight_bytes = sum(t.numel() * t.element_size() for t in st0["Wd"].values())
+    weight_bytes = st0["wbytes"]
     step_bytes = cache_bytes + weight_bytes
 
     res = {
@@ -221,7 +234,7 @@ def main():
                         f"64-token shuffled pages, kv_len = L + 1",
             "batch": B, "context_lo": lo, "context_hi": hi, "page_size": 64,
             "d": s.d, "n_h": s.n_h, "d_h": s.d_h, "d_c": s.d_c, "d_cq": s.d_cq, "d_r": s.d_r,
-            "num_splits": args.splits, "buffer_sets": len(sets),
+            "num_splits": args.splits, "buffer_sets": len(sets), "weights": args.weights,
         },
         "roofline": {
             "bound": "hbm",

@@ -15,9 +15,12 @@
  *    hipStream_t; NULL is the null stream) and returns.  Scratch memory is the
  *    caller-provided `workspace` of at least mla_workspace_size() bytes,
  *    256-byte aligned.
- *  - Matrices are row-major.  Weights are [out][in] with y = W x.  Head i owns
- *    rows [i*d_h, (i+1)*d_h) of W_UQ, W_UK, W_UV, rows [i*d_r, (i+1)*d_r) of
- *    W_QR and columns [i*d_h, (i+1)*d_h) of W_O.
+ *  - Matrices are row-major unless stated.  Weights are [out][in] with
+ *    y = W x.  Head i owns rows [i*d_h, (i+1)*d_h) of W_UQ, W_UK, W_UV, rows
+ *    [i*d_r, (i+1)*d_r) of W_QR and columns [i*d_h, (i+1)*d_h) of W_O.
+ *    Weights may instead be stored tiled (mla_weights.layout,
+ *    mla_pack_weights): same values, an order the decode kernels stream in
+ *    contiguous 1 KB pieces.
  *  - Activations, weights and the cache share one storage dtype (cfg->dtype);
  *    all products accumulate in fp32.
  *  - The latent cache is [num_pages][page_size][d_c + d_r]: each token's row
@@ -78,12 +81,26 @@ typedef struct mla_config {
   double rope_base;   /* <= 0 selects 10000 */
 } mla_config;
 
+/* Storage order of the weight matrices.
+ * MLA_LAYOUT_ROWS:  row-major [out][in].
+ * MLA_LAYOUT_TILES: an [R][C] matrix is cut into 16 x 32 tiles, stored in
+ *   row-major tile order, 512 elements each; element (r, c) of tile
+ *   (r / 16, c / 32) sits at offset 8 * (16 * ((c / 8) % 4) + r % 16) + c % 8
+ *   inside its tile, so eight consecutive columns of a row stay adjacent.
+ *   Needs d, d_cq, d_c and n_h*d_h multiples of 32 and d_h, d_r multiples of
+ *   16 (MLA_ERR_UNSUPPORTED otherwise).  Every entry point accepts either
+ *   order and computes the same results; decode streams tiles faster. */
+typedef enum { MLA_LAYOUT_ROWS = 0, MLA_LAYOUT_TILES = 1 } mla_layout;
+
 /* Device pointers to the eight projection matrices, each [out][in]:
  * W_DKV [d_c][d], W_KR [d_r][d], W_DQ [d_cq][d], W_UQ [n_h*d_h][d_cq],
  * W_QR [n_h*d_r][d_cq], W_UK [n_h*d_h][d_c], W_UV [n_h*d_h][d_c],
- * W_O [d][n_h*d_h].  A call reads only the ones it uses. */
+ * W_O [d][n_h*d_h] ([walkthrough] steps 1-5; [formulas] eq. (9), (12),
+ * (13)), all stored in `layout` (an mla_layout).  A call reads only the ones
+ * it uses. */
 typedef struct mla_weights {
   const void *W_DKV, *W_KR, *W_DQ, *W_UQ, *W_QR, *W_UK, *W_UV, *W_O;
+  int layout;
 } mla_weights;
 
 /* Text for a status code (static storage). */
@@ -96,6 +113,25 @@ int mla_version(void);
  * positions 0..max_pos-1; angles pos * base^(-2k/d_r) are formed in fp64.
  * ([wiki] "与 RoPE 的兼容性": the decoupled RoPE part carries positions.) */
 int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void* stream);
+
+/* Bytes mla_pack_weights writes: the eight matrices back to back, each
+ * starting 256-byte aligned.  0 when the geometry is invalid or does not
+ * admit MLA_LAYOUT_TILES. */
+size_t mla_packed_weights_size(const mla_config* cfg);
+
+/* Copy the row-major weights of `src` (src->layout == MLA_LAYOUT_ROWS) into
+ * d_dst in MLA_LAYOUT_TILES, matrix by matrix in the order of mla_weights at
+ * the offsets mla_packed_weights_size counts; matrices that are null in src
+ * are skipped.  *out receives their device addresses (null where src has
+ * null) and layout = MLA_LAYOUT_TILES.  d_dst: device, 256-byte aligned,
+ * dst_bytes >= mla_packed_weights_size(cfg), not overlapping src; owned by
+ * the caller, who keeps it alive while *out is in use.  Enqueued on
+ * `stream`; src must stay unchanged until the copy has run.
+ * Errors: MLA_ERR_INVALID_ARG (null cfg, src or out; src not row-major),
+ * MLA_ERR_UNSUPPORTED (geometry without a tiled layout), MLA_ERR_WORKSPACE
+ * (d_dst null, misaligned or too small). */
+int mla_pack_weights(const mla_config* cfg, const mla_weights* src, void* d_dst,
+                     size_t dst_bytes, mla_weights* out, void* stream);
 
 /* Bytes of workspace `op` needs.  batch: B for decode ops, T for append and
  * prefill.  max_kv_len: longest kv_len the call may see (decode, prefill).

@@ -14,7 +14,9 @@
 // the work-groups fill the GPU exactly (wgemm_tile).  Its four waves split the
 // chunk four ways; each streams 16-byte pieces of W straight into the B
 // operand of v_mfma_f32_16x16x32_bf16 (lane = weight row, 8 consecutive k) and
-// reuses each activation piece (A operand) for all RB row blocks.  The four
+// reuses each activation piece (A operand) for all RB row blocks.  With W in
+// the tiled layout (tile_index) each such piece of 16 rows is one contiguous
+// 1 KB load, and a wave's share of a 16-row block is one contiguous run.  The four
 // partial tiles are summed in LDS in a fixed order.  Split-K chunks write fp32
 // partials that a small kernel reduces in a fixed order (deterministic).
 #include "mla_internal.h"
@@ -46,7 +48,8 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // launch.  n2 >= N leaves W2 unused.
 // NS > 0: each wave runs exactly NS K-steps of 32, fully unrolled (the
 // decode shapes); NS == 0: a loop over the steps, DEPTH dividing their count.
-template <int RB, int NS, int DEPTH, bool OUT_F32>
+// WT: W (and W2) in the tiled layout, K columns.
+template <int RB, int NS, int DEPTH, bool OUT_F32, bool WT>
 __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int n_groups,
                                                        const __bf16* __restrict__ X, long ldx,
                                                        long x_group_stride, int n_group,
@@ -84,10 +87,17 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
   const bf16x8* wr[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int n = n0 + rb * 16 + r16;   // a 16-row block lies wholly on one side of n2
-    wr[rb] = n0 + rb * 16 >= n2 ? (const bf16x8*)(W2 + (long)(n - n2) * K + kbeg)
-                                : (const bf16x8*)(W + (long)n * K + kbeg);
+    // a 16-row block lies wholly on one side of n2
+    const bool second = n0 + rb * 16 >= n2;
+    const __bf16* wm = second ? W2 : W;
+    const int nb = second ? n0 + rb * 16 - n2 : n0 + rb * 16;
+    if constexpr (WT)
+      wr[rb] = (const bf16x8*)(wm + ((long)(nb >> 4) * (K >> 5) + ((kbeg - 8 * g) >> 5)) * 512) +
+               lane;
+    else
+      wr[rb] = (const bf16x8*)(wm + (long)(nb + r16) * K + kbeg);
   }
+  constexpr int wstep = WT ? 64 : 4;   // bf16x8 units from one K-step of W to the next
 
   f32x4 acc[RB][4];
 #pragma unroll
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
   bf16x8 bq[DEPTH][RB], aq[DEPTH][4];
   auto load = [&](int d, int st) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) bq[d][rb] = wr[rb][4 * st];
+    for (int rb = 0; rb < RB; ++rb) bq[d][rb] = wr[rb][wstep * st];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) aq[d][mb] = xr[mb][xstep * st];
   };
@@ -207,8 +217,10 @@ __global__ void splitk_reduce_kernel(int M, int N, int S, const float* __restric
 // lane reads eight consecutive rows (d) of one 8-byte column chunk and
 // transposes them in registers into four B operands: N block j covers
 // c = 256 ch + 64 wave + 4 r16 + j.  All loads are issued before the first
-// MFMA (one memory round trip).
+// MFMA (one memory round trip).  WT: W_UK in the tiled layout, where the four
+// columns of a row stay contiguous.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <bool WT>
 __global__ __launch_bounds__(256, 1) void absorb_kernel(
     int M, const __bf16* __restrict__ qc, const __bf16* __restrict__ W_UK,
     __bf16* __restrict__ q_abs, float scale, const float* __restrict__ q_r,
@@ -219,12 +231,17 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
   const int r16 = lane & 15, g = lane >> 4;
   const int nmb = min(4, (M - m0 + 15) >> 4);
   const int c0 = 256 * ch + 64 * wave + 4 * r16;
-  const __bf16* w = W_UK + (long)head * 128 * 512 + c0;
+  // row d of W_UK,i, columns c0 .. c0 + 3
+  const __bf16* wh = W_UK + (long)head * 128 * 512;
+  auto wrow = [&](int d) -> const u32x2* {
+    if constexpr (WT) return (const u32x2*)(wh + tile_index(d, c0, 512));
+    return (const u32x2*)(wh + (long)d * 512 + c0);
+  };
   u32x2 v[4][8];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[ks][r] = *(const u32x2*)(w + (long)(32 * ks + 8 * g + r) * 512);
+    for (int r = 0; r < 8; ++r) v[ks][r] = *wrow(32 * ks + 8 * g + r);
   bf16x8 a[4][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -335,11 +352,11 @@ GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split) {
 hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
                  long x_group_stride, int n_group, const void* W, void* Y, long ldy,
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s, bool x_blocked,
-                 bool y_blocked) {
+                 bool y_blocked, bool w_tiled) {
   if (M <= 0) return hipSuccess;
   if (t.rb < 1 || t.rb > 5 || t.splits < 1 || N % (16 * t.rb) != 0 || K % (128 * t.splits) != 0 ||
       (t.splits > 1 && !out_f32) || (y_blocked && (out_f32 || N % 32 != 0)) ||
-      (x_blocked && n_group > 0 && n_group != N))
+      (x_blocked && n_group > 0 && n_group != N) || (w_tiled && K % 32 != 0))
     return hipErrorInvalidValue;
   const int n_groups = N / (16 * t.rb);
   const int kc = K / t.splits;
@@ -348,19 +365,22 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
   const int xb = x_blocked ? 1 : 0, yb = y_blocked ? 1 : 0;
   const dim3 grid(n_groups * t.splits, (M + kMT - 1) / kMT);
   if (n_group <= 0) n_group = N;
-#define MLA_WGEMM_LAUNCH(RB, NS, D)                                                           \
-  do {                                                                                        \
-    if (out_f32)                                                                              \
-      hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, true>), grid, dim3(256), 0, s, M, K, kc,    \
-                         n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
-                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,             \
-                         (const __bf16*)nullptr, N, (float*)nullptr, 0L);                     \
-    else                                                                                      \
-      hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, false>), grid, dim3(256), 0, s, M, K, kc,   \
-                         n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,            \
-                         (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,             \
-                         (const __bf16*)nullptr, N, (float*)nullptr, 0L);                     \
-    return hipGetLastError();                                                                 \
+#define MLA_WGEMM_GO(RB, NS, D, F32, WT)                                                       \
+  hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, F32, WT>), grid, dim3(256), 0, s, M, K, kc,      \
+                     n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,                 \
+                     (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,                  \
+                     (const __bf16*)nullptr, N, (float*)nullptr, 0L)
+#define MLA_WGEMM_LAUNCH(RB, NS, D)                 \
+  do {                                              \
+    if (out_f32 && w_tiled)                         \
+      MLA_WGEMM_GO(RB, NS, D, true, true);          \
+    else if (out_f32)                               \
+      MLA_WGEMM_GO(RB, NS, D, true, false);         \
+    else if (w_tiled)                               \
+      MLA_WGEMM_GO(RB, NS, D, false, true);         \
+    else                                            \
+      MLA_WGEMM_GO(RB, NS, D, false, false);        \
+    return hipGetLastError();                       \
   } while (0)
   // fully unrolled variants for the decode projections' tiles on 256 CUs
   // (W_O, W_UQ / W_UV, W_QR, W_DQ of the DeepSeek-V2 layer)
@@ -382,12 +402,13 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
   }
 #undef MLA_WGEMM_CASE
 #undef MLA_WGEMM_LAUNCH
+#undef MLA_WGEMM_GO
   return hipGetLastError();
 }
 
 hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W1, int N1,
                       void* Y1, long ldy1, const void* W2, int N2, float* Y2, long ldy2,
-                      hipStream_t s) {
+                      bool w_tiled, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   constexpr int RB = 6, NS = 12;
   const int N = N1 + N2;
@@ -395,9 +416,14 @@ hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W
     return hipErrorNotSupported;
   const int n_groups = N / (16 * RB);
   const dim3 grid(n_groups, (M + kMT - 1) / kMT);
-  hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false>), grid, dim3(256), 0, s, M, K, K, n_groups,
-                     (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1, 0L, 1.f,
-                     x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
+  if (w_tiled)
+    hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false, true>), grid, dim3(256), 0, s, M, K, K,
+                       n_groups, (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1,
+                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
+  else
+    hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false, false>), grid, dim3(256), 0, s, M, K, K,
+                       n_groups, (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1,
+                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
   return hipGetLastError();
 }
 
@@ -410,13 +436,19 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
   return hipGetLastError();
 }
 
-hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
-                     const float* q_r, const int32_t* positions, const float* rope, int rope_len,
-                     hipStream_t s) {
+hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
+                     float scale, const float* q_r, const int32_t* positions, const float* rope,
+                     int rope_len, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(absorb_kernel, dim3(2 * 128, (M + kMT - 1) / kMT), dim3(256), 0, s, M,
-                     (const __bf16*)qc, (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions,
-                     rope, rope_len);
+  const dim3 grid(2 * 128, (M + kMT - 1) / kMT);
+  if (w_tiled)
+    hipLaunchKernelGGL(absorb_kernel<true>, grid, dim3(256), 0, s, M, (const __bf16*)qc,
+                       (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions, rope,
+                       rope_len);
+  else
+    hipLaunchKernelGGL(absorb_kernel<false>, grid, dim3(256), 0, s, M, (const __bf16*)qc,
+                       (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions, rope,
+                       rope_len);
   return hipGetLastError();
 }
 

@@ -44,9 +44,17 @@ __device__ inline float block_sum256(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// tiled SIMT GEMM: C = alpha * A * B^T (B(n,k) row- or k-major)
+// tiled SIMT GEMM: C = alpha * A * B^T (B(n,k) as BLayout BL says)
 // ---------------------------------------------------------------------------
-template <typename TA, typename TB, typename TC, bool BK>
+template <int BL>
+__device__ inline long b_index(int n, int k, long ldb) {
+  if constexpr (BL == B_NK) return (long)n * ldb + k;
+  if constexpr (BL == B_KN) return (long)k * ldb + n;
+  if constexpr (BL == B_NK_TILES) return tile_index(n, k, ldb);
+  return tile_index(k, n, ldb);
+}
+
+template <typename TA, typename TB, typename TC, int BL>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
                                                            const TA* __restrict__ A, long lda,
                                                            long sA, const TB* __restrict__ B,
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
     }
     for (int e = threadIdx.x; e < 1024; e += 256) {
       int nn, kk;
-      if (BK) {
+      if (BL == B_KN || BL == B_KN_TILES) {
         kk = e >> 6;
         nn = e & 63;
       } else {
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
       }
       int gn = n0 + nn, gk = k0 + kk;
       float v = 0.f;
-      if (gn < N && gk < K) v = BK ? ld(B + (long)gk * ldb + gn) : ld(B + (long)gn * ldb + gk);
+      if (gn < N && gk < K) v = ld(B + b_index<BL>(gn, gk, ldb));
       Bs[kk][nn] = v;
     }
     __syncthreads();
@@ -114,17 +122,35 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
 }
 
 template <typename TA, typename TB, typename TC>
-hipError_t gemm_launch(bool bk, int M, int N, int K, const void* A, long lda, long sA,
+hipError_t gemm_launch(BLayout bl, int M, int N, int K, const void* A, long lda, long sA,
                        const void* B, long ldb, long sB, void* C, long ldc, long sC, int batch,
                        float alpha, hipStream_t s) {
   dim3 grid((N + 63) / 64, (M + 63) / 64, batch);
-  if (bk)
-    hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC, true>), grid, dim3(256), 0, s, M, N, K,
-                       (const TA*)A, lda, sA, (const TB*)B, ldb, sB, (TC*)C, ldc, sC, alpha);
-  else
-    hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC, false>), grid, dim3(256), 0, s, M, N, K,
-                       (const TA*)A, lda, sA, (const TB*)B, ldb, sB, (TC*)C, ldc, sC, alpha);
+#define MLA_GG(BL)                                                                              \
+  hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC, BL>), grid, dim3(256), 0, s, M, N, K,     \
+                     (const TA*)A, lda, sA, (const TB*)B, ldb, sB, (TC*)C, ldc, sC, alpha)
+  switch (bl) {
+    case B_NK: MLA_GG(B_NK); break;
+    case B_KN: MLA_GG(B_KN); break;
+    case B_NK_TILES: MLA_GG(B_NK_TILES); break;
+    case B_KN_TILES: MLA_GG(B_KN_TILES); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MLA_GG
   return hipGetLastError();
+}
+
+// row-major [R][C] -> tiled layout, one thread per 8-element piece of dst
+template <typename T>
+__global__ void pack_tiles_kernel(const T* __restrict__ src, long R, long C, T* __restrict__ dst) {
+  struct Piece { T v[8]; };
+  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= R * C / 8) return;
+  const long tile = p >> 6, tiles_per_row = C >> 5;
+  const int l = (int)(p & 63);
+  const long r = (tile / tiles_per_row) * 16 + (l & 15);
+  const long c = (tile % tiles_per_row) * 32 + 8 * (l >> 4);
+  ((Piece*)dst)[p] = *(const Piece*)(src + r * C + c);
 }
 
 // ---------------------------------------------------------------------------
@@ -446,9 +472,23 @@ __global__ __launch_bounds__(256) void attn_prefill_generic_kernel(
 
 }  // namespace
 
-hipError_t gemm_generic(GType ta, GType tb, GType tc, bool bk, int M, int N, int K, const void* A,
-                        long lda, long sA, const void* B, long ldb, long sB, void* C, long ldc,
-                        long sC, int batch, float alpha, hipStream_t s) {
+hipError_t pack_tiles(const void* src, long R, long C, int elem_bytes, void* dst, hipStream_t s) {
+  if (R % 16 != 0 || C % 32 != 0 || (elem_bytes != 2 && elem_bytes != 4)) return hipErrorInvalidValue;
+  const long pieces = R * C / 8;
+  if (pieces == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(pack_tiles_kernel<__bf16>, grid, dim3(256), 0, s, (const __bf16*)src, R, C,
+                       (__bf16*)dst);
+  else
+    hipLaunchKernelGGL(pack_tiles_kernel<float>, grid, dim3(256), 0, s, (const float*)src, R, C,
+                       (float*)dst);
+  return hipGetLastError();
+}
+
+hipError_t gemm_generic(GType ta, GType tb, GType tc, BLayout bk, int M, int N, int K,
+                        const void* A, long lda, long sA, const void* B, long ldb, long sB,
+                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
 #define MLA_G(TA_, TB_, TC_) \
   return gemm_launch<TA_, TB_, TC_>(bk, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, alpha, s)

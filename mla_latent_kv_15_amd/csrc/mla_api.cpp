@@ -203,12 +203,13 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
   Carver c(ws);
   QueryWs q;
   carve_query(c, g, B, &q);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
   if (is_v2_fast(g)) {
     const GemmTile tdq = tile_dq(g);
     const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
     // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16
     MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
-                  (long)B * g.d_cq, true, 1.f, s));
+                  (long)B * g.d_cq, true, 1.f, s, false, false, wt));
     if (job)
       MLA_TRY(splitk_reduce_with_plan(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16,
                                       g.d_cq, true, *job, s));
@@ -218,18 +219,19 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
     // (one launch for both where the shape fits its tiling)
     const hipError_t pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq,
-                                     w->W_QR, (int)nr, q.qr, nr, s);
+                                     w->W_QR, (int)nr, q.qr, nr, wt, s);
     if (pe == hipErrorNotSupported) {
       MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
-                    false, 1.f, s, true));
+                    false, 1.f, s, true, false, wt));
       MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
-                    true, 1.f, s, true));
+                    true, 1.f, s, true, false, wt));
     } else {
       MLA_TRY(pe);
     }
     // absorbed query q~_i = W_UK,i^T q^C_i and RoPE(q^R_i), scaled and packed
     // (order B)
-    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, q_abs, g.scale, q.qr, positions, rope, rope_len, s));
+    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, wt, q_abs, g.scale, q.qr, positions, rope, rope_len,
+                      s));
     return MLA_OK;
   }
   const GType T = st(g);
@@ -239,17 +241,17 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
                         j.num_splits, s));
   }
   // c^Q = W_DQ h  (eq. (12))
-  MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, q.cq,
-                       g.d_cq, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(T, T, G_F32, b_layout(wt, false), B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d,
+                       0, q.cq, g.d_cq, 0, 1, 1.f, s));
   // q^C = W_UQ c^Q (eq. (13)) and the per-head RoPE query input W_QR c^Q
-  MLA_TRY(gemm_generic(G_F32, T, G_F32, false, B, g.n_h * g.d_h, g.d_cq, q.cq, g.d_cq, 0, w->W_UQ,
-                       g.d_cq, 0, q.qc, (long)g.n_h * g.d_h, 0, 1, 1.f, s));
-  MLA_TRY(gemm_generic(G_F32, T, G_F32, false, B, g.n_h * g.d_r, g.d_cq, q.cq, g.d_cq, 0, w->W_QR,
-                       g.d_cq, 0, q.qr, (long)g.n_h * g.d_r, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, T, G_F32, b_layout(wt, false), B, g.n_h * g.d_h, g.d_cq, q.cq, g.d_cq,
+                       0, w->W_UQ, g.d_cq, 0, q.qc, (long)g.n_h * g.d_h, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, T, G_F32, b_layout(wt, false), B, g.n_h * g.d_r, g.d_cq, q.cq, g.d_cq,
+                       0, w->W_QR, g.d_cq, 0, q.qr, (long)g.n_h * g.d_r, 0, 1, 1.f, s));
   // absorbed query q~_i = W_UK,i^T q^C_i, scaled (order B)
-  MLA_TRY(gemm_generic(G_F32, T, T, true, B, g.d_c, g.d_h, q.qc, (long)g.n_h * g.d_h, g.d_h,
-                       w->W_UK, g.d_c, (long)g.d_h * g.d_c, q_abs, (long)g.n_h * g.row, g.row,
-                       g.n_h, g.scale, s));
+  MLA_TRY(gemm_generic(G_F32, T, T, b_layout(wt, true), B, g.d_c, g.d_h, q.qc, (long)g.n_h * g.d_h,
+                       g.d_h, w->W_UK, g.d_c, (long)g.d_h * g.d_c, q_abs,
+                       (long)g.n_h * g.row, g.row, g.n_h, g.scale, s));
   // RoPE(q^R_i), scaled, packed after q~_i
   MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
   return MLA_OK;
@@ -316,36 +318,44 @@ int run_output(const Geo& g, const mla_weights* w, const void* lat, int B, void*
   Carver c(ws);
   OutWs o;
   carve_out(c, g, B, &o);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
   if (is_v2_fast(g)) {
     const long nq = (long)g.n_h * g.d_h;
     const GemmTile to = tile_o(g);
     // o_i = W_UV,i o~_i: weight rows of head i read the latent row of head i
     MLA_TRY(wgemm(tile_uv(g), B, (int)nq, g.d_c, lat, (long)g.n_h * g.d_c, g.d_c, g.d_h, w->W_UV,
-                  o.o16, nq, 0, false, 1.f, s, false, true));
+                  o.o16, nq, 0, false, 1.f, s, false, true, wt));
     // u = W_O [o_0 | ... | o_{n_h-1}], split over n_h*d_h, reduced to bf16
     MLA_TRY(wgemm(to, B, g.d, (int)nq, o.o16, nq, 0, 0, w->W_O, o.u_part, g.d, (long)B * g.d, true,
-                  1.f, s, true));
+                  1.f, s, true, false, wt));
     MLA_TRY(splitk_reduce(B, g.d, to.splits, o.u_part, (long)B * g.d, out, g.d, s));
     return MLA_OK;
   }
   const GType T = st(g);
   // o_i = W_UV,i o~_i
-  MLA_TRY(gemm_generic(T, T, G_F32, false, B, g.d_h, g.d_c, lat, (long)g.n_h * g.d_c, g.d_c,
-                       w->W_UV, g.d_c, (long)g.d_h * g.d_c, o.o, (long)g.n_h * g.d_h, g.d_h, g.n_h,
-                       1.f, s));
+  MLA_TRY(gemm_generic(T, T, G_F32, b_layout(wt, false), B, g.d_h, g.d_c, lat, (long)g.n_h * g.d_c,
+                       g.d_c, w->W_UV, g.d_c, (long)g.d_h * g.d_c, o.o,
+                       (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f, s));
   // u = W_O [o_0 | ... | o_{n_h-1}]
-  MLA_TRY(gemm_generic(G_F32, T, T, false, B, g.d, g.n_h * g.d_h, o.o, (long)g.n_h * g.d_h, 0,
-                       w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, T, T, b_layout(wt, false), B, g.d, g.n_h * g.d_h, o.o,
+                       (long)g.n_h * g.d_h, 0, w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1,
+                       1.f, s));
   return MLA_OK;
 }
 
 bool weights_ok(const mla_weights* w, bool query, bool output, bool append, bool kv) {
   if (!w) return false;
+  if (w->layout != MLA_LAYOUT_ROWS && w->layout != MLA_LAYOUT_TILES) return false;
   if (query && (!w->W_DQ || !w->W_UQ || !w->W_QR || !w->W_UK)) return false;
   if (output && (!w->W_UV || !w->W_O)) return false;
   if (append && (!w->W_DKV || !w->W_KR)) return false;
   if (kv && (!w->W_UK || !w->W_UV)) return false;
   return true;
+}
+
+// weights the geometry cannot read in their layout
+int layout_status(const Geo& g, const mla_weights* w) {
+  return w->layout == MLA_LAYOUT_TILES && !tiles_ok(g) ? MLA_ERR_UNSUPPORTED : MLA_OK;
 }
 
 }  // namespace
@@ -393,6 +403,58 @@ int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void
   return hip_status(rope_table_fill(d_table, max_pos, g.d_r, g.base, (hipStream_t)stream));
 }
 
+// rows and columns of the eight matrices, in the order of mla_weights
+static void weight_shapes(const Geo& g, long rc[8][2]) {
+  const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
+  const long shapes[8][2] = {{g.d_c, g.d}, {g.d_r, g.d}, {g.d_cq, g.d}, {nq, g.d_cq},
+                             {nr, g.d_cq}, {nq, g.d_c}, {nq, g.d_c}, {g.d, nq}};
+  for (int i = 0; i < 8; ++i) rc[i][0] = shapes[i][0], rc[i][1] = shapes[i][1];
+}
+
+size_t mla_packed_weights_size(const mla_config* cfg) {
+  Geo g;
+  if (!resolve(cfg, &g) || !tiles_ok(g)) return 0;
+  long rc[8][2];
+  weight_shapes(g, rc);
+  size_t n = 0;
+  for (int i = 0; i < 8; ++i) n += al((size_t)rc[i][0] * rc[i][1] * g.esize());
+  return n;
+}
+
+int mla_pack_weights(const mla_config* cfg, const mla_weights* src, void* d_dst,
+                     size_t dst_bytes, mla_weights* out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !src || !out || src->layout != MLA_LAYOUT_ROWS)
+    return MLA_ERR_INVALID_ARG;
+  if (!tiles_ok(g)) return MLA_ERR_UNSUPPORTED;
+  const size_t total = mla_packed_weights_size(cfg);
+  int r = check_ws(d_dst, dst_bytes, total);
+  if (r) return r;
+  long rc[8][2];
+  weight_shapes(g, rc);
+  const void* in[8] = {src->W_DKV, src->W_KR, src->W_DQ, src->W_UQ,
+                       src->W_QR, src->W_UK, src->W_UV, src->W_O};
+  const uintptr_t d0 = (uintptr_t)d_dst, d1 = d0 + total;
+  for (int i = 0; i < 8; ++i) {
+    const uintptr_t s0 = (uintptr_t)in[i], s1 = s0 + (size_t)rc[i][0] * rc[i][1] * g.esize();
+    if (in[i] && s0 < d1 && d0 < s1) return MLA_ERR_INVALID_ARG;
+  }
+  mla_weights res{};
+  const void** dst[8] = {&res.W_DKV, &res.W_KR, &res.W_DQ, &res.W_UQ,
+                         &res.W_QR, &res.W_UK, &res.W_UV, &res.W_O};
+  char* p = (char*)d_dst;
+  for (int i = 0; i < 8; ++i) {
+    if (in[i]) {
+      MLA_TRY(pack_tiles(in[i], rc[i][0], rc[i][1], g.esize(), p, (hipStream_t)stream));
+      *dst[i] = p;
+    }
+    p += al((size_t)rc[i][0] * rc[i][1] * g.esize());
+  }
+  res.layout = MLA_LAYOUT_TILES;
+  *out = res;
+  return MLA_OK;
+}
+
 size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_len,
                           int num_splits) {
   Geo g;
@@ -416,6 +478,7 @@ int mla_append_kv(const mla_config* cfg, const mla_weights* w, const void* h,
   if (!resolve(cfg, &g) || !weights_ok(w, false, false, true, false) || T < 0 || num_pages < 0 ||
       rope_len < 0)
     return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
   if (T == 0) return MLA_OK;
   if (!h || !positions || !slot_mapping || !rope_table || !kv_cache || num_pages == 0 ||
       rope_len == 0)
@@ -425,11 +488,12 @@ int mla_append_kv(const mla_config* cfg, const mla_weights* w, const void* h,
   hipStream_t s = (hipStream_t)stream;
   float* y = (float*)workspace;
   const GType Ty = st(g);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
   // c^KV_t = W_DKV h_t into columns [0, d_c); W_KR h_t into [d_c, d_c + d_r)
-  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_c, g.d, h, g.d, 0, w->W_DKV, g.d, 0, y, g.row,
-                       0, 1, 1.f, s));
-  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_r, g.d, h, g.d, 0, w->W_KR, g.d, 0,
-                       y + g.d_c, g.row, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_c, g.d, h, g.d, 0, w->W_DKV,
+                       g.d, 0, y, g.row, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_r, g.d, h, g.d, 0, w->W_KR,
+                       g.d, 0, y + g.d_c, g.row, 0, 1, 1.f, s));
   MLA_TRY(append_finish(g, y, positions, slot_mapping, T, rope_table, rope_len, kv_cache,
                         num_pages, s));
   return MLA_OK;
@@ -441,6 +505,7 @@ int mla_decode_query(const mla_config* cfg, const mla_weights* w, const void* h,
   Geo g;
   if (!resolve(cfg, &g) || !weights_ok(w, true, false, false, false) || B < 0 || rope_len < 0)
     return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
   if (B == 0) return MLA_OK;
   if (!h || !positions || !rope_table || rope_len == 0 || !q_abs) return MLA_ERR_INVALID_ARG;
   int r = check_ws(workspace, ws_bytes, ws_query(g, B));
@@ -485,6 +550,7 @@ int mla_decode_output(const mla_config* cfg, const mla_weights* w, const void* l
   Geo g;
   if (!resolve(cfg, &g) || !weights_ok(w, false, true, false, false) || B < 0)
     return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
   if (B == 0) return MLA_OK;
   if (!latent_out || !out) return MLA_ERR_INVALID_ARG;
   int r = check_ws(workspace, ws_bytes, ws_out(g, B));
@@ -500,6 +566,7 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
   Geo g;
   if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, false) || rope_len < 0)
     return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
   // q_abs stands in for the (not yet computed) absorbed query in the checks
   int r = check_attn_args(g, h, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
                           num_splits);
@@ -532,6 +599,7 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
   if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, true) || T < 0 || kv_len < 0 ||
       num_pages < 0 || max_pages < 0 || rope_len < 0)
     return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
   if (T == 0) return MLA_OK;
   if (!h || !positions || !kv_cache || !page_table || !rope_table || !out || kv_len == 0 ||
       num_pages == 0 || rope_len == 0)
@@ -545,30 +613,34 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
   PrefillWs p;
   carve_prefill(c, g, T, kv_len, &p);
   const GType Ty = st(g);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
   const long wq = (long)g.n_h * (g.d_h + g.d_r);
   // query: c^Q, then per head [q^C_i | q^R_i] (192-d at V2), RoPE on q^R
-  MLA_TRY(gemm_generic(Ty, Ty, G_F32, false, T, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d, 0, p.cq,
-                       g.d_cq, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_cq, g.d, h, g.d, 0, w->W_DQ,
+                       g.d, 0, p.cq, g.d_cq, 0, 1, 1.f, s));
   // (the softmax scale is folded into q; RoPE is linear, so rotating the
   // scaled q^R equals scaling the rotated one)
-  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, T, g.d_h, g.d_cq, p.cq, g.d_cq, 0, w->W_UQ,
-                       g.d_cq, (long)g.d_h * g.d_cq, p.q, wq, g.d_h + g.d_r, g.n_h, g.scale, s));
-  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, T, g.d_r, g.d_cq, p.cq, g.d_cq, 0, w->W_QR,
-                       g.d_cq, (long)g.d_r * g.d_cq, p.q + g.d_h, wq, g.d_h + g.d_r, g.n_h,
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), T, g.d_h, g.d_cq, p.cq, g.d_cq, 0,
+                       w->W_UQ, g.d_cq, (long)g.d_h * g.d_cq, p.q, wq, g.d_h + g.d_r, g.n_h,
                        g.scale, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), T, g.d_r, g.d_cq, p.cq, g.d_cq, 0,
+                       w->W_QR, g.d_cq, (long)g.d_r * g.d_cq, p.q + g.d_h, wq, g.d_h + g.d_r,
+                       g.n_h, g.scale, s));
   MLA_TRY(rope_inplace_heads(g, p.q, T, wq, g.d_h, positions, rope_table, rope_len, s));
   // order A: decompress k_j = [W_UK,i c_j | k^R_j] and v_j = W_UV,i c_j per head
   MLA_TRY(gather_rows_f32(g, kv_cache, num_pages, page_table, max_pages, kv_len, p.rows, s));
-  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, kv_len, g.d_h, g.d_c, p.rows, g.row, 0, w->W_UK,
-                       g.d_c, (long)g.d_h * g.d_c, p.kbuf, wq, g.d_h + g.d_r, g.n_h, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), kv_len, g.d_h, g.d_c, p.rows, g.row,
+                       0, w->W_UK, g.d_c, (long)g.d_h * g.d_c, p.kbuf, wq, g.d_h + g.d_r,
+                       g.n_h, 1.f, s));
   MLA_TRY(broadcast_kr(g, p.rows, kv_len, p.kbuf, s));
-  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, false, kv_len, g.d_h, g.d_c, p.rows, g.row, 0, w->W_UV,
-                       g.d_c, (long)g.d_h * g.d_c, p.vbuf, (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f,
-                       s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), kv_len, g.d_h, g.d_c, p.rows, g.row,
+                       0, w->W_UV, g.d_c, (long)g.d_h * g.d_c, p.vbuf,
+                       (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f, s));
   // causal softmax attention with 192-d scores and 128-d values, then W_O
   MLA_TRY(attn_prefill_generic(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, rope_len, p.o, s));
-  MLA_TRY(gemm_generic(G_F32, Ty, Ty, false, T, g.d, g.n_h * g.d_h, p.o, (long)g.n_h * g.d_h, 0,
-                       w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, Ty, b_layout(wt, false), T, g.d, g.n_h * g.d_h, p.o,
+                       (long)g.n_h * g.d_h, 0, w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1,
+                       1.f, s));
   return MLA_OK;
 }
 

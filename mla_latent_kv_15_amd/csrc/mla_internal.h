@@ -81,16 +81,40 @@ __device__ inline long blk_index(int m, int k, int K) {
           (((k >> 3) & 3) << 4) + (m & 15)) * 8 + (k & 7);
 }
 
+// Tiled weight layout (MLA_LAYOUT_TILES): element (r, c) of a [R][C] matrix
+// (R % 16 == 0, C % 32 == 0) sits in tile (r / 16, c / 32), 512 elements,
+// tiles in row-major order; inside a tile at (16 ((c / 8) % 4) + r % 16) * 8
+// + c % 8: the B operand of one 16x16x32 MFMA in lane order.
+__host__ __device__ inline long tile_index(long r, long c, long C) {
+  return (((r >> 4) * (C >> 5) + (c >> 5)) * 64 + (((c >> 3) & 3) << 4) + (r & 15)) * 8 + (c & 7);
+}
+// The geometry admits the tiled layout for all eight matrices and their
+// per-head slices (16-row aligned).
+inline bool tiles_ok(const Geo& g) {
+  return g.d % 32 == 0 && g.d_cq % 32 == 0 && g.d_c % 32 == 0 && (g.n_h * g.d_h) % 32 == 0 &&
+         g.d_h % 16 == 0 && g.d_r % 16 == 0;
+}
+
 // ---------------------------------------------------------------------------
 // generic kernels (any geometry, fp32 or bf16 storage)
 // ---------------------------------------------------------------------------
 enum GType { G_F32 = 0, G_BF16 = 1 };
 
-// C[z][m][n] = alpha * sum_k A[z][m][k] * B[z](n, k); B(n,k) = B[n*ldb+k] or
-// B[k*ldb+n] when b_kmajor.  Types are element types of A, B, C.
-hipError_t gemm_generic(GType ta, GType tb, GType tc, bool b_kmajor, int M, int N, int K,
+// How the generic GEMM finds B(n, k): row-major B[n][k] or B[k][n] (ldb =
+// its row length), or the same matrices in the tiled layout (ldb = columns).
+enum BLayout { B_NK = 0, B_KN = 1, B_NK_TILES = 2, B_KN_TILES = 3 };
+inline BLayout b_layout(bool tiled, bool kmajor) {
+  return (BLayout)((tiled ? 2 : 0) + (kmajor ? 1 : 0));
+}
+
+// C[z][m][n] = alpha * sum_k A[z][m][k] * B[z](n, k), B(n, k) per bl.  Types
+// are element types of A, B, C.
+hipError_t gemm_generic(GType ta, GType tb, GType tc, BLayout bl, int M, int N, int K,
                         const void* A, long lda, long sA, const void* B, long ldb, long sB,
                         void* C, long ldc, long sC, int batch, float alpha, hipStream_t s);
+
+// dst = src ([R][C] row-major) in the tiled layout; elem_bytes 2 or 4.
+hipError_t pack_tiles(const void* src, long R, long C, int elem_bytes, void* dst, hipStream_t s);
 
 hipError_t rope_table_fill(float* table, int max_pos, int d_r, double base, hipStream_t s);
 
@@ -132,7 +156,8 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, in
                           int n_wg_launch, void* part_o, float* part_ml, hipStream_t s);
 // (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
 //  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
-// Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, X bf16 rows);
+// Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, row-major
+// or, w_tiled, in the tiled layout; X bf16 rows);
 // X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx
 // (n_group <= 0: one group).  A work-group streams 16 rb rows x K / splits.
 // splits > 1 requires out_f32: Y is fp32 partials [splits][M][ldy]; else Y is
@@ -150,17 +175,18 @@ GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split);
 // within the compute units).
 hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W1, int N1,
                       void* Y1, long ldy1, const void* W2, int N2, float* Y2, long ldy2,
-                      hipStream_t s);
+                      bool w_tiled, hipStream_t s);
 hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
                  long x_group_stride, int n_group, const void* W, void* Y, long ldy,
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s,
-                 bool x_blocked = false, bool y_blocked = false);
+                 bool x_blocked = false, bool y_blocked = false, bool w_tiled = false);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
-// q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16).
-hipError_t absorb_v2(int M, const void* qc, const void* W_UK, void* q_abs, float scale,
-                     const float* q_r, const int32_t* positions, const float* rope, int rope_len,
-                     hipStream_t s);
+// q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16; W_UK
+// row-major or tiled).
+hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
+                     float scale, const float* q_r, const int32_t* positions, const float* rope,
+                     int rope_len, hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
 hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);

@@ -30,6 +30,9 @@ OP_DECODE_QUERY = 3
 OP_DECODE_ATTENTION = 4
 OP_DECODE_OUTPUT = 5
 
+LAYOUT_ROWS = 0
+LAYOUT_TILES = 1
+
 c_int, c_size_t, c_void_p, c_float, c_double = (ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
                                                 ctypes.c_float, ctypes.c_double)
 
@@ -44,7 +47,7 @@ WEIGHT_ORDER = ("W_DKV", "W_KR", "W_DQ", "W_UQ", "W_QR", "W_UK", "W_UV", "W_O")
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in WEIGHT_ORDER]
+    _fields_ = [(n, c_void_p) for n in WEIGHT_ORDER] + [("layout", c_int)]
 
 
 class MLAError(RuntimeError):
@@ -61,6 +64,8 @@ _SIGS = {
     "mla_version": (c_int, []),
     "mla_rope_table_init": (c_int, [_P, c_int, _P, _P]),
     "mla_workspace_size": (c_size_t, [_P, c_int, c_int, c_int, c_int]),
+    "mla_packed_weights_size": (c_size_t, [_P]),
+    "mla_pack_weights": (c_int, [_P, _P, _P, c_size_t, _P, _P]),
     "mla_append_kv": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, _P, c_size_t, _P]),
     "mla_decode": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, _P, c_int,
                            c_int, _P, c_size_t, _P, _P]),
@@ -111,8 +116,9 @@ def make_config(shape, page_size: int = 64, dtype: str = "bf16", softmax_scale: 
 
 
 def make_weights(tensors: dict) -> Weights:
+    """Row-major weights (MLA_LAYOUT_ROWS) from device tensors."""
     return Weights(*[tensors[n].data_ptr() if tensors.get(n) is not None else None
-                     for n in WEIGHT_ORDER])
+                     for n in WEIGHT_ORDER], LAYOUT_ROWS)
 
 
 def _ptr(t):
@@ -133,6 +139,21 @@ def _ws(ws):
 def workspace_size(cfg: Config, op: int, batch: int, max_kv_len: int = 0,
                    num_splits: int = 0) -> int:
     return int(load().mla_workspace_size(ctypes.byref(cfg), op, batch, max_kv_len, num_splits))
+
+
+def packed_weights_size(cfg: Config) -> int:
+    return int(load().mla_packed_weights_size(ctypes.byref(cfg)))
+
+
+def pack_weights(cfg: Config, weights: Weights, dst, stream=None) -> Weights:
+    """Tiled copies (MLA_LAYOUT_TILES) of row-major `weights` in the device
+    buffer `dst` (at least packed_weights_size bytes, kept alive by the
+    caller while the result is in use)."""
+    out = Weights()
+    _check("mla_pack_weights", load().mla_pack_weights(
+        ctypes.byref(cfg), ctypes.byref(weights), _ptr(dst), dst.numel() * dst.element_size(),
+        ctypes.byref(out), _stream(stream)))
+    return out
 
 
 def rope_table_init(cfg: Config, max_pos: int, table, stream=None):

@@ -110,3 +110,44 @@ def test_empty_batches_are_noops(L):
     assert L.mla_decode_output(ctypes.byref(c), ctypes.byref(wf), z, 0, z, 0, z, z) == 0
     assert L.mla_prefill(ctypes.byref(c), ctypes.byref(wf), z, z, z, 0, z, 0, 0, 0, z, 0, z, 0, z,
                          z) == 0
+
+
+def test_packed_weights_size_and_checks(L):
+    """Tiled weights: byte count, geometry support and argument checks, all
+    decided on the host before anything is enqueued."""
+    c = _cfg()
+    s = inputs.V2
+    mats = [s.d_c * s.d, s.d_r * s.d, s.d_cq * s.d, s.n_h * s.d_h * s.d_cq, s.n_h * s.d_r * s.d_cq,
+            s.n_h * s.d_h * s.d_c, s.n_h * s.d_h * s.d_c, s.d * s.n_h * s.d_h]
+    need = sum(((2 * m + 255) // 256) * 256 for m in mats)
+    assert lib.packed_weights_size(c) == need
+    assert lib.packed_weights_size(_cfg(dtype="f32")) == sum(((4 * m + 255) // 256) * 256
+                                                             for m in mats)
+    # TINY has d_r = 8 and d_cq = 48: no tiled layout
+    t = lib.make_config(inputs.TINY, 64, "f32")
+    assert lib.packed_weights_size(t) == 0
+    p = ctypes.c_void_p(1 << 20)
+    src = lib.Weights(*([4096] * 8))
+    out = lib.Weights()
+    pk = L.mla_pack_weights
+    assert pk(ctypes.byref(t), ctypes.byref(src), p, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_UNSUPPORTED
+    assert pk(None, ctypes.byref(src), p, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_INVALID_ARG
+    assert pk(ctypes.byref(c), None, p, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_INVALID_ARG
+    assert pk(ctypes.byref(c), ctypes.byref(src), p, 1 << 40, None, None) == lib.MLA_ERR_INVALID_ARG
+    tiled = lib.Weights(*([4096] * 8), lib.LAYOUT_TILES)
+    assert pk(ctypes.byref(c), ctypes.byref(tiled), p, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_INVALID_ARG
+    assert pk(ctypes.byref(c), ctypes.byref(src), p, need - 1, ctypes.byref(out), None) == lib.MLA_ERR_WORKSPACE
+    assert pk(ctypes.byref(c), ctypes.byref(src), None, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_WORKSPACE
+    assert pk(ctypes.byref(c), ctypes.byref(src), ctypes.c_void_p((1 << 20) + 64), 1 << 40,
+              ctypes.byref(out), None) == lib.MLA_ERR_WORKSPACE
+    # destination overlapping a source matrix
+    ov = lib.Weights(*([None] * 7), (1 << 20) + 4096)
+    assert pk(ctypes.byref(c), ctypes.byref(ov), p, 1 << 40, ctypes.byref(out), None) == lib.MLA_ERR_INVALID_ARG
+    # entry points reject an unknown layout, and tiles on a geometry without them
+    z = ctypes.c_void_p(4096)
+    bad = lib.Weights(*([4096] * 8), 2)
+    assert L.mla_decode_output(ctypes.byref(c), ctypes.byref(bad), z, 1, z, 1 << 40, z, None) == lib.MLA_ERR_INVALID_ARG
+    tt = lib.Weights(*([4096] * 8), lib.LAYOUT_TILES)
+    assert L.mla_decode_output(ctypes.byref(t), ctypes.byref(tt), z, 1, z, 1 << 40, z, None) == lib.MLA_ERR_UNSUPPORTED
+    assert L.mla_append_kv(ctypes.byref(t), ctypes.byref(tt), z, z, z, 3, z, 10, z, 1, z, 1 << 30,
+                           None) == lib.MLA_ERR_UNSUPPORTED
