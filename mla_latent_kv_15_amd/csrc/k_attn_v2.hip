@@ -735,6 +735,7 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
                                                          const float* __restrict__ part_ml,
                                                          __bf16* __restrict__ lat_out) {
   __shared__ float w[kCombSegs][32];
+  __shared__ float2 s_ml[kCombSegs][32];
   __shared__ float s_M[32], s_inv[32];
   __shared__ __bf16 stage[32][kDc + 8];
   const int b = blockIdx.x, n = blockIdx.y, t = threadIdx.x;
@@ -745,15 +746,26 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     for (int e = t; e < 32 * kDc; e += 256) out[e] = (__bf16)__builtin_nanf("");
     return;
   }
+  // (m, l) of every segment of the head group: one parallel load into LDS
+  // when they fit (else read in the loops below)
+  const bool in_lds = cnt <= kCombSegs;
+  if (in_lds)
+    for (int e = t; e < cnt * 32; e += 256)
+      s_ml[e >> 5][e & 31] =
+          *(const float2*)(part_ml + ((long)(k0 + (e >> 5)) * kHeads + n * 32 + (e & 31)) * 2);
+  __syncthreads();
+  auto ml_of = [&](int s, int hh) -> float2 {
+    if (in_lds) return s_ml[s][hh];
+    return *(const float2*)(part_ml + ((long)(k0 + s) * kHeads + n * 32 + hh) * 2);
+  };
   // per-head max and normaliser
   if (t < 32) {
-    const int hd = n * 32 + t;
     float M = -INFINITY;
-    for (int s = 0; s < cnt; ++s) M = fmaxf(M, part_ml[((long)(k0 + s) * kHeads + hd) * 2]);
+    for (int s = 0; s < cnt; ++s) M = fmaxf(M, ml_of(s, t).x);
     float L = 0.f;
     for (int s = 0; s < cnt; ++s) {
-      const float* ml = part_ml + ((long)(k0 + s) * kHeads + hd) * 2;
-      L += ml[1] * __expf(ml[0] - M);
+      const float2 ml = ml_of(s, t);
+      L += ml.y * __expf(ml.x - M);
     }
     s_M[t] = M;
     s_inv[t] = 1.f / L;
@@ -771,21 +783,34 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     __syncthreads();
     for (int e = t; e < nc * 32; e += 256) {
       const int s = e >> 5, hh = e & 31;
-      const float* ml = part_ml + ((long)(k0 + c0 + s) * kHeads + n * 32 + hh) * 2;
-      w[s][hh] = __expf(ml[0] - s_M[hh]) * s_inv[hh];
+      w[s][hh] = __expf(ml_of(c0 + s, hh).x - s_M[hh]) * s_inv[hh];
     }
     __syncthreads();
-    for (int s = 0; s < nc; ++s) {
-      const float ws = w[s][hd_l];
-      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s) * kHeads * kDc) + t;
+    // four segments' loads in flight at once; the sum still runs over the
+    // segments in order
+    constexpr int kU = 4;
+    for (int s0 = 0; s0 < nc; s0 += kU) {
+      uint2 v[kU][16];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int u = 0; u < kU; ++u) {
+        if (s0 + u >= nc) break;
+        const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s0 + u) * kHeads * kDc) + t;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint2 v = src[((4 * mb + n) * 4 + a) * kThreads];
-          acc[4 * mb + a] += ws * f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-        }
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) v[u][4 * mb + a] = src[((4 * mb + n) * 4 + a) * kThreads];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (s0 + u >= nc) break;
+        const float ws = w[s0 + u][hd_l];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[r] += ws * f32x4{__uint_as_float(v[u][r].x << 16),
+                               __uint_as_float(v[u][r].x & 0xffff0000u),
+                               __uint_as_float(v[u][r].y << 16),
+                               __uint_as_float(v[u][r].y & 0xffff0000u)};
+      }
     }
   }
   // register order -> [head][dim]: element i = 4a + c of accumulator (mb, n)

@@ -20,6 +20,7 @@
 // partial tiles are summed in LDS in a fixed order.  Split-K chunks write fp32
 // partials that a small kernel reduces in a fixed order (deterministic).
 #include "mla_internal.h"
+#include "plan_device.h"
 
 namespace mla {
 
@@ -49,20 +50,21 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // NS > 0: each wave runs exactly NS K-steps of 32, fully unrolled (the
 // decode shapes); NS == 0: a loop over the steps, DEPTH dividing their count.
 // WT: W (and W2) in the tiled layout, K columns.
+#define MLA_WGEMM_PARAMS                                                                     \
+  int M, int K, int kc, int n_groups, const __bf16 *__restrict__ X, long ldx,                \
+      long x_group_stride, int n_group, const __bf16 *__restrict__ W, void *__restrict__ Y,  \
+      long ldy, long y_split_stride, float alpha, int x_blocked, int y_blocked,              \
+      const __bf16 *__restrict__ W2, int n2, float *__restrict__ Y2, long ldy2
+#define MLA_WGEMM_FWD                                                                        \
+  M, K, kc, n_groups, X, ldx, x_group_stride, n_group, W, Y, ldy, y_split_stride, alpha,     \
+      x_blocked, y_blocked, W2, n2, Y2, ldy2
+// the work of work-group (bx, by)
 template <int RB, int NS, int DEPTH, bool OUT_F32, bool WT>
-__global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int n_groups,
-                                                       const __bf16* __restrict__ X, long ldx,
-                                                       long x_group_stride, int n_group,
-                                                       const __bf16* __restrict__ W,
-                                                       void* __restrict__ Y, long ldy,
-                                                       long y_split_stride, float alpha,
-                                                       int x_blocked, int y_blocked,
-                                                       const __bf16* __restrict__ W2, int n2,
-                                                       float* __restrict__ Y2, long ldy2) {
+__device__ __forceinline__ void wgemm_wg(const int bx, const int by, MLA_WGEMM_PARAMS) {
   __shared__ f32x4 red[4][RB][4][64];  // [wave][rb][mb][lane]
-  const int ng = blockIdx.x % n_groups, sp = blockIdx.x / n_groups;
+  const int ng = bx % n_groups, sp = bx / n_groups;
   const int n0 = ng * 16 * RB;
-  const int m0 = blockIdx.y * kMT;
+  const int m0 = by * kMT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int kw = kc >> 2;                       // this wave's share of the chunk
@@ -196,6 +198,23 @@ __global__ __launch_bounds__(256, 1) void wgemm_kernel(int M, int K, int kc, int
   }
 }
 
+template <int RB, int NS, int DEPTH, bool OUT_F32, bool WT>
+__global__ __launch_bounds__(256, 1) void wgemm_kernel(MLA_WGEMM_PARAMS) {
+  wgemm_wg<RB, NS, DEPTH, OUT_F32, WT>(blockIdx.x, blockIdx.y, MLA_WGEMM_FWD);
+}
+
+// The same GEMM and, in one extra work-group (the last of each row), the
+// split-KV plan: a GEMM work-group leaves room on its compute unit for the
+// planner, which then runs beside the GEMM instead of after it.
+template <int RB, int NS, int DEPTH, bool OUT_F32, bool WT>
+__global__ __launch_bounds__(256, 1) void wgemm_plan_kernel(MLA_WGEMM_PARAMS, PlanJob job) {
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0) plan_build(job);
+    return;
+  }
+  wgemm_wg<RB, NS, DEPTH, OUT_F32, WT>(blockIdx.x, blockIdx.y, MLA_WGEMM_FWD);
+}
+
 // out[m][n] = sum_s part[s][m][n] (fixed order), as bf16
 // (blocked: out in the blocked activation layout with K = N)
 __global__ void splitk_reduce_kernel(int M, int N, int S, const float* __restrict__ part,
@@ -207,6 +226,20 @@ __global__ void splitk_reduce_kernel(int M, int N, int S, const float* __restric
   float v = 0.f;
   for (int s = 0; s < S; ++s) v += part[s * split_stride + (long)m * N + n];
   out[blocked ? blk_index(m, n, N) : (long)m * ldo + n] = (__bf16)v;
+}
+
+// the same, four consecutive outputs per thread (N, ldo multiples of 4)
+__global__ void splitk_reduce4_kernel(int M, int N, int S, const float* __restrict__ part,
+                                      long split_stride, __bf16* __restrict__ out, long ldo,
+                                      int blocked) {
+  const long idx = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (idx >= (long)M * N) return;
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) v += *(const f32x4*)(part + s * split_stride + (long)m * N + n);
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  *(bf16x4*)(out + (blocked ? blk_index(m, n, N) : (long)m * ldo + n)) = o;
 }
 
 // The absorbed query of one head i and 64 batch rows: q~_i = scale * W_UK,i^T
@@ -231,6 +264,23 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
   const int r16 = lane & 15, g = lane >> 4;
   const int nmb = min(4, (M - m0 + 15) >> 4);
   const int c0 = 256 * ch + 64 * wave + 4 * r16;
+  // RoPE part, rows 32 ch .. 32 ch + 31 of the block: row m, rotation pair k
+  // of q^R_i (NaN for a position outside the table); four per thread, loaded
+  // before everything else and stored last
+  constexpr int kPer = 32 * 32 / 256;
+  float2 x[kPer], cs[kPer];
+  int mm[kPer];
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = threadIdx.x + 256 * it;
+    const int m = min(m0 + 32 * ch + (e >> 5), M - 1), k = e & 31;
+    mm[it] = m0 + 32 * ch + (e >> 5);
+    x[it] = *(const float2*)(q_r + ((long)m * 128 + head) * 64 + 2 * k);
+    const int pos = positions[m];
+    const bool ok = pos >= 0 && pos < rope_len;
+    cs[it] = *(const float2*)(rope + ((long)(ok ? pos : 0) * 32 + k) * 2);
+    if (!ok) cs[it] = float2{__builtin_nanf(""), __builtin_nanf("")};
+  }
   // row d of W_UK,i, columns c0 .. c0 + 3
   const __bf16* wh = W_UK + (long)head * 128 * 512;
   auto wrow = [&](int d) -> const u32x2* {
@@ -288,23 +338,7 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
       *(bf16x4*)(q_abs + ((long)m * 128 + head) * 576 + c0) = o;
     }
   }
-  // RoPE part, rows 32 ch .. 32 ch + 31 of the block: row m, rotation pair k
-  // of q^R_i (NaN for a position outside the table); four per thread, all
-  // loads issued before the first store
-  constexpr int kPer = 32 * 32 / 256;
-  float2 x[kPer], cs[kPer];
-  int mm[kPer];
-#pragma unroll
-  for (int it = 0; it < kPer; ++it) {
-    const int e = threadIdx.x + 256 * it;
-    const int m = min(m0 + 32 * ch + (e >> 5), M - 1), k = e & 31;
-    mm[it] = m0 + 32 * ch + (e >> 5);
-    x[it] = *(const float2*)(q_r + ((long)m * 128 + head) * 64 + 2 * k);
-    const int pos = positions[m];
-    const bool ok = pos >= 0 && pos < rope_len;
-    cs[it] = *(const float2*)(rope + ((long)(ok ? pos : 0) * 32 + k) * 2);
-    if (!ok) cs[it] = float2{__builtin_nanf(""), __builtin_nanf("")};
-  }
+  // RoPE part (its loads were issued first)
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
     const int e = threadIdx.x + 256 * it, k = e & 31;
@@ -406,6 +440,30 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
   return hipGetLastError();
 }
 
+hipError_t wgemm_with_plan(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
+                          const void* W, float* Y, long ldy, long y_split_stride, bool w_tiled,
+                          const PlanJob& job, hipStream_t s) {
+  // the fully unrolled tile of the W_DQ projection: 3 row blocks, 5 K-steps
+  // per wave
+  constexpr int RB = 3, NS = 5;
+  if (M <= 0 || t.rb != RB || t.splits < 1 || N % (16 * RB) != 0 || K % (128 * t.splits) != 0 ||
+      K / t.splits != 4 * 32 * NS)
+    return hipErrorNotSupported;
+  const int n_groups = N / (16 * RB), kc = K / t.splits;
+  const dim3 grid(n_groups * t.splits + 1, (M + kMT - 1) / kMT);
+#define MLA_WGEMM_PLAN(WT)                                                                      \
+  hipLaunchKernelGGL((wgemm_plan_kernel<RB, NS, NS, true, WT>), grid, dim3(256), 0, s, M, K, kc, \
+                     n_groups, (const __bf16*)X, ldx, 0L, N, (const __bf16*)W, (void*)Y, ldy,    \
+                     y_split_stride, 1.f, 0, 0, (const __bf16*)nullptr, N, (float*)nullptr, 0L,  \
+                     job)
+  if (w_tiled)
+    MLA_WGEMM_PLAN(true);
+  else
+    MLA_WGEMM_PLAN(false);
+#undef MLA_WGEMM_PLAN
+  return hipGetLastError();
+}
+
 hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W1, int N1,
                       void* Y1, long ldy1, const void* W2, int N2, float* Y2, long ldy2,
                       bool w_tiled, hipStream_t s) {
@@ -431,8 +489,13 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
                          long ldo, hipStream_t s, bool blocked) {
   long n = (long)M * N;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
-                     N, S, part, split_stride, (__bf16*)out, ldo, blocked ? 1 : 0);
+  if (N % 4 == 0 && split_stride % 4 == 0 && (blocked || ldo % 4 == 0) &&
+      ((uintptr_t)part & 15) == 0 && ((uintptr_t)out & 7) == 0)
+    hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                       s, M, N, S, part, split_stride, (__bf16*)out, ldo, blocked ? 1 : 0);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       M, N, S, part, split_stride, (__bf16*)out, ldo, blocked ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -207,10 +207,19 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
   if (is_v2_fast(g)) {
     const GemmTile tdq = tile_dq(g);
     const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
-    // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16
-    MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
-                  (long)B * g.d_cq, true, 1.f, s, false, false, wt));
+    // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16; the plan is
+    // built beside the GEMM where its tile allows, else with the reduction
+    hipError_t pe = hipErrorNotSupported;
     if (job)
+      pe = wgemm_with_plan(tdq, B, g.d_cq, g.d, h, g.d, w->W_DQ, q.cq_part, g.d_cq,
+                           (long)B * g.d_cq, wt, *job, s);
+    if (pe == hipErrorNotSupported) {
+      MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
+                    (long)B * g.d_cq, true, 1.f, s, false, false, wt));
+    } else {
+      MLA_TRY(pe);
+    }
+    if (job && pe == hipErrorNotSupported)
       MLA_TRY(splitk_reduce_with_plan(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16,
                                       g.d_cq, true, *job, s));
     else
@@ -218,8 +227,8 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
                             true));
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
     // (one launch for both where the shape fits its tiling)
-    const hipError_t pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq,
-                                     w->W_QR, (int)nr, q.qr, nr, wt, s);
+    pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq, w->W_QR, (int)nr, q.qr,
+                    nr, wt, s);
     if (pe == hipErrorNotSupported) {
       MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
                     false, 1.f, s, true, false, wt));

@@ -169,6 +169,12 @@ struct GemmTile {
   int splits;   // K chunks
 };
 GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split);
+// Split-K fp32 wgemm (row-major X) whose launch also builds the plan of `job`
+// in one extra work-group; hipErrorNotSupported unless the tile is the W_DQ
+// one (3 row blocks, K / splits = 640).
+hipError_t wgemm_with_plan(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
+                          const void* W, float* Y, long ldy, long y_split_stride, bool w_tiled,
+                          const PlanJob& job, hipStream_t s);
 // Y1 = X . W1^T (bf16, N1 rows) and Y2 = X . W2^T (fp32, N2 rows) in one
 // launch of 96-row work-groups without a K split; hipErrorNotSupported when
 // the shape does not fit that tiling (K = 1536, N1 + N2 a multiple of 96

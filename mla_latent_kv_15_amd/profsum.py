@@ -21,7 +21,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates a traffic measurement of the attention path
-TRAFFIC_SOURCES = ("csrc/k_attn_v2.hip", "csrc/k_plan.hip")
+TRAFFIC_SOURCES = ("csrc/k_attn_v2.hip", "csrc/k_plan.hip", "csrc/plan_device.h")
 
 
 def sources_digest() -> str:
