@@ -8,7 +8,8 @@ context lengths uniform on [1024, 8192], 64-token pages in shuffled order,
 bf16 weights/cache with fp32 accumulation, query positions equal to each
 sequence's length (kv_len = L + 1).  The weights are packed once, before
 timing, into the tiled layout the decode GEMMs stream (--weights rows keeps
-them row-major).  Inputs are seeded synthetic data resident in HBM; two
+them row-major; --weights merged runs mla_decode_merged on the products
+W_UK,i^T W_UQ,i and W_O,i W_UV,i computed once before timing, tiled).  Inputs are seeded synthetic data resident in HBM; two
 full buffer sets (weights + cache) alternate between steps so that the 256 MB
 last-level cache cannot serve a step from the previous one.
 
@@ -45,7 +46,7 @@ WORKLOADS = {
 }
 
 
-def build_set(s, B, lo, hi, cid, sub, device, inputs, lib, cfg, tiles):
+def build_set(s, B, lo, hi, cid, sub, device, inputs, lib, cfg, weights):
     import numpy as np
     import torch
     L = inputs.make_lengths(B, lo, hi, cid)
@@ -59,16 +60,25 @@ def build_set(s, B, lo, hi, cid, sub, device, inputs, lib, cfg, tiles):
     Wd = device.weights(W)
     del W
     wbytes = sum(t.numel() * t.element_size() for t in Wd.values())
-    wts, packed = lib.make_weights(Wd), None
-    if tiles:
+    wts, packed, merged = lib.make_weights(Wd), None, None
+    if weights != "rows":
         # one-time layout change at load; the row-major copies are dropped
         packed = device.workspace(lib.packed_weights_size(cfg))
-        wts = lib.pack_weights(cfg, wts, packed)
+        rows = wts
+        wts = lib.pack_weights(cfg, rows, packed)
+        if weights == "merged":
+            Mq = torch.empty(s.n_h * s.d_c, s.d_cq, dtype=torch.bfloat16, device="cuda")
+            Mo = torch.empty(s.d, s.n_h * s.d_c, dtype=torch.bfloat16, device="cuda")
+            lib.merge_weights(cfg, rows, lib.LAYOUT_TILES, Mq, Mo)
+            merged = dict(Mq=Mq, Mo=Mo, mw=lib.MergedWeights(wts.W_DQ, wts.W_QR, Mq.data_ptr(),
+                                                             Mo.data_ptr(), lib.LAYOUT_TILES))
+            wbytes = (Wd["W_DQ"].numel() + Wd["W_QR"].numel() + Mq.numel() + Mo.numel()) * 2
         torch.cuda.synchronize()
         Wd = None
     Hq = inputs.make_hidden(B, s, cid, "bf16", sub=sub)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
     return dict(L=L, kv=kv, paged=paged, cache=cache, Wd=Wd, wts=wts, packed=packed, wbytes=wbytes,
+                merged=merged,
                 h=device.tensor(Hq), pos=i32(L), kv_d=i32(kv), pt=i32(paged.page_table),
                 Hq=Hq, offs=offs)
 
@@ -142,8 +152,9 @@ def main():
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--sets", type=int, default=2)
-    ap.add_argument("--weights", default="tiles", choices=("tiles", "rows"),
-                    help="weight layout (default: packed into tiles before timing)")
+    ap.add_argument("--weights", default="tiles", choices=("tiles", "rows", "merged"),
+                    help="weight layout (default: packed into tiles before timing); merged: "
+                         "decode from the offline products W_UK^T W_UQ and W_O W_UV")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -175,19 +186,24 @@ def main():
     B, lo, hi, cid = WORKLOADS[args.workload]
     cfg = lib.make_config(s, 64, "bf16")
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")
-    sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib, cfg, args.weights == "tiles")
+    sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib, cfg, args.weights)
             for k in range(args.sets)]
     st0 = sets[0]
     max_kv = int(max(int(st["kv"].max()) for st in sets))
     rope = torch.empty(max_kv + 1, s.d_r // 2, 2, dtype=torch.float32, device="cuda")
     lib.rope_table_init(cfg, max_kv + 1, rope)
-    ws = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE, B, max_kv, args.splits))
+    op = lib.OP_DECODE_MERGED if args.weights == "merged" else lib.OP_DECODE
+    ws = device.workspace(lib.workspace_size(cfg, op, B, max_kv, args.splits))
     outs = [torch.empty(B, s.d, dtype=torch.bfloat16, device="cuda") for _ in sets]
 
     def step(i):
         st = sets[i % len(sets)]
-        lib.decode(cfg, st["wts"], st["h"], st["pos"], st["cache"], st["pt"], st["kv_d"], max_kv,
-                   rope, args.splits, ws, outs[i % len(sets)])
+        if args.weights == "merged":
+            lib.decode_merged(cfg, st["merged"]["mw"], st["h"], st["pos"], st["cache"], st["pt"],
+                              st["kv_d"], max_kv, rope, args.splits, ws, outs[i % len(sets)])
+        else:
+            lib.decode(cfg, st["wts"], st["h"], st["pos"], st["cache"], st["pt"], st["kv_d"],
+                       max_kv, rope, args.splits, ws, outs[i % len(sets)])
 
     for i in range(args.warmup):
         step(i)
@@ -230,7 +246,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"mla_decode, DeepSeek-V2 layer, batch {B}, context U[{lo},{hi}], "
+            "workload": f"{'mla_decode_merged' if args.weights == 'merged' else 'mla_decode'}, "
+                        f"DeepSeek-V2 layer, batch {B}, context U[{lo},{hi}], "
                         f"64-token shuffled pages, kv_len = L + 1",
             "batch": B, "context_lo": lo, "context_hi": hi, "page_size": 64,
             "d": s.d, "n_h": s.n_h, "d_h": s.d_h, "d_c": s.d_c, "d_cq": s.d_cq, "d_r": s.d_r,

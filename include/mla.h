@@ -63,7 +63,8 @@ typedef enum {
   MLA_OP_PREFILL = 2,
   MLA_OP_DECODE_QUERY = 3,
   MLA_OP_DECODE_ATTENTION = 4,
-  MLA_OP_DECODE_OUTPUT = 5
+  MLA_OP_DECODE_OUTPUT = 5,
+  MLA_OP_DECODE_MERGED = 6
 } mla_op;
 
 /* Layer geometry.  DeepSeek-V2: d=5120, n_h=128, d_h=128, d_c=512,
@@ -203,6 +204,41 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                 const int32_t* page_table, int max_pages, int kv_len, int T,
                 const float* rope_table, int rope_len, void* workspace, size_t ws_bytes,
                 void* out, void* stream);
+
+/* Offline-merged absorption matrices ([walkthrough] §3 顺序 B: the product
+ * of the two matrices is computed once at deployment and decoding runs order
+ * B on it; [formulas] §三: W^UK is absorbed into the query projection, W^UV
+ * into W^O):
+ *   W_UQK [n_h*d_c][d_cq]: rows [i*d_c, (i+1)*d_c) hold W_UK,i^T W_UQ,i, so
+ *     that q~_i = W_UQK,i c^Q;
+ *   W_OUV [d][n_h*d_c]: columns [i*d_c, (i+1)*d_c) hold W_O,i W_UV,i, W_O,i
+ *     being columns [i*d_h, (i+1)*d_h) of W_O, so that u = sum_i W_OUV,i o~_i.
+ * With W_DQ and W_QR as in mla_weights; all four stored in `layout`. */
+typedef struct mla_merged_weights {
+  const void *W_DQ, *W_QR, *W_UQK, *W_OUV;
+  int layout;
+} mla_merged_weights;
+
+/* Compute W_UQK and W_OUV (sums over d_h in fp32, rounded to cfg->dtype) from
+ * the row-major W_UQ, W_UK, W_UV and W_O of src (src->layout must be
+ * MLA_LAYOUT_ROWS) and store them in `layout` at d_W_UQK
+ * (n_h*d_c*d_cq elements) and d_W_OUV (d*n_h*d_c elements): device buffers
+ * owned by the caller, overlapping nothing else.  A one-time deployment step
+ * (plain SIMT kernels).  Errors: MLA_ERR_INVALID_ARG (null argument, a
+ * needed matrix missing, src not row-major, unknown layout),
+ * MLA_ERR_UNSUPPORTED (MLA_LAYOUT_TILES on a geometry without tiles). */
+int mla_merge_weights(const mla_config* cfg, const mla_weights* src, int layout, void* d_W_UQK,
+                      void* d_W_OUV, void* stream);
+
+/* mla_decode from the merged matrices: Q~_i = [W_UQK,i c^Q | RoPE(W_QR,i
+ * c^Q)] * scale, the same attention, then u = W_OUV o~.  Arguments, layouts
+ * and error behaviour as mla_decode; workspace mla_workspace_size(cfg,
+ * MLA_OP_DECODE_MERGED, B, max_kv_len, num_splits). */
+int mla_decode_merged(const mla_config* cfg, const mla_merged_weights* w, const void* h,
+                      const int32_t* positions, const void* kv_cache, int num_pages,
+                      const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+                      int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+                      void* workspace, size_t ws_bytes, void* out, void* stream);
 
 /* Kernel timing for measurement tools (not needed for computing).  While
  * enabled, every mla_decode / mla_decode_attention call records a HIP event

@@ -54,10 +54,11 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   int M, int K, int kc, int n_groups, const __bf16 *__restrict__ X, long ldx,                \
       long x_group_stride, int n_group, const __bf16 *__restrict__ W, void *__restrict__ Y,  \
       long ldy, long y_split_stride, float alpha, int x_blocked, int y_blocked,              \
-      const __bf16 *__restrict__ W2, int n2, float *__restrict__ Y2, long ldy2
+      const __bf16 *__restrict__ W2, int n2, float *__restrict__ Y2, long ldy2, int y_grp,   \
+      long y_grp_stride
 #define MLA_WGEMM_FWD                                                                        \
   M, K, kc, n_groups, X, ldx, x_group_stride, n_group, W, Y, ldy, y_split_stride, alpha,     \
-      x_blocked, y_blocked, W2, n2, Y2, ldy2
+      x_blocked, y_blocked, W2, n2, Y2, ldy2, y_grp, y_grp_stride
 // the work of work-group (bx, by)
 template <int RB, int NS, int DEPTH, bool OUT_F32, bool WT>
 __device__ __forceinline__ void wgemm_wg(const int bx, const int by, MLA_WGEMM_PARAMS) {
@@ -191,6 +192,9 @@ __device__ __forceinline__ void wgemm_wg(const int bx, const int by, MLA_WGEMM_P
           ((float*)Y)[sp * y_split_stride + (long)m * ldy + n] = alpha * v[i];
         else if (y_blocked)
           ((__bf16*)Y)[blk_index(m, n, n_groups * 16 * RB)] = (__bf16)(alpha * v[i]);
+        else if (y_grp > 0)
+          ((__bf16*)Y)[(long)m * ldy + (long)(n / y_grp) * y_grp_stride + n % y_grp] =
+              (__bf16)(alpha * v[i]);
         else
           ((__bf16*)Y)[(long)m * ldy + n] = (__bf16)(alpha * v[i]);
       }
@@ -386,11 +390,12 @@ GemmTile wgemm_tile(int N, int K, int n_group, bool allow_split) {
 hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
                  long x_group_stride, int n_group, const void* W, void* Y, long ldy,
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s, bool x_blocked,
-                 bool y_blocked, bool w_tiled) {
+                 bool y_blocked, bool w_tiled, int y_grp, long y_grp_stride) {
   if (M <= 0) return hipSuccess;
   if (t.rb < 1 || t.rb > 5 || t.splits < 1 || N % (16 * t.rb) != 0 || K % (128 * t.splits) != 0 ||
       (t.splits > 1 && !out_f32) || (y_blocked && (out_f32 || N % 32 != 0)) ||
-      (x_blocked && n_group > 0 && n_group != N) || (w_tiled && K % 32 != 0))
+      (x_blocked && n_group > 0 && n_group != N) || (w_tiled && K % 32 != 0) ||
+      (y_grp > 0 && (out_f32 || y_blocked)) || y_grp < 0)
     return hipErrorInvalidValue;
   const int n_groups = N / (16 * t.rb);
   const int kc = K / t.splits;
@@ -403,7 +408,7 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
   hipLaunchKernelGGL((wgemm_kernel<RB, NS, D, F32, WT>), grid, dim3(256), 0, s, M, K, kc,      \
                      n_groups, (const __bf16*)X, ldx, x_group_stride, n_group,                 \
                      (const __bf16*)W, Y, ldy, y_split_stride, alpha, xb, yb,                  \
-                     (const __bf16*)nullptr, N, (float*)nullptr, 0L)
+                     (const __bf16*)nullptr, N, (float*)nullptr, 0L, y_grp, y_grp_stride)
 #define MLA_WGEMM_LAUNCH(RB, NS, D)                 \
   do {                                              \
     if (out_f32 && w_tiled)                         \
@@ -455,7 +460,7 @@ hipError_t wgemm_with_plan(const GemmTile& t, int M, int N, int K, const void* X
   hipLaunchKernelGGL((wgemm_plan_kernel<RB, NS, NS, true, WT>), grid, dim3(256), 0, s, M, K, kc, \
                      n_groups, (const __bf16*)X, ldx, 0L, N, (const __bf16*)W, (void*)Y, ldy,    \
                      y_split_stride, 1.f, 0, 0, (const __bf16*)nullptr, N, (float*)nullptr, 0L,  \
-                     job)
+                     0, 0L, job)
   if (w_tiled)
     MLA_WGEMM_PLAN(true);
   else
@@ -477,11 +482,11 @@ hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W
   if (w_tiled)
     hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false, true>), grid, dim3(256), 0, s, M, K, K,
                        n_groups, (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1,
-                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
+                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2, 0, 0L);
   else
     hipLaunchKernelGGL((wgemm_kernel<RB, NS, 4, false, false>), grid, dim3(256), 0, s, M, K, K,
                        n_groups, (const __bf16*)X, (long)K, 0L, N, (const __bf16*)W1, Y1, ldy1,
-                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2);
+                       0L, 1.f, x_blocked ? 1 : 0, 0, (const __bf16*)W2, N1, Y2, ldy2, 0, 0L);
   return hipGetLastError();
 }
 

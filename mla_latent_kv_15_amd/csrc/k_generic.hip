@@ -54,12 +54,15 @@ __device__ inline long b_index(int n, int k, long ldb) {
   return tile_index(k, n, ldb);
 }
 
+// a_kmajor: A(m, k) = A[k * lda + m] instead of A[m * lda + k]; c_tiled: C in
+// the tiled layout with ldc columns (sC then counts elements of that layout)
 template <typename TA, typename TB, typename TC, int BL>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
                                                            const TA* __restrict__ A, long lda,
                                                            long sA, const TB* __restrict__ B,
                                                            long ldb, long sB, TC* __restrict__ C,
-                                                           long ldc, long sC, float alpha) {
+                                                           long ldc, long sC, float alpha,
+                                                           int a_kmajor, int c_tiled) {
   __shared__ float As[16][65];
   __shared__ float Bs[16][65];
   const long z = blockIdx.z;
@@ -77,7 +80,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
     for (int e = threadIdx.x; e < 1024; e += 256) {
       int mm = e >> 4, kk = e & 15;
       int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < K) ? ld(A + (long)gm * lda + gk) : 0.f;
+      As[kk][mm] = (gm < M && gk < K)
+                       ? ld(A + (a_kmajor ? (long)gk * lda + gm : (long)gm * lda + gk))
+                       : 0.f;
     }
     for (int e = threadIdx.x; e < 1024; e += 256) {
       int nn, kk;
@@ -116,7 +121,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int gn = n0 + tx + 16 * j;
-      if (gn < N) st(C + (long)gm * ldc + gn, alpha * acc[i][j]);
+      if (gn < N)
+        st(C + (c_tiled ? tile_index(gm, gn, ldc) : (long)gm * ldc + gn), alpha * acc[i][j]);
     }
   }
 }
@@ -124,11 +130,12 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(int M, int N, int K,
 template <typename TA, typename TB, typename TC>
 hipError_t gemm_launch(BLayout bl, int M, int N, int K, const void* A, long lda, long sA,
                        const void* B, long ldb, long sB, void* C, long ldc, long sC, int batch,
-                       float alpha, hipStream_t s) {
+                       float alpha, hipStream_t s, int a_kmajor, int c_tiled) {
   dim3 grid((N + 63) / 64, (M + 63) / 64, batch);
 #define MLA_GG(BL)                                                                              \
   hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC, BL>), grid, dim3(256), 0, s, M, N, K,     \
-                     (const TA*)A, lda, sA, (const TB*)B, ldb, sB, (TC*)C, ldc, sC, alpha)
+                     (const TA*)A, lda, sA, (const TB*)B, ldb, sB, (TC*)C, ldc, sC, alpha,      \
+                     a_kmajor, c_tiled)
   switch (bl) {
     case B_NK: MLA_GG(B_NK); break;
     case B_KN: MLA_GG(B_KN); break;
@@ -488,10 +495,12 @@ hipError_t pack_tiles(const void* src, long R, long C, int elem_bytes, void* dst
 
 hipError_t gemm_generic(GType ta, GType tb, GType tc, BLayout bk, int M, int N, int K,
                         const void* A, long lda, long sA, const void* B, long ldb, long sB,
-                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s) {
+                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s,
+                        bool a_kmajor, bool c_tiled) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
 #define MLA_G(TA_, TB_, TC_) \
-  return gemm_launch<TA_, TB_, TC_>(bk, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, alpha, s)
+  return gemm_launch<TA_, TB_, TC_>(bk, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, alpha, \
+                                    s, a_kmajor ? 1 : 0, c_tiled ? 1 : 0)
   if (ta == G_F32 && tb == G_F32 && tc == G_F32) MLA_G(float, float, float);
   if (ta == G_BF16 && tb == G_BF16 && tc == G_F32) MLA_G(__bf16, __bf16, float);
   if (ta == G_BF16 && tb == G_BF16 && tc == G_BF16) MLA_G(__bf16, __bf16, __bf16);

@@ -78,6 +78,8 @@ GemmTile tile_uq(const Geo& g) { return wgemm_tile(g.n_h * g.d_h, g.d_cq, 0, fal
 GemmTile tile_qr(const Geo& g) { return wgemm_tile(g.n_h * g.d_r, g.d_cq, 0, false); }
 GemmTile tile_uv(const Geo& g) { return wgemm_tile(g.n_h * g.d_h, g.d_c, g.d_h, false); }
 GemmTile tile_o(const Geo& g) { return wgemm_tile(g.d, g.n_h * g.d_h, 0, true); }
+GemmTile tile_uqk(const Geo& g) { return wgemm_tile(g.n_h * g.d_c, g.d_cq, 0, false); }
+GemmTile tile_ouv(const Geo& g) { return wgemm_tile(g.d, g.n_h * g.d_c, 0, true); }
 
 struct QueryWs {
   float *cq, *qc, *qr;   // generic: fp32 intermediates
@@ -178,6 +180,17 @@ size_t ws_decode(const Geo& g, int B, int ns) {
   // the plan has a region of its own: it is built during the query
   return ws_decode_head(g, B) + al(plan_bytes(B, ns)) + sub;
 }
+// merged decode: the output GEMM's split-K partials (MFMA path)
+size_t ws_out_merged(const Geo& g, int B) {
+  return is_v2_fast(g) ? al(sizeof(float) * (size_t)tile_ouv(g).splits * B * g.d) : 0;
+}
+size_t ws_decode_merged(const Geo& g, int B, int ns) {
+  size_t sub = ws_query(g, B);
+  size_t a = ws_attn(g, B, ns), o = ws_out_merged(g, B);
+  if (a > sub) sub = a;
+  if (o > sub) sub = o;
+  return ws_decode_head(g, B) + al(plan_bytes(B, ns)) + sub;
+}
 size_t ws_append(const Geo& g, int T) { return al(sizeof(float) * (size_t)T * g.row); }
 size_t ws_prefill(const Geo& g, int T, int kv_len) {
   Carver c(nullptr);
@@ -197,24 +210,20 @@ int check_ws(void* ws, size_t have, size_t need) {
 // ---------------------------------------------------------------------------
 // job: a split plan to build during the query (in the launch of the W_DQ
 // reduction on the fast path, which leaves it idle compute units)
-int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* positions, int B,
-              const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s,
-              const PlanJob* job = nullptr) {
-  Carver c(ws);
-  QueryWs q;
-  carve_query(c, g, B, &q);
-  const bool wt = w->layout == MLA_LAYOUT_TILES;
+// c^Q = W_DQ h (eq. (12)): on the MFMA path split over d and reduced to
+// bf16 in the blocked layout (q.cq16), the plan of `job` built beside the GEMM
+// where its tile allows, else with the reduction; on the generic path fp32
+// (q.cq), the plan in a launch of its own.
+int run_cq(const Geo& g, const void* W_DQ, bool wt, const void* h, int B, const QueryWs& q,
+           hipStream_t s, const PlanJob* job) {
   if (is_v2_fast(g)) {
     const GemmTile tdq = tile_dq(g);
-    const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
-    // c^Q = W_DQ h (eq. (12)), split over d, reduced to bf16; the plan is
-    // built beside the GEMM where its tile allows, else with the reduction
     hipError_t pe = hipErrorNotSupported;
     if (job)
-      pe = wgemm_with_plan(tdq, B, g.d_cq, g.d, h, g.d, w->W_DQ, q.cq_part, g.d_cq,
+      pe = wgemm_with_plan(tdq, B, g.d_cq, g.d, h, g.d, W_DQ, q.cq_part, g.d_cq,
                            (long)B * g.d_cq, wt, *job, s);
     if (pe == hipErrorNotSupported) {
-      MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, q.cq_part, g.d_cq,
+      MLA_TRY(wgemm(tdq, B, g.d_cq, g.d, h, g.d, 0, 0, W_DQ, q.cq_part, g.d_cq,
                     (long)B * g.d_cq, true, 1.f, s, false, false, wt));
     } else {
       MLA_TRY(pe);
@@ -225,9 +234,31 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     else
       MLA_TRY(splitk_reduce(B, g.d_cq, tdq.splits, q.cq_part, (long)B * g.d_cq, q.cq16, g.d_cq, s,
                             true));
+    return MLA_OK;
+  }
+  if (job) {
+    const PlanJob& j = *job;
+    MLA_TRY(launch_plan(j.p, j.kv_lens, j.B, j.max_kv_len, j.max_pages, j.page, j.tile,
+                        j.num_splits, s));
+  }
+  MLA_TRY(gemm_generic(st(g), st(g), G_F32, b_layout(wt, false), B, g.d_cq, g.d, h, g.d, 0, W_DQ,
+                       g.d, 0, q.cq, g.d_cq, 0, 1, 1.f, s));
+  return MLA_OK;
+}
+
+int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* positions, int B,
+              const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s,
+              const PlanJob* job = nullptr) {
+  Carver c(ws);
+  QueryWs q;
+  carve_query(c, g, B, &q);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
+  if (int r = run_cq(g, w->W_DQ, wt, h, B, q, s, job)) return r;
+  if (is_v2_fast(g)) {
+    const long nq = (long)g.n_h * g.d_h, nr = (long)g.n_h * g.d_r;
     // q^C = W_UQ c^Q (eq. (13)) in bf16; the RoPE query input W_QR c^Q in fp32
     // (one launch for both where the shape fits its tiling)
-    pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq, w->W_QR, (int)nr, q.qr,
+    hipError_t pe = wgemm_pair(B, g.d_cq, q.cq16, true, w->W_UQ, (int)nq, q.qc16, nq, w->W_QR, (int)nr, q.qr,
                     nr, wt, s);
     if (pe == hipErrorNotSupported) {
       MLA_TRY(wgemm(tile_uq(g), B, (int)nq, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQ, q.qc16, nq, 0,
@@ -244,14 +275,6 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     return MLA_OK;
   }
   const GType T = st(g);
-  if (job) {
-    const PlanJob& j = *job;
-    MLA_TRY(launch_plan(j.p, j.kv_lens, j.B, j.max_kv_len, j.max_pages, j.page, j.tile,
-                        j.num_splits, s));
-  }
-  // c^Q = W_DQ h  (eq. (12))
-  MLA_TRY(gemm_generic(T, T, G_F32, b_layout(wt, false), B, g.d_cq, g.d, h, g.d, 0, w->W_DQ, g.d,
-                       0, q.cq, g.d_cq, 0, 1, 1.f, s));
   // q^C = W_UQ c^Q (eq. (13)) and the per-head RoPE query input W_QR c^Q
   MLA_TRY(gemm_generic(G_F32, T, G_F32, b_layout(wt, false), B, g.n_h * g.d_h, g.d_cq, q.cq, g.d_cq,
                        0, w->W_UQ, g.d_cq, 0, q.qc, (long)g.n_h * g.d_h, 0, 1, 1.f, s));
@@ -349,6 +372,55 @@ int run_output(const Geo& g, const mla_weights* w, const void* lat, int B, void*
   MLA_TRY(gemm_generic(G_F32, T, T, b_layout(wt, false), B, g.d, g.n_h * g.d_h, o.o,
                        (long)g.n_h * g.d_h, 0, w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1,
                        1.f, s));
+  return MLA_OK;
+}
+
+// Query side from the merged matrix: Q~_i = [W_UQK,i c^Q | RoPE(W_QR,i c^Q)]
+// * scale ([walkthrough] §3 顺序 B with the product computed offline).
+int run_query_merged(const Geo& g, const mla_merged_weights* w, const void* h,
+                     const int32_t* positions, int B, const float* rope, int rope_len, void* ws,
+                     void* q_abs, hipStream_t s, const PlanJob* job) {
+  Carver c(ws);
+  QueryWs q;
+  carve_query(c, g, B, &q);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
+  if (int r = run_cq(g, w->W_DQ, wt, h, B, q, s, job)) return r;
+  const long nk = (long)g.n_h * g.d_c, nr = (long)g.n_h * g.d_r;
+  if (is_v2_fast(g)) {
+    // q~ for all heads, scaled, straight into the latent part of each
+    // head's row of q_abs
+    MLA_TRY(wgemm(tile_uqk(g), B, (int)nk, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_UQK, q_abs,
+                  (long)g.n_h * g.row, 0, false, g.scale, s, true, false, wt, g.d_c, g.row));
+    MLA_TRY(wgemm(tile_qr(g), B, (int)nr, g.d_cq, q.cq16, g.d_cq, 0, 0, w->W_QR, q.qr, nr, 0,
+                  true, 1.f, s, true, false, wt));
+  } else {
+    const GType T = st(g);
+    MLA_TRY(gemm_generic(G_F32, T, T, b_layout(wt, false), B, g.d_c, g.d_cq, q.cq, g.d_cq, 0,
+                         w->W_UQK, g.d_cq, (long)g.d_c * g.d_cq, q_abs, (long)g.n_h * g.row,
+                         g.row, g.n_h, g.scale, s));
+    MLA_TRY(gemm_generic(G_F32, T, G_F32, b_layout(wt, false), B, (int)nr, g.d_cq, q.cq, g.d_cq,
+                         0, w->W_QR, g.d_cq, 0, q.qr, nr, 0, 1, 1.f, s));
+  }
+  MLA_TRY(pack_query_rope(g, q.qr, positions, B, rope, rope_len, q_abs, s));
+  return MLA_OK;
+}
+
+// u = W_OUV [o~_0; ...; o~_{n_h-1}] ([formulas] §三: W^UV absorbed into W^O).
+int run_output_merged(const Geo& g, const mla_merged_weights* w, const void* lat, int B, void* ws,
+                      void* out, hipStream_t s) {
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
+  const long nk = (long)g.n_h * g.d_c;
+  if (is_v2_fast(g)) {
+    const GemmTile t = tile_ouv(g);
+    float* part = (float*)ws;
+    MLA_TRY(wgemm(t, B, g.d, (int)nk, lat, nk, 0, 0, w->W_OUV, part, g.d, (long)B * g.d, true,
+                  1.f, s, false, false, wt));
+    MLA_TRY(splitk_reduce(B, g.d, t.splits, part, (long)B * g.d, out, g.d, s));
+    return MLA_OK;
+  }
+  const GType T = st(g);
+  MLA_TRY(gemm_generic(T, T, T, b_layout(wt, false), B, g.d, (int)nk, lat, nk, 0, w->W_OUV, nk, 0,
+                       out, g.d, 0, 1, 1.f, s));
   return MLA_OK;
 }
 
@@ -475,6 +547,7 @@ size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_l
     case MLA_OP_DECODE_QUERY: return ws_query(g, batch);
     case MLA_OP_DECODE_ATTENTION: return ws_attn(g, batch, num_splits);
     case MLA_OP_DECODE_OUTPUT: return ws_out(g, batch);
+    case MLA_OP_DECODE_MERGED: return ws_decode_merged(g, batch, num_splits);
     default: return 0;
   }
 }
@@ -597,6 +670,65 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
                     num_splits, sub, lat, s, &plan);
   if (r) return r;
   return run_output(g, w, lat, B, sub, out, s);
+}
+
+int mla_merge_weights(const mla_config* cfg, const mla_weights* src, int layout, void* d_W_UQK,
+                      void* d_W_OUV, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !src || src->layout != MLA_LAYOUT_ROWS || !src->W_UQ || !src->W_UK ||
+      !src->W_UV || !src->W_O || !d_W_UQK || !d_W_OUV ||
+      (layout != MLA_LAYOUT_ROWS && layout != MLA_LAYOUT_TILES))
+    return MLA_ERR_INVALID_ARG;
+  const bool wt = layout == MLA_LAYOUT_TILES;
+  if (wt && !tiles_ok(g)) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const GType T = st(g);
+  const long nk = (long)g.n_h * g.d_c, nq = (long)g.n_h * g.d_h;
+  // W_UQK,i [d_c][d_cq] = sum_d W_UK,i[d][.] (x) W_UQ,i[d][.]: A(c, d) =
+  // W_UK,i[d][c] (k-major), B(k', d) = W_UQ,i[d][k'] (k-major); head i's rows
+  // start at the same element in either layout
+  MLA_TRY(gemm_generic(T, T, T, B_KN, g.d_c, g.d_cq, g.d_h, src->W_UK, g.d_c,
+                       (long)g.d_h * g.d_c, src->W_UQ, g.d_cq, (long)g.d_h * g.d_cq, d_W_UQK,
+                       g.d_cq, (long)g.d_c * g.d_cq, g.n_h, 1.f, s, true, wt));
+  // W_OUV[.][i d_c + c] = sum_d W_O[.][i d_h + d] W_UV,i[d][c]: A = W_O's head
+  // columns, B(c, d) = W_UV,i[d][c]; head i's column block starts i d_c
+  // elements into a row-major row, 16 i d_c elements into the tiles
+  MLA_TRY(gemm_generic(T, T, T, B_KN, g.d, g.d_c, g.d_h, src->W_O, nq, g.d_h, src->W_UV, g.d_c,
+                       (long)g.d_h * g.d_c, d_W_OUV, nk, wt ? 16L * g.d_c : (long)g.d_c, g.n_h,
+                       1.f, s, false, wt));
+  return MLA_OK;
+}
+
+int mla_decode_merged(const mla_config* cfg, const mla_merged_weights* w, const void* h,
+                      const int32_t* positions, const void* kv_cache, int num_pages,
+                      const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+                      int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+                      void* workspace, size_t ws_bytes, void* out, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !w || !w->W_DQ || !w->W_QR || !w->W_UQK || !w->W_OUV ||
+      (w->layout != MLA_LAYOUT_ROWS && w->layout != MLA_LAYOUT_TILES) || rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (w->layout == MLA_LAYOUT_TILES && !tiles_ok(g)) return MLA_ERR_UNSUPPORTED;
+  int r = check_attn_args(g, h, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
+                          num_splits);
+  if (r || B == 0) return r;
+  if (!h || !positions || !rope_table || rope_len == 0 || !out) return MLA_ERR_INVALID_ARG;
+  r = check_ws(workspace, ws_bytes, ws_decode_merged(g, B, num_splits));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  void* q_abs = c.take((size_t)B * g.n_h * g.row * g.esize());
+  void* lat = c.take((size_t)B * g.n_h * g.d_c * g.esize());
+  PlanPtrs plan;
+  carve_plan(c.take(plan_bytes(B, num_splits)), B, num_splits, &plan);
+  const PlanJob job = plan_job(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits);
+  void* sub = c.base + c.used;
+  r = run_query_merged(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s, &job);
+  if (r) return r;
+  r = run_attention(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
+                    num_splits, sub, lat, s, &plan);
+  if (r) return r;
+  return run_output_merged(g, w, lat, B, sub, out, s);
 }
 
 int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,

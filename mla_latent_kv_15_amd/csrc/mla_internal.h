@@ -107,11 +107,13 @@ inline BLayout b_layout(bool tiled, bool kmajor) {
   return (BLayout)((tiled ? 2 : 0) + (kmajor ? 1 : 0));
 }
 
-// C[z][m][n] = alpha * sum_k A[z][m][k] * B[z](n, k), B(n, k) per bl.  Types
-// are element types of A, B, C.
+// C[z][m][n] = alpha * sum_k A[z](m, k) * B[z](n, k), B(n, k) per bl, A(m, k)
+// = A[m*lda + k] or, a_kmajor, A[k*lda + m]; c_tiled: C (ldc columns) in the
+// tiled layout.  Types are element types of A, B, C.
 hipError_t gemm_generic(GType ta, GType tb, GType tc, BLayout bl, int M, int N, int K,
                         const void* A, long lda, long sA, const void* B, long ldb, long sB,
-                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s);
+                        void* C, long ldc, long sC, int batch, float alpha, hipStream_t s,
+                        bool a_kmajor = false, bool c_tiled = false);
 
 // dst = src ([R][C] row-major) in the tiled layout; elem_bytes 2 or 4.
 hipError_t pack_tiles(const void* src, long R, long C, int elem_bytes, void* dst, hipStream_t s);
@@ -161,7 +163,8 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, in
 // X row m for weight rows n lives at X + (n / n_group) * x_group_stride + m * ldx
 // (n_group <= 0: one group).  A work-group streams 16 rb rows x K / splits.
 // splits > 1 requires out_f32: Y is fp32 partials [splits][M][ldy]; else Y is
-// [M][ldy], bf16 or fp32.  x_blocked: X (ungrouped) is in the blocked
+// [M][ldy], bf16 or fp32 (y_grp > 0, bf16: column n lands at (n / y_grp) *
+// y_grp_stride + n % y_grp of its row).  x_blocked: X (ungrouped) is in the blocked
 // activation layout [ceil(M/64)][K/32][4][64][8] (1 KB per MFMA operand, rows
 // padded to 64); y_blocked: bf16 Y is written in that layout with K = N.
 struct GemmTile {
@@ -185,7 +188,8 @@ hipError_t wgemm_pair(int M, int K, const void* X, bool x_blocked, const void* W
 hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx,
                  long x_group_stride, int n_group, const void* W, void* Y, long ldy,
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s,
-                 bool x_blocked = false, bool y_blocked = false, bool w_tiled = false);
+                 bool x_blocked = false, bool y_blocked = false, bool w_tiled = false,
+                 int y_grp = 0, long y_grp_stride = 0);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16; W_UK

@@ -29,6 +29,7 @@ OP_PREFILL = 2
 OP_DECODE_QUERY = 3
 OP_DECODE_ATTENTION = 4
 OP_DECODE_OUTPUT = 5
+OP_DECODE_MERGED = 6
 
 LAYOUT_ROWS = 0
 LAYOUT_TILES = 1
@@ -48,6 +49,11 @@ WEIGHT_ORDER = ("W_DKV", "W_KR", "W_DQ", "W_UQ", "W_QR", "W_UK", "W_UV", "W_O")
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in WEIGHT_ORDER] + [("layout", c_int)]
+
+
+class MergedWeights(ctypes.Structure):
+    _fields_ = [("W_DQ", c_void_p), ("W_QR", c_void_p), ("W_UQK", c_void_p), ("W_OUV", c_void_p),
+                ("layout", c_int)]
 
 
 class MLAError(RuntimeError):
@@ -73,6 +79,9 @@ _SIGS = {
     "mla_decode_attention": (c_int, [_P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, c_int, _P,
                                      c_size_t, _P, _P]),
     "mla_decode_output": (c_int, [_P, _P, _P, c_int, _P, c_size_t, _P, _P]),
+    "mla_merge_weights": (c_int, [_P, _P, c_int, _P, _P, _P]),
+    "mla_decode_merged": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, _P,
+                                  c_int, c_int, _P, c_size_t, _P, _P]),
     "mla_profile_enable": (c_int, [c_int]),
     "mla_profile_attention_ms": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
     "mla_prefill": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P, c_int, _P,
@@ -211,6 +220,24 @@ def prefill(cfg, weights, h, positions, kv_cache, page_table, kv_len, rope_table
         ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), _ptr(positions), _ptr(kv_cache),
         kv_cache.shape[0], _ptr(page_table), page_table.shape[0], kv_len, h.shape[0],
         _ptr(rope_table), rope_table.shape[0], wp, wn, _ptr(out), _stream(stream)))
+
+
+def merge_weights(cfg, weights: Weights, layout: int, W_UQK, W_OUV, stream=None):
+    """W_UQK [n_h*d_c][d_cq] and W_OUV [d][n_h*d_c] from row-major `weights`,
+    written in `layout` into the device tensors W_UQK and W_OUV."""
+    _check("mla_merge_weights", load().mla_merge_weights(
+        ctypes.byref(cfg), ctypes.byref(weights), layout, _ptr(W_UQK), _ptr(W_OUV),
+        _stream(stream)))
+
+
+def decode_merged(cfg, mweights: MergedWeights, h, positions, kv_cache, page_table, kv_lens,
+                  max_kv_len, rope_table, num_splits, workspace, out, stream=None):
+    wp, wn = _ws(workspace)
+    _check("mla_decode_merged", load().mla_decode_merged(
+        ctypes.byref(cfg), ctypes.byref(mweights), _ptr(h), _ptr(positions), _ptr(kv_cache),
+        kv_cache.shape[0], _ptr(page_table), page_table.shape[1], _ptr(kv_lens), h.shape[0],
+        max_kv_len, _ptr(rope_table), rope_table.shape[0], num_splits, wp, wn, _ptr(out),
+        _stream(stream)))
 
 
 def profile_enable(on: bool):

@@ -202,6 +202,47 @@ def attend_order_b(q_c, q_r, c, k_r, W_UK, W_UV, scale: float) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# order B on matrices multiplied out ahead of time ([walkthrough] §3 顺序 B:
+# the product is computed once at deployment and decoding runs B on it;
+# [formulas] §三: W^UK goes into the query projection, W^UV into W^O)
+# ---------------------------------------------------------------------------
+
+def merged_query_matrix(W_UQ, W_UK, n_h: int) -> np.ndarray:
+    """W_UQK,i = W_UK,i^T W_UQ,i ([d_c][d_c'] per head), stacked by head, so
+    that q~_i = W_UQK,i c^Q.  Returns [n_h * d_c][d_c']."""
+    W_UQ, W_UK = np.asarray(W_UQ, F64), np.asarray(W_UK, F64)
+    d_h = W_UQ.shape[0] // n_h
+    return np.concatenate([W_UK[i * d_h:(i + 1) * d_h].T @ W_UQ[i * d_h:(i + 1) * d_h]
+                           for i in range(n_h)], axis=0)
+
+
+def merged_output_matrix(W_O, W_UV, n_h: int) -> np.ndarray:
+    """W_OUV,i = W_O,i W_UV,i ([d][d_c] per head; W_O,i = the head's d_h
+    columns of W_O), side by side, so that u = sum_i W_OUV,i o~_i.  Returns
+    [d][n_h * d_c]."""
+    W_O, W_UV = np.asarray(W_O, F64), np.asarray(W_UV, F64)
+    d_h = W_UV.shape[0] // n_h
+    return np.concatenate([W_O[:, i * d_h:(i + 1) * d_h] @ W_UV[i * d_h:(i + 1) * d_h]
+                           for i in range(n_h)], axis=1)
+
+
+def decode_merged(h_q, pos: int, c, k_r, Wm: Dict[str, np.ndarray], n_h: int, base: float,
+                  scale: float) -> np.ndarray:
+    """One decode query from the merged matrices (Wm holds W_DQ, W_QR, W_UQK,
+    W_OUV): c^Q = W_DQ h; Q~_i = [W_UQK,i c^Q ; RoPE(W_QR,i c^Q)] * scale;
+    o~ by latent attention over the rows [c_j ; k^R_j]; u = W_OUV [o~_0; ...]."""
+    c, k_r = np.asarray(c, F64), np.asarray(k_r, F64)
+    d_c, d_r = c.shape[1], k_r.shape[1]
+    c_q = np.asarray(Wm["W_DQ"], F64) @ np.asarray(h_q, F64)
+    qt = (np.asarray(Wm["W_UQK"], F64) @ c_q).reshape(n_h, d_c)
+    W_QR = np.asarray(Wm["W_QR"], F64)
+    q_r = np.stack([rope(W_QR[i * d_r:(i + 1) * d_r] @ c_q, pos, base) for i in range(n_h)])
+    Qt = np.concatenate([qt, q_r], axis=1) * scale
+    o_lat = latent_attention(Qt, np.concatenate([c, k_r], axis=1), d_c)
+    return np.asarray(Wm["W_OUV"], F64) @ o_lat.reshape(-1)
+
+
+# ---------------------------------------------------------------------------
 # step 5: integrate ([walkthrough] step 5)
 # ---------------------------------------------------------------------------
 

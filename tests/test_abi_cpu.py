@@ -151,3 +151,39 @@ def test_packed_weights_size_and_checks(L):
     assert L.mla_decode_output(ctypes.byref(t), ctypes.byref(tt), z, 1, z, 1 << 40, z, None) == lib.MLA_ERR_UNSUPPORTED
     assert L.mla_append_kv(ctypes.byref(t), ctypes.byref(tt), z, z, z, 3, z, 10, z, 1, z, 1 << 30,
                            None) == lib.MLA_ERR_UNSUPPORTED
+
+
+def test_merged_entry_points_reject_bad_arguments(L):
+    """mla_merge_weights and mla_decode_merged check everything on the host."""
+    c = _cfg()
+    p = ctypes.c_void_p(1 << 20)
+    src = lib.Weights(*([4096] * 8))
+    mg = L.mla_merge_weights
+    assert mg(ctypes.byref(c), None, 0, p, p, None) == lib.MLA_ERR_INVALID_ARG
+    assert mg(ctypes.byref(c), ctypes.byref(src), 0, None, p, None) == lib.MLA_ERR_INVALID_ARG
+    assert mg(ctypes.byref(c), ctypes.byref(src), 2, p, p, None) == lib.MLA_ERR_INVALID_ARG
+    tiled = lib.Weights(*([4096] * 8), lib.LAYOUT_TILES)
+    assert mg(ctypes.byref(c), ctypes.byref(tiled), 0, p, p, None) == lib.MLA_ERR_INVALID_ARG
+    no_uv = lib.Weights(4096, 4096, 4096, 4096, 4096, 4096, None, 4096)
+    assert mg(ctypes.byref(c), ctypes.byref(no_uv), 0, p, p, None) == lib.MLA_ERR_INVALID_ARG
+    t = lib.make_config(inputs.TINY, 64, "f32")
+    assert mg(ctypes.byref(t), ctypes.byref(src), lib.LAYOUT_TILES, p, p, None) == lib.MLA_ERR_UNSUPPORTED
+    # merged decode: workspace size, weights and arguments
+    assert lib.workspace_size(c, lib.OP_DECODE_MERGED, 64, 8193, 0) > 0
+    assert lib.workspace_size(t, lib.OP_DECODE_MERGED, 3, 40, 0) > 0
+    dm = L.mla_decode_merged
+    mw = lib.MergedWeights(4096, 4096, 4096, None, 0)
+    z = ctypes.c_void_p(4096)
+    assert dm(ctypes.byref(c), ctypes.byref(mw), z, z, z, 4, z, 2, z, 1, 100, z, 10, 0, z, 1 << 40,
+              z, None) == lib.MLA_ERR_INVALID_ARG
+    mw = lib.MergedWeights(4096, 4096, 4096, 4096, 0)
+    # max_kv_len beyond the page table's reach, workspace too small
+    assert dm(ctypes.byref(c), ctypes.byref(mw), z, z, z, 4, z, 2, z, 1, 129, z, 200, 0, z, 1 << 40,
+              z, None) == lib.MLA_ERR_INVALID_ARG
+    assert dm(ctypes.byref(c), ctypes.byref(mw), z, z, z, 4, z, 2, z, 1, 100, z, 200, 0, z, 16,
+              z, None) == lib.MLA_ERR_WORKSPACE
+    mt = lib.MergedWeights(4096, 4096, 4096, 4096, lib.LAYOUT_TILES)
+    assert dm(ctypes.byref(t), ctypes.byref(mt), z, z, z, 4, z, 2, z, 1, 100, z, 200, 0, z, 1 << 40,
+              z, None) == lib.MLA_ERR_UNSUPPORTED
+    assert dm(ctypes.byref(c), ctypes.byref(mw), None, None, None, 0, None, 0, None, 0, 0, None, 0,
+              0, None, 0, None, None) == 0

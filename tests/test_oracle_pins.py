@@ -300,3 +300,57 @@ def test_max_rel_error_metric():
     assert math.isclose(oracle.max_rel_error(y, ref), 0.02)
     y[0, 0] = np.nan
     assert oracle.max_rel_error(y, ref) == float("inf")
+
+
+# ---------------------------------------------------------------------------
+# order B on matrices multiplied out ahead of time
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+def test_merged_matrices_bruteforce(si):
+    """Each entry of W_UK,i^T W_UQ,i and W_O,i W_UV,i as an explicit sum over d_h."""
+    s = SMALL_SHAPES[si]
+    W = _weights64(s, 600 + si)
+    Mq = oracle.merged_query_matrix(W["W_UQ"], W["W_UK"], s.n_h)
+    Mo = oracle.merged_output_matrix(W["W_O"], W["W_UV"], s.n_h)
+    assert Mq.shape == (s.n_h * s.d_c, s.d_cq) and Mo.shape == (s.d, s.n_h * s.d_c)
+    UK, UQ, UV, O = W["W_UK"], W["W_UQ"], W["W_UV"], W["W_O"]
+    for i in range(s.n_h):
+        for c in range(s.d_c):
+            for k in range(s.d_cq):
+                ref = 0.0
+                for d in range(s.d_h):
+                    ref += UK[i * s.d_h + d, c] * UQ[i * s.d_h + d, k]
+                assert abs(Mq[i * s.d_c + c, k] - ref) <= 1e-12 * (1.0 + abs(ref))
+        for n in range(s.d):
+            for c in range(s.d_c):
+                ref = 0.0
+                for d in range(s.d_h):
+                    ref += O[n, i * s.d_h + d] * UV[i * s.d_h + d, c]
+                assert abs(Mo[n, i * s.d_c + c] - ref) <= 1e-12 * (1.0 + abs(ref))
+
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+def test_merged_decode_equals_order_a(si):
+    """The merged matrices give the layer's output (associativity): the same
+    token as order A, and each merged product equals its two factors applied
+    one after the other."""
+    s = SMALL_SHAPES[si]
+    W = _weights64(s, 610 + si)
+    N = 9
+    H = inputs.make_hidden(N, s, 610 + si, "f32").f64()
+    Mq = oracle.merged_query_matrix(W["W_UQ"], W["W_UK"], s.n_h)
+    Mo = oracle.merged_output_matrix(W["W_O"], W["W_UV"], s.n_h)
+    Wm = {"W_DQ": W["W_DQ"], "W_QR": W["W_QR"], "W_UQK": Mq, "W_OUV": Mo}
+    c, kr = oracle.latent_rows(H, W["W_DKV"], W["W_KR"], np.arange(N), 10000.0)
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    u = oracle.decode_merged(H[-1], N - 1, c, kr, Wm, s.n_h, 10000.0, sc)
+    ref = oracle.decode_from_hidden(H, W, s.n_h, 10000.0, order="A")
+    assert _rel(u, ref) < 1e-10
+    rng = np.random.default_rng(si)
+    cq = rng.standard_normal(s.d_cq)
+    q_c = np.stack([W["W_UQ"][i * s.d_h:(i + 1) * s.d_h] @ cq for i in range(s.n_h)])
+    via = oracle.absorbed_query(q_c, np.zeros((s.n_h, s.d_r)), W["W_UK"], 1.0)[:, :s.d_c]
+    assert _rel((Mq @ cq).reshape(s.n_h, s.d_c), via) < 1e-12
+    o_lat = rng.standard_normal((s.n_h, s.d_c))
+    assert _rel(Mo @ o_lat.reshape(-1), oracle.latent_output(o_lat, W["W_UV"], W["W_O"])) < 1e-12
