@@ -144,6 +144,76 @@ def measured_traffic(workload):
         return None
 
 
+def mha_baseline(args, B, lo, hi, cid):
+    """Attention only, same batch: decode over an MHA-equivalent cache (a key
+    and a value per head and token, 64 KB per token) against MLA's latent
+    cache (1152 B per token).  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_15_amd import device, inputs, lib
+    s = inputs.V2
+    cfg = lib.make_config(s, 64, "bf16")
+    lib.load()
+    st = build_set(s, B, lo, hi, cid, 0, device, inputs, lib, cfg, "tiles")
+    kv = st["kv"]
+    max_kv = int(kv.max())
+    rope = torch.empty(max_kv + 1, s.d_r // 2, 2, dtype=torch.float32, device="cuda")
+    lib.rope_table_init(cfg, max_kv + 1, rope)
+    q_lat = torch.empty(B, s.n_h, s.row, dtype=torch.bfloat16, device="cuda")
+    ws = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE_QUERY, B))
+    lib.decode_query(cfg, st["wts"], st["h"], st["pos"], rope, ws, q_lat)
+    # the multi-head cache: same pages, rows of 2 * n_h * d_h bf16, N(0,1)
+    width = 2 * s.n_h * s.d_h
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cid)
+    n_pages = st["paged"].num_pages
+    mha_cache = torch.randn(n_pages, 64, width, dtype=torch.bfloat16, device="cuda", generator=gen)
+    q_mha = torch.randn(B, s.n_h, s.d_h, dtype=torch.bfloat16, device="cuda", generator=gen)
+    ws_m = device.workspace(lib.workspace_size(cfg, lib.OP_MHA_DECODE, B, max_kv, 0))
+    ws_a = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE_ATTENTION, B, max_kv, 0))
+    o_m = torch.empty(B, s.n_h, s.d_h, dtype=torch.bfloat16, device="cuda")
+    o_a = torch.empty(B, s.n_h, s.d_c, dtype=torch.bfloat16, device="cuda")
+
+    def run_mha():
+        lib.mha_decode_attention(cfg, q_mha, mha_cache, st["pt"], st["kv_d"], max_kv, 0, ws_m, o_m)
+
+    def run_mla():
+        lib.decode_attention(cfg, q_lat, st["cache"], st["pt"], st["kv_d"], max_kv, 0, ws_a, o_a)
+
+    res = {}
+    for name, fn, n in (("mha", run_mha, max(3, args.steps // 10)), ("mla", run_mla, args.steps)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n
+    toks = int(kv.sum())
+    mha_bytes = toks * width * 2
+    mla_bytes = toks * BYTES_PER_TOKEN
+    out = {
+        "metric": "decode attention time, MHA-equivalent cache vs MLA latent cache",
+        "unit": "ms", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+        "config": {"workload": f"attention only, DeepSeek-V2 heads (128 x 128), batch {B}, "
+                               f"context U[{lo},{hi}], 64-token shuffled pages",
+                   "cached_tokens": toks},
+        "mha": {"ms": res["mha"], "cache_bytes": mha_bytes,
+                "GBps": mha_bytes / (res["mha"] * 1e-3) / 1e9,
+                "kernels": "mha_decode_kernel + combine_kernel (plan included)"},
+        "mla": {"ms": res["mla"], "cache_bytes": mla_bytes,
+                "GBps": mla_bytes / (res["mla"] * 1e-3) / 1e9,
+                "kernels": "attn_v2_kernel + combine_v2_kernel (plan included)"},
+        "cache_ratio": mha_bytes / mla_bytes,
+        "time_ratio": res["mha"] / res["mla"],
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +227,9 @@ def main():
                          "decode from the offline products W_UK^T W_UQ and W_O W_UV")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--baseline", choices=("mha",), default=None,
+                    help="instead of the step: time decode attention over an MHA-equivalent "
+                         "cache against MLA's on the same batch and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -184,6 +257,9 @@ def main():
     lib.load()
     s = inputs.V2
     B, lo, hi, cid = WORKLOADS[args.workload]
+    if args.baseline == "mha":
+        mha_baseline(args, B, lo, hi, cid)
+        return
     cfg = lib.make_config(s, 64, "bf16")
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")
     sets = [build_set(s, B, lo, hi, cid, k, device, inputs, lib, cfg, args.weights)

@@ -64,7 +64,8 @@ typedef enum {
   MLA_OP_DECODE_QUERY = 3,
   MLA_OP_DECODE_ATTENTION = 4,
   MLA_OP_DECODE_OUTPUT = 5,
-  MLA_OP_DECODE_MERGED = 6
+  MLA_OP_DECODE_MERGED = 6,
+  MLA_OP_MHA_DECODE = 7
 } mla_op;
 
 /* Layer geometry.  DeepSeek-V2: d=5120, n_h=128, d_h=128, d_c=512,
@@ -239,6 +240,25 @@ int mla_decode_merged(const mla_config* cfg, const mla_merged_weights* w, const 
                       const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
                       int max_kv_len, const float* rope_table, int rope_len, int num_splits,
                       void* workspace, size_t ws_bytes, void* out, void* stream);
+
+/* Baseline, not MLA: decode attention over an MHA-equivalent cache, the
+ * multi-head cache the pages weigh MLA against ([formulas] §一 and §三;
+ * [walkthrough] §2).  Every cached token holds a key and a value for each
+ * head (2*n_h*d_h numbers against MLA's d_c + d_r), and head i attends with
+ * its own keys: out[b][i] = sum_j softmax_j(scale * q[b][i] . k_ij) v_ij over
+ * j < kv_lens[b].  Uses cfg's n_h, d_h, page_size and dtype.
+ * q: device [B][n_h][d_h]; out: device [B][n_h][d_h]; kv_cache: device
+ * [num_pages][page_size][2][n_h][d_h] (the keys of all heads, then the
+ * values), 16-byte aligned; page_table, kv_lens, max_kv_len, num_splits and
+ * the NaN rule for invalid entries as mla_decode_attention.  scale <= 0
+ * selects 1/sqrt(d_h).  d_h must be a multiple of 16 with d_h/16 a power of
+ * two <= 64 (MLA_ERR_UNSUPPORTED otherwise).  Workspace:
+ * mla_workspace_size(cfg, MLA_OP_MHA_DECODE, B, max_kv_len, num_splits). */
+int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* kv_cache,
+                             int num_pages, const int32_t* page_table, int max_pages,
+                             const int32_t* kv_lens, int B, int max_kv_len, float scale,
+                             int num_splits, void* workspace, size_t ws_bytes, void* out,
+                             void* stream);
 
 /* Kernel timing for measurement tools (not needed for computing).  While
  * enabled, every mla_decode / mla_decode_attention call records a HIP event

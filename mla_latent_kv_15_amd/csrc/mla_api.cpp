@@ -191,6 +191,12 @@ size_t ws_decode_merged(const Geo& g, int B, int ns) {
   if (o > sub) sub = o;
   return ws_decode_head(g, B) + al(plan_bytes(B, ns)) + sub;
 }
+// MHA baseline: the plan, fp32 partials and their (m, l)
+size_t ws_mha(const Geo& g, int B, int ns) {
+  const PlanDims pd = plan_dims(B, ns);
+  return al(plan_bytes(B, ns)) + al(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_h) +
+         al(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
+}
 size_t ws_append(const Geo& g, int T) { return al(sizeof(float) * (size_t)T * g.row); }
 size_t ws_prefill(const Geo& g, int T, int kv_len) {
   Carver c(nullptr);
@@ -548,6 +554,7 @@ size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_l
     case MLA_OP_DECODE_ATTENTION: return ws_attn(g, batch, num_splits);
     case MLA_OP_DECODE_OUTPUT: return ws_out(g, batch);
     case MLA_OP_DECODE_MERGED: return ws_decode_merged(g, batch, num_splits);
+    case MLA_OP_MHA_DECODE: return ws_mha(g, batch, num_splits);
     default: return 0;
   }
 }
@@ -729,6 +736,40 @@ int mla_decode_merged(const mla_config* cfg, const mla_merged_weights* w, const 
                     num_splits, sub, lat, s, &plan);
   if (r) return r;
   return run_output_merged(g, w, lat, B, sub, out, s);
+}
+
+int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* kv_cache,
+                             int num_pages, const int32_t* page_table, int max_pages,
+                             const int32_t* kv_lens, int B, int max_kv_len, float scale,
+                             int num_splits, void* workspace, size_t ws_bytes, void* out,
+                             void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || B < 0 || num_pages < 0 || max_pages < 0 || max_kv_len < 0 ||
+      num_splits < 0 || num_splits > 4096)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q || !kv_cache || !page_table || !kv_lens || !out || num_pages == 0 || max_pages == 0 ||
+      max_kv_len == 0 || (long)max_kv_len > (long)max_pages * g.page ||
+      ((uintptr_t)kv_cache & 15))
+    return MLA_ERR_INVALID_ARG;
+  if (!mha_supported(g)) return MLA_ERR_UNSUPPORTED;
+  int r = check_ws(workspace, ws_bytes, ws_mha(g, B, num_splits));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  const PlanDims pd = plan_dims(B, num_splits);
+  Carver c(workspace);
+  PlanPtrs plan;
+  carve_plan(c.take(plan_bytes(B, num_splits)), B, num_splits, &plan);
+  float* part_o = (float*)c.take(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_h);
+  float* part_ml = (float*)c.take(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
+  MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)g.d_h));
+  MLA_TRY(mha_decode(g, q, kv_cache, num_pages, page_table, max_pages, plan, pd.max_segs, sc,
+                     part_o, part_ml, out, s));
+  Geo gc = g;   // the merge of latent partials, with head width d_h
+  gc.d_c = g.d_h;
+  MLA_TRY(combine_partials(gc, plan, B, part_o, part_ml, out, s));
+  return MLA_OK;
 }
 
 int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,

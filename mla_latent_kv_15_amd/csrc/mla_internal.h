@@ -150,6 +150,16 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
                                 const float* vbuf, const int32_t* positions, int T, int kv_len,
                                 int rope_len, float* o, hipStream_t s);
 
+// MHA-equivalent decode attention over a [pages][page][2][n_h][d_h] cache
+// (k_mha.hip): d_h a multiple of 16 with d_h / 16 a power of two <= 64.
+bool mha_supported(const Geo& g);
+// One work-group per (segment, group of heads); a sequence with one segment
+// gets out directly, the others fp32 partials [segment][n_h][d_h] and
+// (m, l) [segment][n_h] for combine_partials (with d_c = d_h).
+hipError_t mha_decode(const Geo& g, const void* q, const void* cache, int num_pages,
+                      const int32_t* page_table, int max_pages, const PlanPtrs& plan, int max_segs,
+                      float scale, float* part_o, float* part_ml, void* out, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // MFMA kernels for the V2 bf16 shape
 // ---------------------------------------------------------------------------

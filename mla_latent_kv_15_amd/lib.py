@@ -30,6 +30,7 @@ OP_DECODE_QUERY = 3
 OP_DECODE_ATTENTION = 4
 OP_DECODE_OUTPUT = 5
 OP_DECODE_MERGED = 6
+OP_MHA_DECODE = 7
 
 LAYOUT_ROWS = 0
 LAYOUT_TILES = 1
@@ -82,6 +83,8 @@ _SIGS = {
     "mla_merge_weights": (c_int, [_P, _P, c_int, _P, _P, _P]),
     "mla_decode_merged": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, _P,
                                   c_int, c_int, _P, c_size_t, _P, _P]),
+    "mla_mha_decode_attention": (c_int, [_P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, c_float,
+                                         c_int, _P, c_size_t, _P, _P]),
     "mla_profile_enable": (c_int, [c_int]),
     "mla_profile_attention_ms": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
     "mla_prefill": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P, c_int, _P,
@@ -238,6 +241,17 @@ def decode_merged(cfg, mweights: MergedWeights, h, positions, kv_cache, page_tab
         kv_cache.shape[0], _ptr(page_table), page_table.shape[1], _ptr(kv_lens), h.shape[0],
         max_kv_len, _ptr(rope_table), rope_table.shape[0], num_splits, wp, wn, _ptr(out),
         _stream(stream)))
+
+
+def mha_decode_attention(cfg, q, kv_cache, page_table, kv_lens, max_kv_len, num_splits,
+                         workspace, out, scale: float = 0.0, stream=None):
+    """Baseline: decode attention over an MHA-equivalent cache
+    [pages][page][2][n_h][d_h]; q, out [B][n_h][d_h]."""
+    wp, wn = _ws(workspace)
+    _check("mla_mha_decode_attention", load().mla_mha_decode_attention(
+        ctypes.byref(cfg), _ptr(q), _ptr(kv_cache), kv_cache.shape[0], _ptr(page_table),
+        page_table.shape[1], _ptr(kv_lens), q.shape[0], max_kv_len, scale, num_splits, wp, wn,
+        _ptr(out), _stream(stream)))
 
 
 def profile_enable(on: bool):

@@ -243,6 +243,24 @@ def decode_merged(h_q, pos: int, c, k_r, Wm: Dict[str, np.ndarray], n_h: int, ba
 
 
 # ---------------------------------------------------------------------------
+# the multi-head baseline the pages weigh MLA against ([formulas] §一 and §三;
+# [walkthrough] §2): a key and a value cached per head and token
+# ---------------------------------------------------------------------------
+
+def mha_attention(q, K, V, scale: float) -> np.ndarray:
+    """One query of every head over a multi-head cache: q [n_h][d_h], K and V
+    [N][n_h][d_h]; head i: o_i = sum_j softmax_j(scale q_i . K[j, i]) V[j, i].
+    Returns [n_h][d_h]."""
+    q, K, V = (np.asarray(x, F64) for x in (q, K, V))
+    n_h = q.shape[0]
+    out = []
+    for i in range(n_h):
+        p = softmax(K[:, i] @ q[i] * scale)
+        out.append(p @ V[:, i])
+    return np.stack(out)
+
+
+# ---------------------------------------------------------------------------
 # step 5: integrate ([walkthrough] step 5)
 # ---------------------------------------------------------------------------
 

@@ -354,3 +354,30 @@ def test_merged_decode_equals_order_a(si):
     assert _rel((Mq @ cq).reshape(s.n_h, s.d_c), via) < 1e-12
     o_lat = rng.standard_normal((s.n_h, s.d_c))
     assert _rel(Mo @ o_lat.reshape(-1), oracle.latent_output(o_lat, W["W_UV"], W["W_O"])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# the multi-head baseline
+# ---------------------------------------------------------------------------
+
+def test_mha_attention_bruteforce_and_textbook():
+    """Python loops, PyTorch's attention (float64, CPU) and the uniform closed form."""
+    rng = np.random.default_rng(7)
+    n_h, d_h, N = 3, 5, 11
+    q, K, V = rng.standard_normal((n_h, d_h)), rng.standard_normal((N, n_h, d_h)), \
+        rng.standard_normal((N, n_h, d_h))
+    sc = 0.37
+    o = oracle.mha_attention(q, K, V, sc)
+    for i in range(n_h):
+        s = [sum(q[i, e] * K[j, i, e] for e in range(d_h)) * sc for j in range(N)]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = sum(w)
+        for e in range(d_h):
+            ref = sum(w[j] * V[j, i, e] for j in range(N)) / tot
+            assert abs(o[i, e] - ref) < 1e-12
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], torch.from_numpy(K).permute(1, 0, 2).contiguous(),
+        torch.from_numpy(V).permute(1, 0, 2).contiguous(), scale=sc)
+    assert _rel(o, t[:, 0, :].numpy()) < 1e-12
+    assert _rel(oracle.mha_attention(np.zeros((n_h, d_h)), K, V, sc), V.mean(axis=0)) < 1e-12
