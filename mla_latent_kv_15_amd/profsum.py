@@ -4,6 +4,7 @@ WRITE_SIZE counters, scaled by what the same counters read for a plain copy
 of known size.
 
     python -m mla_latent_kv_15_amd.profsum trace DB
+    python -m mla_latent_kv_15_amd.profsum counters --kernel attn_v2_kernel DB [DB ...]
     python -m mla_latent_kv_15_amd.profsum traffic --kernel attn_v2_kernel \\
         --fetch DB --write DB --copy-fetch DB --copy-write DB --copy-bytes N
 
@@ -77,11 +78,20 @@ def counter_mean(db: str, counter: str, kernel: str) -> tuple[float, int]:
     return sum(per.values()) / len(per), len(per)
 
 
+def counter_names(db: str) -> list:
+    cur = sqlite3.connect(db).cursor()
+    return sorted(r[0] for r in cur.execute(
+        "select distinct counter_name from counters_collection").fetchall())
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("db")
+    k = sub.add_parser("counters")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("dbs", nargs="+")
     f = sub.add_parser("traffic")
     f.add_argument("--kernel", required=True)
     f.add_argument("--fetch", required=True)
@@ -93,6 +103,13 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_table(a.db))
+        return
+    if a.cmd == "counters":
+        print(f"kernel: {a.kernel} (mean per dispatch, summed over counter instances)")
+        for db in a.dbs:
+            for c in counter_names(db):
+                v, n = counter_mean(db, c, a.kernel)
+                print(f"{c:32s} {v:18.1f}   ({n} dispatches)")
         return
     # FETCH_SIZE / WRITE_SIZE are in KiB per dispatch
     fk, nf = counter_mean(a.fetch, "FETCH_SIZE", a.kernel)
