@@ -130,3 +130,30 @@ def test_v2_decode_merged_batch():
         worst = max(worst, oracle.max_rel_error(u[b], ref))
     log(f"v2 merged decode worst rel err {worst:.3e}")
     assert worst < TOL["bf16"]
+
+
+def test_v2_decode_merged_many_rows():
+    """More than one 64-row activation block: merged and unmerged decode of
+    the same batch agree within the bf16 tolerance (each is checked against
+    the oracle elsewhere)."""
+    s = inputs.V2
+    layer = Layer(s, 34, "bf16", keep_host=False)
+    B = 70
+    L = inputs.make_lengths(B, 50, 600, 34)
+    kv = (L + 1).astype(np.int32)
+    paged = inputs.make_paged(kv, 64, 34, shuffle=True)
+    offs = np.concatenate([[0], np.cumsum(kv)[:-1]]).astype(np.int64)
+    rows = inputs.make_cache_rows(int(kv.sum()), s, 34, "bf16")
+    cache = cache_from_rows(layer, rows, paged, offs)
+    hq = device.tensor(inputs.make_hidden(B, s, 34, "bf16"))
+    rope = layer.rope(int(kv.max()) + 1)
+    _buf, wt = _pack(layer)
+    Tq, To = _merge(layer, lib.LAYOUT_TILES)
+    mw = lib.MergedWeights(wt.W_DQ, wt.W_QR, Tq.data_ptr(), To.data_ptr(), lib.LAYOUT_TILES)
+    log("v2 merged decode, B=70")
+    um = device.to_f64(_decode_merged(layer, mw, hq, L, cache, paged.page_table, kv,
+                                      int(kv.max()), rope))
+    uu = device.to_f64(layer.decode(hq, L, cache, paged.page_table, kv, int(kv.max()), rope))
+    torch.cuda.synchronize()
+    assert np.isfinite(um).all()
+    assert oracle.max_rel_error(um, uu) < TOL["bf16"]

@@ -77,10 +77,10 @@ def test_pack_matches_rearrangement(shape, dtype):
     assert off == lib.packed_weights_size(layer.cfg)
 
 
-def test_v2_decode_tiles_bit_identical():
+@pytest.mark.parametrize("B", [64, 130])
+def test_v2_decode_tiles_bit_identical(B):
     s = inputs.V2
     layer = Layer(s, 22, "bf16", keep_host=False)
-    B = 64
     L = inputs.make_lengths(B, 100, 3000, 22)
     kv = (L + 1).astype(np.int32)
     paged = inputs.make_paged(kv, 64, 22, shuffle=True)
@@ -90,7 +90,7 @@ def test_v2_decode_tiles_bit_identical():
     hq = device.tensor(inputs.make_hidden(B, s, 22, "bf16"))
     rope = layer.rope(int(kv.max()) + 1)
     _buf, wt = _pack(layer)
-    log("v2 decode rows / tiles")
+    log(f"v2 decode rows / tiles, B={B}")
     out_r = layer.decode(hq, L, cache, paged.page_table, kv, int(kv.max()), rope)
     q_r = layer.decode_query(hq, L, rope)
     lat = layer.decode_attention(q_r, cache, paged.page_table, kv, int(kv.max()))
