@@ -65,7 +65,8 @@ typedef enum {
   MLA_OP_DECODE_ATTENTION = 4,
   MLA_OP_DECODE_OUTPUT = 5,
   MLA_OP_DECODE_MERGED = 6,
-  MLA_OP_MHA_DECODE = 7
+  MLA_OP_MHA_DECODE = 7,
+  MLA_OP_ATTENTION_BACKWARD = 8
 } mla_op;
 
 /* Layer geometry.  DeepSeek-V2: d=5120, n_h=128, d_h=128, d_c=512,
@@ -259,6 +260,29 @@ int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* k
                              const int32_t* kv_lens, int B, int max_kv_len, float scale,
                              int num_splits, void* workspace, size_t ws_bytes, void* out,
                              void* stream);
+
+/* Order-A attention backward ([walkthrough] §3 顺序 A: training keeps W_UK
+ * and W_UV as two matrices, each with its own gradient).  Forward, as in
+ * mla_prefill: query t at positions[t] attends to the cached rows
+ * j <= positions[t] (j < kv_len) of one sequence, per head i
+ *   k_ij = [W_UK,i c_j | k^R_j], v_ij = W_UV,i c_j,
+ *   p_tij = softmax_j(scale q_ti . k_ij), o_ti = sum_j p_tij v_ij.
+ * Given dO = dL/do, writes dL/dW_UK and dL/dW_UV ([n_h*d_h][d_c] each, so
+ * the two up-projections get separate gradients), dL/dq ([T][n_h][d_h+d_r]:
+ * q^C then q^R per head) and dL/dC ([kv_len][d_c+d_r]: latent then RoPE key
+ * per cached row).  q: device fp32 [T][n_h][d_h+d_r] (RoPE applied, not
+ * scaled; scale = cfg->softmax_scale or 1/sqrt(d_h+d_r)); dO: device fp32
+ * [T][n_h][d_h]; positions: device int32 [T]; cache and page_table as
+ * mla_prefill; W_UK, W_UV from w in either layout; outputs device fp32.
+ * A query whose position is outside [0, kv_len) makes every gradient NaN.
+ * Workspace: mla_workspace_size(cfg, MLA_OP_ATTENTION_BACKWARD, T, kv_len, 0),
+ * which holds [n_h][T][kv_len] probabilities twice (a training-step check,
+ * not a long-context kernel).  Generic fp32 kernels. */
+int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const float* q,
+                           const int32_t* positions, const void* kv_cache, int num_pages,
+                           const int32_t* page_table, int max_pages, int kv_len, int T,
+                           const float* dO, void* workspace, size_t ws_bytes, float* dW_UK,
+                           float* dW_UV, float* dq, float* dC, void* stream);
 
 /* Kernel timing for measurement tools (not needed for computing).  While
  * enabled, every mla_decode / mla_decode_attention call records a HIP event

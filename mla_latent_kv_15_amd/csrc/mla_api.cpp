@@ -197,6 +197,29 @@ size_t ws_mha(const Geo& g, int B, int ns) {
   return al(plan_bytes(B, ns)) + al(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_h) +
          al(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
 }
+// order-A backward: rows, K, V, P, dS, dV, dK, per-head dk^R, two dc parts
+struct BwdWs {
+  float *rows, *K, *V, *P, *dS, *dV, *dK, *dkr, *lat_k, *lat_v;
+};
+void carve_bwd(Carver& c, const Geo& g, int T, int N, BwdWs* w) {
+  const size_t hd = (size_t)g.n_h * g.d_h;
+  w->rows = (float*)c.take(sizeof(float) * (size_t)N * g.row);
+  w->K = (float*)c.take(sizeof(float) * (size_t)N * hd);
+  w->V = (float*)c.take(sizeof(float) * (size_t)N * hd);
+  w->P = (float*)c.take(sizeof(float) * (size_t)g.n_h * T * N);
+  w->dS = (float*)c.take(sizeof(float) * (size_t)g.n_h * T * N);
+  w->dV = (float*)c.take(sizeof(float) * (size_t)N * hd);
+  w->dK = (float*)c.take(sizeof(float) * (size_t)N * hd);
+  w->dkr = (float*)c.take(sizeof(float) * (size_t)g.n_h * N * g.d_r);
+  w->lat_k = (float*)c.take(sizeof(float) * (size_t)N * g.d_c);
+  w->lat_v = (float*)c.take(sizeof(float) * (size_t)N * g.d_c);
+}
+size_t ws_bwd(const Geo& g, int T, int N) {
+  Carver c(nullptr);
+  BwdWs w;
+  carve_bwd(c, g, T, N, &w);
+  return c.used;
+}
 size_t ws_append(const Geo& g, int T) { return al(sizeof(float) * (size_t)T * g.row); }
 size_t ws_prefill(const Geo& g, int T, int kv_len) {
   Carver c(nullptr);
@@ -555,6 +578,7 @@ size_t mla_workspace_size(const mla_config* cfg, int op, int batch, int max_kv_l
     case MLA_OP_DECODE_OUTPUT: return ws_out(g, batch);
     case MLA_OP_DECODE_MERGED: return ws_decode_merged(g, batch, num_splits);
     case MLA_OP_MHA_DECODE: return ws_mha(g, batch, num_splits);
+    case MLA_OP_ATTENTION_BACKWARD: return ws_bwd(g, batch, max_kv_len);
     default: return 0;
   }
 }
@@ -769,6 +793,67 @@ int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* k
   Geo gc = g;   // the merge of latent partials, with head width d_h
   gc.d_c = g.d_h;
   MLA_TRY(combine_partials(gc, plan, B, part_o, part_ml, out, s));
+  return MLA_OK;
+}
+
+int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const float* q,
+                           const int32_t* positions, const void* kv_cache, int num_pages,
+                           const int32_t* page_table, int max_pages, int kv_len, int T,
+                           const float* dO, void* workspace, size_t ws_bytes, float* dW_UK,
+                           float* dW_UV, float* dq, float* dC, void* stream) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, false, false, false, true) || T < 0 || kv_len < 0 ||
+      num_pages < 0 || max_pages < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
+  if (T == 0 || kv_len == 0) return T == 0 ? MLA_OK : MLA_ERR_INVALID_ARG;
+  if (!q || !positions || !kv_cache || !page_table || !dO || !dW_UK || !dW_UV || !dq || !dC ||
+      num_pages == 0 || (long)kv_len > (long)max_pages * g.page)
+    return MLA_ERR_INVALID_ARG;
+  if (!generic_ok(g)) return MLA_ERR_UNSUPPORTED;
+  int r = check_ws(workspace, ws_bytes, ws_bwd(g, T, kv_len));
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  BwdWs b;
+  carve_bwd(c, g, T, kv_len, &b);
+  const GType Ty = st(g);
+  const bool wt = w->layout == MLA_LAYOUT_TILES;
+  const int N = kv_len, dqw = g.d_h + g.d_r;
+  const long hd = (long)g.n_h * g.d_h, TN = (long)T * N;
+  // the forward's pieces: cached rows, K^C = W_UK,i c_j and V = W_UV,i c_j
+  MLA_TRY(gather_rows_f32(g, kv_cache, num_pages, page_table, max_pages, N, b.rows, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), N, g.d_h, g.d_c, b.rows, g.row, 0,
+                       w->W_UK, g.d_c, (long)g.d_h * g.d_c, b.K, hd, g.d_h, g.n_h, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, false), N, g.d_h, g.d_c, b.rows, g.row, 0,
+                       w->W_UV, g.d_c, (long)g.d_h * g.d_c, b.V, hd, g.d_h, g.n_h, 1.f, s));
+  // softmax and its backward: P, dS [n_h][T][N]
+  MLA_TRY(attn_bwd_ps(g, N, T, g.scale, q, positions, b.K, b.V, b.rows, dO, b.P, b.dS, s));
+  // dv_ij = sum_t p_tij dO_ti;  dk^C_ij = scale sum_t ds_tij q^C_ti
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, N, g.d_h, T, b.P, N, TN, dO, hd, g.d_h, b.dV,
+                       hd, g.d_h, g.n_h, 1.f, s, true));
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, N, g.d_h, T, b.dS, N, TN, q,
+                       (long)g.n_h * dqw, dqw, b.dK, hd, g.d_h, g.n_h, g.scale, s, true));
+  // dq^C_ti = scale sum_j ds_tij k^C_ij;  dq^R_ti = scale sum_j ds_tij k^R_j
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, T, g.d_h, N, b.dS, N, TN, b.K, hd, g.d_h, dq,
+                       (long)g.n_h * dqw, dqw, g.n_h, g.scale, s));
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, T, g.d_r, N, b.dS, N, TN, b.rows + g.d_c, g.row,
+                       0, dq + g.d_h, (long)g.n_h * dqw, dqw, g.n_h, g.scale, s));
+  // dk^R per head: scale sum_t ds_tij q^R_ti, summed over heads below
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, N, g.d_r, T, b.dS, N, TN, q + g.d_h,
+                       (long)g.n_h * dqw, dqw, b.dkr, g.d_r, (long)N * g.d_r, g.n_h, g.scale, s,
+                       true));
+  // dW_UK,i = sum_j dk^C_ij c_j^T;  dW_UV,i = sum_j dv_ij c_j^T
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, g.d_h, g.d_c, N, b.dK, hd, g.d_h, b.rows, g.row,
+                       0, dW_UK, g.d_c, (long)g.d_h * g.d_c, g.n_h, 1.f, s, true));
+  MLA_TRY(gemm_generic(G_F32, G_F32, G_F32, B_KN, g.d_h, g.d_c, N, b.dV, hd, g.d_h, b.rows, g.row,
+                       0, dW_UV, g.d_c, (long)g.d_h * g.d_c, g.n_h, 1.f, s, true));
+  // dc_j = sum_i W_UK,i^T dk^C_ij + W_UV,i^T dv_ij (one product over all heads each)
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, true), N, g.d_c, (int)hd, b.dK, hd, 0,
+                       w->W_UK, g.d_c, 0, b.lat_k, g.d_c, 0, 1, 1.f, s));
+  MLA_TRY(gemm_generic(G_F32, Ty, G_F32, b_layout(wt, true), N, g.d_c, (int)hd, b.dV, hd, 0,
+                       w->W_UV, g.d_c, 0, b.lat_v, g.d_c, 0, 1, 1.f, s));
+  MLA_TRY(attn_bwd_dc(g, N, b.lat_k, b.lat_v, b.dkr, dC, s));
   return MLA_OK;
 }
 

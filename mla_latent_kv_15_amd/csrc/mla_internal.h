@@ -150,6 +150,15 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
                                 const float* vbuf, const int32_t* positions, int T, int kv_len,
                                 int rope_len, float* o, hipStream_t s);
 
+// Order-A backward pieces (k_backward.hip): P and dS [n_h][T][N] per (query,
+// head) from q [T][n_h][d_h + d_r], K, V [N][n_h][d_h], rows [N][row] and dO
+// [T][n_h][d_h]; and dC [N][row] = [lat_k + lat_v | sum_i dkr[i]].
+hipError_t attn_bwd_ps(const Geo& g, int N, int T, float scale, const float* q,
+                       const int32_t* positions, const float* K, const float* V,
+                       const float* rows, const float* dO, float* P, float* dS, hipStream_t s);
+hipError_t attn_bwd_dc(const Geo& g, int N, const float* lat_k, const float* lat_v,
+                       const float* dkr, float* dC, hipStream_t s);
+
 // MHA-equivalent decode attention over a [pages][page][2][n_h][d_h] cache
 // (k_mha.hip): d_h a multiple of 16 with d_h / 16 a power of two <= 64.
 bool mha_supported(const Geo& g);

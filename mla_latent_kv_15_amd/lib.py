@@ -31,6 +31,7 @@ OP_DECODE_ATTENTION = 4
 OP_DECODE_OUTPUT = 5
 OP_DECODE_MERGED = 6
 OP_MHA_DECODE = 7
+OP_ATTENTION_BACKWARD = 8
 
 LAYOUT_ROWS = 0
 LAYOUT_TILES = 1
@@ -85,6 +86,8 @@ _SIGS = {
                                   c_int, c_int, _P, c_size_t, _P, _P]),
     "mla_mha_decode_attention": (c_int, [_P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, c_float,
                                          c_int, _P, c_size_t, _P, _P]),
+    "mla_attention_backward": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P,
+                                       _P, c_size_t, _P, _P, _P, _P, _P]),
     "mla_profile_enable": (c_int, [c_int]),
     "mla_profile_attention_ms": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
     "mla_prefill": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P, c_int, _P,
@@ -252,6 +255,17 @@ def mha_decode_attention(cfg, q, kv_cache, page_table, kv_lens, max_kv_len, num_
         ctypes.byref(cfg), _ptr(q), _ptr(kv_cache), kv_cache.shape[0], _ptr(page_table),
         page_table.shape[1], _ptr(kv_lens), q.shape[0], max_kv_len, scale, num_splits, wp, wn,
         _ptr(out), _stream(stream)))
+
+
+def attention_backward(cfg, weights, q, positions, kv_cache, page_table_row, kv_len, dO, workspace,
+                       dW_UK, dW_UV, dq, dC, stream=None):
+    """Order-A attention backward: gradients of W_UK, W_UV, q and the cached
+    rows for one sequence (page_table_row [max_pages]); all fp32 device tensors."""
+    wp, wn = _ws(workspace)
+    _check("mla_attention_backward", load().mla_attention_backward(
+        ctypes.byref(cfg), ctypes.byref(weights), _ptr(q), _ptr(positions), _ptr(kv_cache),
+        kv_cache.shape[0], _ptr(page_table_row), page_table_row.shape[0], kv_len, q.shape[0],
+        _ptr(dO), wp, wn, _ptr(dW_UK), _ptr(dW_UV), _ptr(dq), _ptr(dC), _stream(stream)))
 
 
 def profile_enable(on: bool):

@@ -320,6 +320,51 @@ def prefill_order_a(H: np.ndarray, positions, c, k_r, W: Dict[str, np.ndarray], 
 
 
 # ---------------------------------------------------------------------------
+# order A backward ([walkthrough] §3 顺序 A: training keeps W_UK and W_UV as
+# two matrices, each with its own gradient path)
+# ---------------------------------------------------------------------------
+
+def attend_order_a_backward(q_c, q_r, positions, c, k_r, W_UK, W_UV, scale: float, dO):
+    """Gradients of causal order-A attention.  Forward, for query t at
+    position positions[t] and head i over the cached rows j <= positions[t]:
+      k_ij = [W_UK,i c_j ; k^R_j],  v_ij = W_UV,i c_j,
+      s_tij = scale [q^C_ti ; q^R_ti] . k_ij,  p_tij = softmax_j(s_tij),
+      o_ti = sum_j p_tij v_ij.
+    Given dO = dL/do [T][n_h][d_h], the chain rule through these steps gives
+      dv_ij = sum_t p_tij dO_ti,   dp_tij = dO_ti . v_ij,
+      ds_tij = p_tij (dp_tij - sum_j' p_tij' dp_tij'),
+      dk_ij = scale sum_t ds_tij [q^C_ti ; q^R_ti],
+      dq_ti = scale sum_j ds_tij k_ij,
+      dW_UK,i = sum_j dk^C_ij c_j^T,  dW_UV,i = sum_j dv_ij c_j^T,
+      dc_j = sum_i (W_UK,i^T dk^C_ij + W_UV,i^T dv_ij),  dk^R_j = sum_i dk^R_ij.
+    q_c [T][n_h][d_h], q_r [T][n_h][d_R], c [N][d_c], k_r [N][d_R].
+    Returns dict(dW_UK, dW_UV [n_h d_h][d_c], dq_c, dq_r, dc [N][d_c], dk_r [N][d_R])."""
+    q_c, q_r, c, k_r, dO = (np.asarray(x, F64) for x in (q_c, q_r, c, k_r, dO))
+    W_UK, W_UV = np.asarray(W_UK, F64), np.asarray(W_UV, F64)
+    T, n_h, d_h = q_c.shape
+    N = c.shape[0]
+    mask = np.arange(N)[None, :] <= np.asarray(positions)[:, None]
+    out = {k: np.zeros_like(v) for k, v in (("dW_UK", W_UK), ("dW_UV", W_UV), ("dq_c", q_c),
+                                            ("dq_r", q_r), ("dc", c), ("dk_r", k_r))}
+    for i in range(n_h):
+        hs = slice(i * d_h, (i + 1) * d_h)
+        K, V = c @ W_UK[hs].T, c @ W_UV[hs].T
+        S = np.where(mask, scale * (q_c[:, i] @ K.T + q_r[:, i] @ k_r.T), -np.inf)
+        P = softmax(S, axis=1)
+        dP = dO[:, i] @ V.T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dV = P.T @ dO[:, i]
+        dK = scale * dS.T @ q_c[:, i]
+        out["dq_c"][:, i] = scale * dS @ K
+        out["dq_r"][:, i] = scale * dS @ k_r
+        out["dk_r"] += scale * dS.T @ q_r[:, i]
+        out["dW_UK"][hs] = dK.T @ c
+        out["dW_UV"][hs] = dV.T @ c
+        out["dc"] += dK @ W_UK[hs] + dV @ W_UV[hs]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # brute force (tiny shapes only): explicit loops, no matrix routines and no
 # reuse of the functions above
 # ---------------------------------------------------------------------------

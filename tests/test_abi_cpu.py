@@ -187,3 +187,29 @@ def test_merged_entry_points_reject_bad_arguments(L):
               z, None) == lib.MLA_ERR_UNSUPPORTED
     assert dm(ctypes.byref(c), ctypes.byref(mw), None, None, None, 0, None, 0, None, 0, 0, None, 0,
               0, None, 0, None, None) == 0
+
+
+def test_backward_and_mha_reject_bad_arguments(L):
+    c = _cfg()
+    p = ctypes.c_void_p(4096)
+    wf = lib.Weights(*([4096] * 8))
+    bw = L.mla_attention_backward
+    args = lambda **kw: [kw.get(k, v) for k, v in (  # noqa: E731
+        ("cfg", ctypes.byref(c)), ("w", ctypes.byref(wf)), ("q", p), ("pos", p), ("cache", p),
+        ("np", 4), ("pt", p), ("mp", 2), ("kv", 100), ("T", 3), ("dO", p), ("ws", p),
+        ("wsb", 1 << 40), ("dWk", p), ("dWv", p), ("dq", p), ("dC", p), ("s", None))]
+    assert bw(*args(w=None)) == lib.MLA_ERR_INVALID_ARG
+    assert bw(*args(kv=129)) == lib.MLA_ERR_INVALID_ARG           # past the page table
+    assert bw(*args(dq=None)) == lib.MLA_ERR_INVALID_ARG
+    assert bw(*args(wsb=16)) == lib.MLA_ERR_WORKSPACE
+    assert bw(*args(T=0)) == 0
+    assert lib.workspace_size(c, lib.OP_ATTENTION_BACKWARD, 64, 64, 0) > 2 * 128 * 64 * 64 * 4
+    # MHA baseline: d_h without a power-of-two count of 16-wide pieces
+    odd = lib.make_config(inputs.Shape(d=64, n_h=4, d_h=48, d_c=32, d_cq=64, d_r=16), 64, "f32")
+    mh = L.mla_mha_decode_attention
+    assert mh(ctypes.byref(odd), p, p, 4, p, 2, p, 1, 100, ctypes.c_float(0.0), 0, p, 1 << 40, p,
+              None) == lib.MLA_ERR_UNSUPPORTED
+    assert mh(ctypes.byref(c), p, ctypes.c_void_p(4096 + 8), 4, p, 2, p, 1, 100,
+              ctypes.c_float(0.0), 0, p, 1 << 40, p, None) == lib.MLA_ERR_INVALID_ARG
+    assert mh(ctypes.byref(c), p, p, 4, p, 2, p, 1, 100, ctypes.c_float(0.0), 0, p, 16, p,
+              None) == lib.MLA_ERR_WORKSPACE

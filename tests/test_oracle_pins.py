@@ -381,3 +381,79 @@ def test_mha_attention_bruteforce_and_textbook():
         torch.from_numpy(V).permute(1, 0, 2).contiguous(), scale=sc)
     assert _rel(o, t[:, 0, :].numpy()) < 1e-12
     assert _rel(oracle.mha_attention(np.zeros((n_h, d_h)), K, V, sc), V.mean(axis=0)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# order A backward
+# ---------------------------------------------------------------------------
+
+def _order_a_torch(q_c, q_r, positions, c, k_r, W_UK, W_UV, scale):
+    """The causal order-A forward written with torch operations (float64), so
+    that autograd supplies reference gradients."""
+    T, n_h, d_h = q_c.shape
+    N = c.shape[0]
+    mask = torch.arange(N)[None, :] <= torch.as_tensor(positions)[:, None]
+    outs = []
+    for i in range(n_h):
+        K = c @ W_UK[i * d_h:(i + 1) * d_h].T
+        V = c @ W_UV[i * d_h:(i + 1) * d_h].T
+        S = scale * (q_c[:, i] @ K.T + q_r[:, i] @ k_r.T)
+        S = S.masked_fill(~mask, float("-inf"))
+        outs.append(torch.softmax(S, dim=1) @ V)
+    return torch.stack(outs, dim=1)
+
+
+@pytest.mark.parametrize("si", range(len(SMALL_SHAPES)))
+def test_order_a_backward_matches_autograd(si):
+    s = SMALL_SHAPES[si]
+    rng = np.random.default_rng(700 + si)
+    N, T = 9, 4
+    positions = np.array([N - 4, 0, N - 1, 3])
+    W = _weights64(s, 700 + si)
+    q_c, q_r = rng.standard_normal((T, s.n_h, s.d_h)), rng.standard_normal((T, s.n_h, s.d_r))
+    c, k_r = rng.standard_normal((N, s.d_c)), rng.standard_normal((N, s.d_r))
+    dO = rng.standard_normal((T, s.n_h, s.d_h))
+    sc = oracle.default_scale(s.d_h, s.d_r)
+    g = oracle.attend_order_a_backward(q_c, q_r, positions, c, k_r, W["W_UK"], W["W_UV"], sc, dO)
+    ts = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+          for k, v in (("q_c", q_c), ("q_r", q_r), ("c", c), ("k_r", k_r), ("W_UK", W["W_UK"]),
+                       ("W_UV", W["W_UV"]))}
+    o = _order_a_torch(ts["q_c"], ts["q_r"], positions, ts["c"], ts["k_r"], ts["W_UK"],
+                       ts["W_UV"], sc)
+    (o * torch.from_numpy(dO)).sum().backward()
+    for mine, theirs in (("dW_UK", "W_UK"), ("dW_UV", "W_UV"), ("dq_c", "q_c"), ("dq_r", "q_r"),
+                         ("dc", "c"), ("dk_r", "k_r")):
+        ref = ts[theirs].grad.numpy()
+        assert np.abs(g[mine] - ref).max() <= 1e-10 * (1.0 + np.abs(ref).max()), mine
+    # the forward these gradients belong to is the oracle's own order A
+    o_ref = np.stack([oracle.attend_order_a(q_c[t], q_r[t], c[:positions[t] + 1],
+                                            k_r[:positions[t] + 1], W["W_UK"], W["W_UV"], sc)
+                      for t in range(T)])
+    assert _rel(o.detach().numpy(), o_ref) < 1e-12
+
+
+def test_order_a_backward_finite_differences():
+    """Central differences of L = sum(dO * o) in a few weight entries."""
+    s = SMALL_SHAPES[1]
+    rng = np.random.default_rng(750)
+    N, T = 7, 3
+    positions = np.array([6, 2, 4])
+    W = _weights64(s, 750)
+    q_c, q_r = rng.standard_normal((T, s.n_h, s.d_h)), rng.standard_normal((T, s.n_h, s.d_r))
+    c, k_r = rng.standard_normal((N, s.d_c)), rng.standard_normal((N, s.d_r))
+    dO = rng.standard_normal((T, s.n_h, s.d_h))
+    sc = 0.3
+    g = oracle.attend_order_a_backward(q_c, q_r, positions, c, k_r, W["W_UK"], W["W_UV"], sc, dO)
+
+    def loss(W_UK, W_UV):
+        o = np.stack([oracle.attend_order_a(q_c[t], q_r[t], c[:positions[t] + 1],
+                                            k_r[:positions[t] + 1], W_UK, W_UV, sc)
+                      for t in range(T)])
+        return float((o * dO).sum())
+    eps = 1e-6
+    for name, (r, col) in (("W_UK", (1, 2)), ("W_UK", (9, 0)), ("W_UV", (4, 7)), ("W_UV", (20, 11))):
+        Wp, Wm = {k: v.copy() for k, v in W.items()}, {k: v.copy() for k, v in W.items()}
+        Wp[name][r, col] += eps
+        Wm[name][r, col] -= eps
+        fd = (loss(Wp["W_UK"], Wp["W_UV"]) - loss(Wm["W_UK"], Wm["W_UV"])) / (2 * eps)
+        assert abs(fd - g["d" + name][r, col]) < 1e-7
