@@ -214,6 +214,69 @@ def mha_baseline(args, B, lo, hi, cid):
     print(json.dumps(out), flush=True)
 
 
+def backward_measure(args, T):
+    """Order-A attention backward (mla_attention_backward) at the V2 head
+    shape: T causal queries over T cached rows of one sequence.  Prints one
+    JSON line with the algorithmic fp32 flop rate against the fp32 vector
+    peak (the kernels are generic SIMT)."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_15_amd import device, inputs, lib
+    s = inputs.V2
+    cfg = lib.make_config(s, 64, "bf16")
+    lib.load()
+    N = T
+    W = device.weights(inputs.make_weights(s, 60, "bf16"))
+    wts = lib.make_weights(W)
+    paged = inputs.make_paged([N], 64, 60, shuffle=True)
+    rows = inputs.make_cache_rows(N, s, 60, "bf16")
+    cache = device.bits_tensor(inputs.scatter_rows(rows.bits, paged, np.array([0]), fill=0))
+    q = torch.from_numpy(inputs.normal((T, s.n_h, s.d_h + s.d_r), 1.0, 60,
+                                       inputs.STREAM_QUERY)).cuda()
+    dO = torch.from_numpy(inputs.normal((T, s.n_h, s.d_h), 1.0, 60, inputs.STREAM_QUERY, 1)).cuda()
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    pt = torch.from_numpy(paged.page_table[0].astype(np.int32)).cuda()
+    ws = device.workspace(lib.workspace_size(cfg, lib.OP_ATTENTION_BACKWARD, T, N, 0))
+    f = lambda *shape: torch.empty(*shape, dtype=torch.float32, device="cuda")  # noqa: E731
+    outs = (f(s.n_h * s.d_h, s.d_c), f(s.n_h * s.d_h, s.d_c), f(T, s.n_h, s.d_h + s.d_r),
+            f(N, s.row))
+
+    def run():
+        lib.attention_backward(cfg, wts, q, pos, cache, pt, N, dO, ws, *outs)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    n = max(2, args.steps // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    h, dh, dr, dc = s.n_h, s.d_h, s.d_r, s.d_c
+    flop = 2.0 * (2 * N * h * dh * dc            # K^C, V recomputed
+                  + T * N * h * (dh + dr)        # scores
+                  + T * N * h * dh               # dp
+                  + 2 * N * T * h * dh           # dV, dK^C
+                  + T * N * h * (dh + dr)        # dq
+                  + N * T * h * dr               # dk^R
+                  + 2 * h * dh * dc * N          # dW_UK, dW_UV
+                  + 2 * N * h * dh * dc)         # dc
+    tflops = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "order-A attention backward (dW_UK, dW_UV, dq, dC)",
+        "unit": "ms", "value": ms, "higher_is_better": False, "data": "synthetic",
+        "dtype": "f32 (bf16 weights and cache)",
+        "config": {"workload": f"V2 heads (128 x 128, d_c 512, d_r 64), {T} causal queries over "
+                               f"{N} cached rows"},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": tflops / 157.3, "flop": flop},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +293,9 @@ def main():
     ap.add_argument("--baseline", choices=("mha",), default=None,
                     help="instead of the step: time decode attention over an MHA-equivalent "
                          "cache against MLA's on the same batch and exit")
+    ap.add_argument("--backward", type=int, default=0, metavar="T",
+                    help="instead of the step: time the order-A attention backward for T "
+                         "queries over T cached rows and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -259,6 +325,9 @@ def main():
     B, lo, hi, cid = WORKLOADS[args.workload]
     if args.baseline == "mha":
         mha_baseline(args, B, lo, hi, cid)
+        return
+    if args.backward:
+        backward_measure(args, args.backward)
         return
     cfg = lib.make_config(s, 64, "bf16")
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")
