@@ -52,3 +52,19 @@ def test_scratch_cap():
     with pytest.raises(RuntimeError, match="scratch"):
         build._check_scratch("k_attn_v2.hip", remarks)
     build._check_scratch("k_attn_v2.hip", remarks.replace(str(build.MAX_SCRATCH + 4), "24"))
+
+
+def test_no_scratch_kernels_reject_any_spill():
+    from mla_latent_kv_15_amd import build
+    ok = ("remark: Function Name: _ZN3mla12_GLOBAL__N_117combine_v2_kernelEv\n"
+          "remark:     ScratchSize [bytes/lane]: 0\n")
+    build._check_scratch("/x/k_attn_v2.hip", ok)
+    bad = ok.replace("ScratchSize [bytes/lane]: 0", "ScratchSize [bytes/lane]: 16")
+    with pytest.raises(RuntimeError):
+        build._check_scratch("/x/k_attn_v2.hip", bad)
+    # the attention kernel keeps its own cap
+    hot = ("remark: Function Name: _ZN3mla12_GLOBAL__N_114attn_v2_kernelEv\n"
+           "remark:     ScratchSize [bytes/lane]: 64\n")
+    build._check_scratch("/x/k_attn_v2.hip", hot)
+    with pytest.raises(RuntimeError):
+        build._check_scratch("/x/k_attn_v2.hip", hot.replace(": 64", ": 4096"))
