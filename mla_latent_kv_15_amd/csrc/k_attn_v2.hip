@@ -831,107 +831,116 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
 }
 
 // ---------------------------------------------------------------------------
-// the same merge for small batches: one wave per (sequence, head block n of
-// 32, latent run of 32 dims).  Accumulator x = 4 mb + n of the attention
-// kernel's wave wo holds, in element 4a' + c at lane (m32, hf), head 32n + m32
-// and dim 128 wo + 4 (8a' + 4 hf + c) + mb; the merge wave z = 4 wo + a takes
-// a' = a of all four mb: dims 128 wo + 32 a .. + 31, one contiguous run.
-// Sixteen times the work-groups of combine_v2_kernel, so that a few
-// sequences with many segments each still spread over the GPU.
+// the same merge for small batches: one work-group of two waves per
+// (sequence, head block n of 32, latent run of 32 dims).  Accumulator
+// x = 4 mb + n of the attention kernel's wave wo holds, in element 4a' + c at
+// lane (m32, hf), head 32n + m32 and dim 128 wo + 4 (8a' + 4 hf + c) + mb; the
+// work-group z = 4 wo + a takes a' = a of all four mb: dims 128 wo + 32 a ..
+// + 31, one contiguous run.  Sixteen times the work-groups of
+// combine_v2_kernel, so that a few sequences with many segments each still
+// spread over the GPU; within a work-group wave q sums the segments
+// s = q (mod 2), the first loads are issued before the softmax statistics are
+// formed, and the two waves' sums are added at the end.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void combine_v2_runs_kernel(PlanPtrs plan,
-                                                        const __bf16* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml,
-                                                        __bf16* __restrict__ lat_out) {
-  __shared__ float w[kCombSegs][32];
-  __shared__ float2 s_ml[kCombSegs][32];
+constexpr int kRunSegs = 264;   // (m, l) kept in LDS: every automatic plan (<= CUs + 1 segments)
+
+__global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
+                                                         const __bf16* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml,
+                                                         __bf16* __restrict__ lat_out) {
+  __shared__ float2 s_ml[kRunSegs][32];   // (m, l), then the segment weights in .x
   __shared__ float s_M[32], s_inv[32];
+  __shared__ f32x4 s_acc[4][64];          // wave 1's sums
   __shared__ __bf16 stage[32][32 + 8];
   const int b = blockIdx.x, n = blockIdx.y, wo = blockIdx.z >> 2, a = blockIdx.z & 3;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
   const int cnt = plan.seq_seg_count[b];
   const int k0 = plan.seq_seg_start[b];
   __bf16* out = lat_out + ((long)b * kHeads + n * 32) * kDc + 128 * wo + 32 * a;
-  if (cnt == 0) {
-    for (int e = lane; e < 32 * 32; e += 64)
+  if (cnt == 0 || cnt > kRunSegs) {
+    // no valid segment: NaN.  (More segments than kRunSegs come only from a
+    // forced split count beyond the work-group budget; the host sends those
+    // to combine_v2_kernel.)
+    for (int e = tid; e < 32 * 32; e += 128)
       out[(e >> 5) * kDc + (e & 31)] = (__bf16)__builtin_nanf("");
     return;
   }
-  // (m, l) of every segment of the head group: one parallel load into LDS
-  // when they fit (else read in the loops below)
-  const bool in_lds = cnt <= kCombSegs;
-  if (in_lds)
-    for (int e = lane; e < cnt * 32; e += 64)
-      s_ml[e >> 5][e & 31] =
-          *(const float2*)(part_ml + ((long)(k0 + (e >> 5)) * kHeads + n * 32 + (e & 31)) * 2);
-  __syncthreads();
-  auto ml_of = [&](int s, int hh) -> float2 {
-    if (in_lds) return s_ml[s][hh];
-    return *(const float2*)(part_ml + ((long)(k0 + s) * kHeads + n * 32 + hh) * 2);
-  };
-  // per-head max and normaliser
-  if (lane < 32) {
-    float M = -INFINITY;
-    for (int s = 0; s < cnt; ++s) M = fmaxf(M, ml_of(s, lane).x);
-    float L = 0.f;
-    for (int s = 0; s < cnt; ++s) {
-      const float2 ml = ml_of(s, lane);
-      L += ml.y * __expf(ml.x - M);
+  const int hd_l = lane & 31;
+  // this wave's segments s = q, q + 2, ...: the first kU in flight now
+  constexpr int kU = 8;
+  uint2 v[kU][4];
+  auto issue = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int su = min(s0 + 2 * u, cnt - 1);   // past the end: re-read, weight 0
+      const uint2* src =
+          (const uint2*)(part_o + (long)(k0 + su) * kHeads * kDc) + wo * 64 + lane;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) v[u][mb] = src[((4 * mb + n) * 4 + a) * kThreads];
     }
-    s_M[lane] = M;
-    s_inv[lane] = 1.f / L;
+  };
+  issue(q);
+  for (int e = tid; e < cnt * 32; e += 128)
+    s_ml[e >> 5][e & 31] =
+        *(const float2*)(part_ml + ((long)(k0 + (e >> 5)) * kHeads + n * 32 + (e & 31)) * 2);
+  __syncthreads();
+  // per-head max and normaliser: lane pair (hd, hd + 32) of wave 0 splits the
+  // segments by parity
+  if (q == 0) {
+    const int h2 = lane >> 5;
+    float M = -INFINITY;
+    for (int s = h2; s < cnt; s += 2) M = fmaxf(M, s_ml[s][hd_l].x);
+    M = fmaxf(M, __shfl_xor(M, 32));
+    float L = 0.f;
+    for (int s = h2; s < cnt; s += 2) L += s_ml[s][hd_l].y * __expf(s_ml[s][hd_l].x - M);
+    L += __shfl_xor(L, 32);
+    if (h2 == 0) {
+      s_M[hd_l] = M;
+      s_inv[hd_l] = 1.f / L;
+    }
   }
   __syncthreads();
-  const int hd_l = lane & 31;
+  for (int e = tid; e < cnt * 32; e += 128) {
+    const int s = e >> 5, hh = e & 31;
+    s_ml[s][hh].x = __expf(s_ml[s][hh].x - s_M[hh]) * s_inv[hh];
+  }
+  __syncthreads();
   f32x4 acc[4];   // [mb]
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = f32x4{};
-  for (int c0 = 0; c0 < cnt; c0 += kCombSegs) {
-    const int nc = min(kCombSegs, cnt - c0);
-    __syncthreads();
-    for (int e = lane; e < nc * 32; e += 64) {
-      const int s = e >> 5, hh = e & 31;
-      w[s][hh] = __expf(ml_of(c0 + s, hh).x - s_M[hh]) * s_inv[hh];
-    }
-    __syncthreads();
-    // sixteen segments' loads in flight at once; the sum still runs over the
-    // segments in order
-    constexpr int kU = 16;
-    for (int s0 = 0; s0 < nc; s0 += kU) {
-      uint2 v[kU][4];
-      // (a segment past the end re-reads the last one and gets weight 0;
-      // predicated rather than a loop exit, so the loads stay in registers)
+  for (int s0 = q; s0 < cnt; s0 += 2 * kU) {
+    if (s0 != q) issue(s0);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int su = min(s0 + u, nc - 1);
-        const uint2* src =
-            (const uint2*)(part_o + (long)(k0 + c0 + su) * kHeads * kDc) + wo * 64 + lane;
+    for (int u = 0; u < kU; ++u) {
+      const int su = s0 + 2 * u;
+      if (su >= cnt) continue;
+      const float ws = s_ml[su][hd_l].x;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) v[u][mb] = src[((4 * mb + n) * 4 + a) * kThreads];
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (s0 + u >= nc) continue;
-        const float ws = w[s0 + u][hd_l];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[mb] += ws * f32x4{__uint_as_float(v[u][mb].x << 16),
-                                __uint_as_float(v[u][mb].x & 0xffff0000u),
-                                __uint_as_float(v[u][mb].y << 16),
-                                __uint_as_float(v[u][mb].y & 0xffff0000u)};
-      }
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb] += ws * f32x4{__uint_as_float(v[u][mb].x << 16),
+                              __uint_as_float(v[u][mb].x & 0xffff0000u),
+                              __uint_as_float(v[u][mb].y << 16),
+                              __uint_as_float(v[u][mb].y & 0xffff0000u)};
     }
   }
-  // element c of acc[mb] at lane (m32, hf): head 32n + m32, dim
-  // 32 a + 16 hf + 4 c + mb of this work-group's run
-  const int hf = lane >> 5;
+  if (q == 1)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) stage[hd_l][16 * hf + 4 * c + mb] = (__bf16)acc[mb][c];
+    for (int mb = 0; mb < 4; ++mb) s_acc[mb][lane] = acc[mb];
   __syncthreads();
-  for (int e = lane; e < 32 * 4; e += 64) {
-    const int hh = e >> 2, c8 = e & 3;
+  if (q == 0) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] += s_acc[mb][lane];
+    // element c of acc[mb] at lane (m32, hf): head 32n + m32, dim
+    // 32 a + 16 hf + 4 c + mb of this work-group's run
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) stage[hd_l][16 * hf + 4 * c + mb] = (__bf16)acc[mb][c];
+  }
+  __syncthreads();
+  {
+    const int hh = tid >> 2, c8 = tid & 3;
     *(uint4*)(out + (long)hh * kDc + 8 * c8) = *(const uint4*)(&stage[hh][8 * c8]);
   }
 }
@@ -949,17 +958,20 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, in
   return hipGetLastError();
 }
 
-hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,
+hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   // 4 B work-groups of 256 threads fill the GPU for batches from 32 up; below
-  // that, 64 B single-wave work-groups
-  if (B >= 32)
+  // that, 64 B two-wave work-groups, as long as a sequence's segments fit
+  // their LDS table (an automatic plan makes at most work-groups + 1; a forced
+  // one, num_splits)
+  const int max_per_seq = num_splits > 0 ? num_splits : plan_dims(B, 0).max_wg + 1;
+  if (B >= 32 || max_per_seq > kRunSegs)
     hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan,
                        (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   else
-    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves), dim3(64), 0, s,
-                       plan, (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
+    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves), dim3(128), 0,
+                       s, plan, (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   return hipGetLastError();
 }
 

@@ -364,7 +364,7 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
     MLA_TRY(attn_decode_v2(g, q_abs, cache, num_pages, page_table, max_pages, plan, a.max_wg,
                            a.part_o, a.part_ml, s));
     MLA_TRY(g_prof.mark(1, s));
-    MLA_TRY(combine_decode_v2(plan, B, a.part_o, a.part_ml, lat, s));
+    MLA_TRY(combine_decode_v2(plan, B, num_splits, a.part_o, a.part_ml, lat, s));
   } else {
     MLA_TRY(attn_decode_generic(g, q_abs, cache, num_pages, page_table, max_pages, plan,
                                 a.max_segs, a.part_o, a.part_ml, lat, s));

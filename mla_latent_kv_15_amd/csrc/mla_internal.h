@@ -217,7 +217,7 @@ hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void
                      float scale, const float* q_r, const int32_t* positions, const float* rope,
                      int rope_len, hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
-hipError_t combine_decode_v2(const PlanPtrs& plan, int B, const void* part_o,
+hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);
 
 }  // namespace mla
