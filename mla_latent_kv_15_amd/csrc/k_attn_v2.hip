@@ -119,6 +119,17 @@ __device__ inline int xor_here(int x) {
   }
 }
 
+// This lane's index, formed at the point of use.  A lane-derived value kept
+// from the kernel's start is live across the sub-tile loop, where the
+// register budget spills it, and the spill's reload in a segment's epilogue
+// waits for every vector memory operation in flight (vmcnt(0)): the next
+// segment's query, its first sub-tiles and the partial stores.
+__device__ inline int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // f(integral_constant<int, I>) for I in [I0, N): unrolled with compile-time indices
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -323,11 +334,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
 
   bf16x8 qreg[kKSteps];    // absorbed query, B operand (lane = head, 8 dims per K-step half)
   auto load_q = [&](int b) {
-    const int hd = wave * 32 + (lane & 31), hh = lane >> 5;   // head, lane half
-    const bf16x8* qs = (const bf16x8*)(q_abs + ((long)b * kHeads + hd) * kRow + 8 * hh);
+    // The query arrives in the query-tile layout (qtile_index): each load
+    // reads 1 KB contiguously (in rows, 16 B from each of 64 rows 1152 B
+    // apart, the loads took several microseconds per segment).  A buffer
+    // resource on sequence b's tiles and a 32-bit per-lane offset formed
+    // here: a 64-bit per-lane address would be kept live across the sub-tile
+    // loop, spilled, and its reload would wait for every memory operation in
+    // flight.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int off = (wave * kKSteps * 64 + ln) * 16;
+    constexpr int step = 1024;   // bytes from one K-step to the next
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q_abs + (long)b * kHeads * kRow), 0, kHeads * kRowBytes, kRsrcWord3);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qs[2 * ks];
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, ks * step, 0));
   };
+
+
   // the query must have landed before the sub-tile loop: a query load left in
   // flight would make the compiler wait inside the loop behind ring loads
   auto consume_q = [&]() {
@@ -450,7 +475,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       {
         // P buffer 1 reads as the P of sub-tile -1 in iteration 0: zero it
         const u32x4 z = {};
-        int tl = wave * 64 + lane;   // (threadIdx.x is not kept live)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // the address is formed here, not kept across the loop
+        const int tl = wave * 64 + ln;
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * tl, z);
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * (tl + kThreads), z);
       }
@@ -680,8 +707,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     // order (8-byte piece 4x + a of a lane holds elements 4a .. 4a + 3 of
     // accumulator x); merged later
     {
-      const int tl = wave * 64 + lane;   // (threadIdx.x is not kept live)
-      uint2* dst = (uint2*)(part_o + (long)k * kHeads * kDc) + tl;
+      const int ln = lane_here();
+      uint2* dst = (uint2*)(part_o + (long)k * kHeads * kDc) + (wave * 64 + ln);
 #pragma unroll
       for (int x = 0; x < 16; ++x)
 #pragma unroll
@@ -696,13 +723,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           // VGPRs, and reading all accumulators ahead would not fit beside it
           if (a == 3) __builtin_amdgcn_sched_barrier(0);
         }
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      // l over all 32 tokens of a sub-tile: lanes (m32, 0) and (m32, 1) hold
+      // halves of head m32's sum
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                       __float_as_uint(l_run), false, false);
+      const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const bool bad = (badm >> (k & 31)) & 1u;
       badm &= ~(1u << (k & 31));
-      if (h == 0) {
-        int hd = head;
-        asm volatile("" : "+v"(hd));
-        float2* ml = (float2*)(part_ml + ((long)k * kHeads + hd) * 2);
+      if (ln < 32) {
+        float2* ml = (float2*)(part_ml + ((long)k * kHeads + wave * 32 + ln) * 2);
         *ml = float2{m_ref * kLn2, bad ? __builtin_nanf("") : l_tot};
       }
     }
@@ -722,6 +751,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     cursor_after_prefetch();   // from pid_next: the window of segment k
     pid_next = pid_n2;
   }
+}
+
+// Rows [B][128][576] -> query tiles (qtile_index): one 16-byte piece (eight
+// consecutive numbers of one row, which stay consecutive) per thread.
+__global__ __launch_bounds__(256) void qtile_pack_kernel(const uint4* __restrict__ rows, long n,
+                                                         uint4* __restrict__ tiles) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= n) return;
+  const long r = p / (kRow / 8);                  // row = m * 128 + head
+  const int d = 8 * (int)(p - r * (kRow / 8));
+  tiles[qtile_index(r / kHeads, (int)(r % kHeads), d) / 8] = rows[p];
 }
 
 // ---------------------------------------------------------------------------
@@ -947,14 +987,22 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
 
 }  // namespace
 
-hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
                           int n_wg_launch, void* part_o, float* part_ml, hipStream_t s) {
   if (n_wg_launch <= 0) return hipSuccess;
   hipLaunchKernelGGL(attn_v2_kernel, dim3(n_wg_launch), dim3(kThreads), 0, s,
-                     (const __bf16*)q_abs, (const __bf16*)cache, num_pages, page_table, max_pages,
-                     g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
+                     (const __bf16*)q_tiles, (const __bf16*)cache, num_pages, page_table,
+                     max_pages, g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
                      (const Seg*)plan.segs, (__bf16*)part_o, part_ml);
+  return hipGetLastError();
+}
+
+hipError_t pack_query_tiles(const void* rows, int B, void* tiles, hipStream_t s) {
+  const long n = (long)B * kHeads * (kRow / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(qtile_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint4*)rows, n, (uint4*)tiles);
   return hipGetLastError();
 }
 

@@ -260,10 +260,23 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <bool WT>
 __global__ __launch_bounds__(256, 1) void absorb_kernel(
     int M, const __bf16* __restrict__ qc, const __bf16* __restrict__ W_UK,
-    __bf16* __restrict__ q_abs, float scale, const float* __restrict__ q_r,
+    __bf16* __restrict__ q_abs, int q_tiled, float scale, const float* __restrict__ q_r,
     const int32_t* __restrict__ positions, const float* __restrict__ rope, int rope_len) {
-  const int head = blockIdx.x >> 1, ch = blockIdx.x & 1;
+  // Work-groups are dispatched round-robin over the eight XCDs.  In the
+  // query-tile layout the eight heads 8k .. 8k + 7 share every 128-byte line
+  // (16 bytes each), so all sixteen work-groups of such a group (eight heads,
+  // two column halves) go to one XCD: its L2 then holds whole lines, and no
+  // line reaches memory partly written from several L2s.
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int pair = 4 * xcd + (k >> 3);           // (head group, column half)
+  const int head = 8 * (pair >> 1) + (k & 7), ch = pair & 1;
   const int m0 = blockIdx.y * kMT;
+  // element (m, head, d) of the output; four (two) consecutive d from a
+  // multiple of four (two) stay consecutive in both layouts
+  auto qidx = [&](long m, int d) -> long {
+    return q_tiled ? qtile_index(m, head, d) : (m * 128 + head) * 576 + d;
+  };
+
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int nmb = min(4, (M - m0 + 15) >> 4);
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = (__bf16)(scale * acc[mb][j][i]);
-      *(bf16x4*)(q_abs + ((long)m * 128 + head) * 576 + c0) = o;
+      *(bf16x4*)(q_abs + qidx(m, c0)) = o;
     }
   }
   // RoPE part (its loads were issued first)
@@ -350,8 +363,7 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
     const float o0 = (x[it].x * cs[it].x - x[it].y * cs[it].y) * scale;
     const float o1 = (x[it].x * cs[it].y + x[it].y * cs[it].x) * scale;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    *(bf16x2*)(q_abs + ((long)mm[it] * 128 + head) * 576 + 512 + 2 * k) =
-        bf16x2{(__bf16)o0, (__bf16)o1};
+    *(bf16x2*)(q_abs + qidx(mm[it], 512 + 2 * k)) = bf16x2{(__bf16)o0, (__bf16)o1};
   }
 }
 
@@ -505,18 +517,18 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
 }
 
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
-                     float scale, const float* q_r, const int32_t* positions, const float* rope,
-                     int rope_len, hipStream_t s) {
+                     bool q_tiled, float scale, const float* q_r, const int32_t* positions,
+                     const float* rope, int rope_len, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(2 * 128, (M + kMT - 1) / kMT);
   if (w_tiled)
     hipLaunchKernelGGL(absorb_kernel<true>, grid, dim3(256), 0, s, M, (const __bf16*)qc,
-                       (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions, rope,
-                       rope_len);
+                       (const __bf16*)W_UK, (__bf16*)q_abs, (int)q_tiled, scale, q_r,
+                       positions, rope, rope_len);
   else
     hipLaunchKernelGGL(absorb_kernel<false>, grid, dim3(256), 0, s, M, (const __bf16*)qc,
-                       (const __bf16*)W_UK, (__bf16*)q_abs, scale, q_r, positions, rope,
-                       rope_len);
+                       (const __bf16*)W_UK, (__bf16*)q_abs, (int)q_tiled, scale, q_r,
+                       positions, rope, rope_len);
   return hipGetLastError();
 }
 

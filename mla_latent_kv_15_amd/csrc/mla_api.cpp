@@ -105,13 +105,15 @@ void carve_query(Carver& c, const Geo& g, int B, QueryWs* w) {
 struct AttnWs {
   void* plan;
   float *part_o, *part_ml;
+  void* q_tiles;   // MFMA path, query given in rows: its query-tile copy
   int max_segs, max_wg;
 };
-void carve_attn(Carver& c, const Geo& g, int B, int num_splits, AttnWs* w) {
+void carve_attn(Carver& c, const Geo& g, int B, int num_splits, AttnWs* w, bool q_rows = true) {
   PlanDims pd = plan_dims(B, num_splits);
   w->max_segs = pd.max_segs;
   w->max_wg = pd.max_wg;
   w->plan = c.take(plan_bytes(B, num_splits));
+  w->q_tiles = (q_rows && is_v2_fast(g)) ? c.take((size_t)B * g.n_h * g.row * g.esize()) : nullptr;
   w->part_o = (float*)c.take(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_c);
   w->part_ml = (float*)c.take(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
 }
@@ -157,10 +159,10 @@ size_t ws_query(const Geo& g, int B) {
   carve_query(c, g, B, &w);
   return c.used;
 }
-size_t ws_attn(const Geo& g, int B, int ns) {
+size_t ws_attn(const Geo& g, int B, int ns, bool q_rows = true) {
   Carver c(nullptr);
   AttnWs w;
-  carve_attn(c, g, B, ns, &w);
+  carve_attn(c, g, B, ns, &w, q_rows);
   return c.used;
 }
 size_t ws_out(const Geo& g, int B) {
@@ -174,7 +176,7 @@ size_t ws_decode_head(const Geo& g, int B) {
 }
 size_t ws_decode(const Geo& g, int B, int ns) {
   size_t sub = ws_query(g, B);
-  size_t a = ws_attn(g, B, ns), o = ws_out(g, B);
+  size_t a = ws_attn(g, B, ns, false), o = ws_out(g, B);
   if (a > sub) sub = a;
   if (o > sub) sub = o;
   // the plan has a region of its own: it is built during the query
@@ -277,7 +279,7 @@ int run_cq(const Geo& g, const void* W_DQ, bool wt, const void* h, int B, const 
 
 int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* positions, int B,
               const float* rope, int rope_len, void* ws, void* q_abs, hipStream_t s,
-              const PlanJob* job = nullptr) {
+              const PlanJob* job = nullptr, bool q_tiled = false) {
   Carver c(ws);
   QueryWs q;
   carve_query(c, g, B, &q);
@@ -299,8 +301,8 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
     }
     // absorbed query q~_i = W_UK,i^T q^C_i and RoPE(q^R_i), scaled and packed
     // (order B)
-    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, wt, q_abs, g.scale, q.qr, positions, rope, rope_len,
-                      s));
+    MLA_TRY(absorb_v2(B, q.qc16, w->W_UK, wt, q_abs, q_tiled, g.scale, q.qr, positions, rope,
+                      rope_len, s));
     return MLA_OK;
   }
   const GType T = st(g);
@@ -346,10 +348,10 @@ Profiler g_prof;
 int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pages,
                   const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
                   int max_kv_len, int num_splits, void* ws, void* lat, hipStream_t s,
-                  const PlanPtrs* pre = nullptr) {
+                  const PlanPtrs* pre = nullptr, bool q_tiled = false) {
   Carver c(ws);
   AttnWs a;
-  carve_attn(c, g, B, num_splits, &a);
+  carve_attn(c, g, B, num_splits, &a, !q_tiled);
   PlanPtrs plan;
   const bool fast = is_v2_fast(g);
   if (pre) {
@@ -361,7 +363,13 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
   MLA_TRY(g_prof.mark(0, s));
   if (fast) {
     // the MFMA kernel writes every segment as a partial; its merge follows
-    MLA_TRY(attn_decode_v2(g, q_abs, cache, num_pages, page_table, max_pages, plan, a.max_wg,
+    // the MFMA kernel loads the query in the query-tile layout
+    const void* qt = q_abs;
+    if (!q_tiled) {
+      MLA_TRY(pack_query_tiles(q_abs, B, a.q_tiles, s));
+      qt = a.q_tiles;
+    }
+    MLA_TRY(attn_decode_v2(g, qt, cache, num_pages, page_table, max_pages, plan, a.max_wg,
                            a.part_o, a.part_ml, s));
     MLA_TRY(g_prof.mark(1, s));
     MLA_TRY(combine_decode_v2(plan, B, num_splits, a.part_o, a.part_ml, lat, s));
@@ -695,10 +703,12 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
   carve_plan(c.take(plan_bytes(B, num_splits)), B, num_splits, &plan);
   const PlanJob job = plan_job(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits);
   void* sub = c.base + c.used;
-  r = run_query(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s, &job);
+  // the absorbed query stays inside the step: on the V2 fast path it is
+  // written in the query-tile layout the attention kernel loads contiguously
+  r = run_query(g, w, h, positions, B, rope_table, rope_len, sub, q_abs, s, &job, true);
   if (r) return r;
   r = run_attention(g, q_abs, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
-                    num_splits, sub, lat, s, &plan);
+                    num_splits, sub, lat, s, &plan, true);
   if (r) return r;
   return run_output(g, w, lat, B, sub, out, s);
 }

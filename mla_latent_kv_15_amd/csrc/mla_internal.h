@@ -88,6 +88,17 @@ __device__ inline long blk_index(int m, int k, int K) {
 __host__ __device__ inline long tile_index(long r, long c, long C) {
   return (((r >> 4) * (C >> 5) + (c >> 5)) * 64 + (((c >> 3) & 3) << 4) + (r & 15)) * 8 + (c & 7);
 }
+// Query tiles: the absorbed query of the V2 fast path (128 heads of 576
+// numbers per sequence) in the register order of the attention kernel's B
+// operand, so that each of its query loads reads 1 KB contiguously instead of
+// 16 B from each of 64 rows 1152 B apart.  Element (m, head, d) sits at
+// [m][head / 32][d / 16][lane][d % 8] with lane = head % 32 + 32 ((d / 8) % 2):
+// the 64 lanes of one wave's K-step of 16 numbers, 8 bf16 each.  A sequence's
+// tiles occupy the same 147,456 bytes as its rows.
+__host__ __device__ inline long qtile_index(long m, int head, int d) {
+  return (((m * 4 + (head >> 5)) * 36 + (d >> 4)) * 64 + (head & 31) + 32 * ((d >> 3) & 1)) * 8 +
+         (d & 7);
+}
 // The geometry admits the tiled layout for all eight matrices and their
 // per-head slices (16-row aligned).
 inline bool tiles_ok(const Geo& g) {
@@ -172,9 +183,12 @@ hipError_t mha_decode(const Geo& g, const void* q, const void* cache, int num_pa
 // ---------------------------------------------------------------------------
 // MFMA kernels for the V2 bf16 shape
 // ---------------------------------------------------------------------------
-hipError_t attn_decode_v2(const Geo& g, const void* q_abs, const void* cache, int num_pages,
+// q_tiles: the absorbed query in the query-tile layout (qtile_index).
+hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, const void* cache, int num_pages,
                           const int32_t* page_table, int max_pages, const PlanPtrs& plan,
                           int n_wg_launch, void* part_o, float* part_ml, hipStream_t s);
+// Rows [B][128][576] (bf16) rearranged into the query-tile layout.
+hipError_t pack_query_tiles(const void* rows, int B, void* tiles, hipStream_t s);
 // (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
 //  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
 // Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, row-major
@@ -211,11 +225,12 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
                  int y_grp = 0, long y_grp_stride = 0);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
-// q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i (V2 geometry, bf16; W_UK
-// row-major or tiled).
+// q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i and q_abs[b][i][512:576] =
+// scale * RoPE(q^R_i) (V2 geometry, bf16; W_UK row-major or tiled); q_tiled:
+// written in the query-tile layout (qtile_index) instead of rows.
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
-                     float scale, const float* q_r, const int32_t* positions, const float* rope,
-                     int rope_len, hipStream_t s);
+                     bool q_tiled, float scale, const float* q_r, const int32_t* positions,
+                     const float* rope, int rope_len, hipStream_t s);
 // Merge of the register-order partials attn_decode_v2 writes.
 hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);
