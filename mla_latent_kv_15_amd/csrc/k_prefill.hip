@@ -1,0 +1,196 @@
+// Causal prefill attention in order A for the DeepSeek-V2 head shape
+// (n_h = 128, scores over 192 numbers, values of 128), on gfx950 MFMA.
+//
+// What it computes ([walkthrough] §3, order A, the form training uses, with
+// the keys and values decompressed per head): for query t at position p_t
+// and head i,
+//   o_ti = sum_{j <= p_t} softmax_j(q_ti . k_ij) v_ij,   j < kv_len,
+// q_ti = [q^C_ti | RoPE(q^R_ti)] with the softmax scale folded in,
+// k_ij = [W_UK,i c_j | k^R_j], v_ij = W_UV,i c_j.  A query whose position
+// lies outside [0, kv_len) gets NaN.
+//
+// Design: one wave per (block of 32 queries, head).  The scores are formed
+// transposed, S^T[key][query] = K . Q^T, with v_mfma_f32_32x32x16_bf16, so
+// that every lane owns one query: its softmax statistics stay in the lane
+// apart from one permlane32 swap with the lane 32 apart, which holds the
+// other half of the block's keys.  Four more swaps turn the numerators into
+// the B operand of O^T[dim][query] += V^T . P^T, without LDS.  K, V and Q
+// arrive as fp32 and are rounded to bf16 in registers; accumulation is fp32
+// with an online softmax in the log2 domain.  Key blocks past the block's
+// furthest query position are skipped (causality).  o is written as bf16
+// rows [T][n_h * d_h], the input of the W_O product.
+#include <math.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kH = 128;    // heads
+constexpr int kW = 192;    // query and key width
+constexpr int kDv = 128;   // value width
+constexpr int kQB = 32;    // queries per wave
+constexpr int kKB = 32;    // keys per block
+constexpr int kKSteps = kW / 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline bf16x8 to_bf16x8(const float4 a, const float4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a.x;
+  r[1] = (__bf16)a.y;
+  r[2] = (__bf16)a.z;
+  r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x;
+  r[5] = (__bf16)b.y;
+  r[6] = (__bf16)b.z;
+  r[7] = (__bf16)b.w;
+  return r;
+}
+
+__device__ inline uint32_t pack2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
+}
+
+// MFMA operand layouts (32 x 32 x 16): lane l = (c, h), c = l & 31,
+// h = l >> 5.  A[m][k]: lane holds row m = c, k = 8h .. 8h + 7.  B[k][n]:
+// lane holds column n = c, k = 8h .. 8h + 7.  D[m][n]: lane holds column
+// n = c, rows 8 (r >> 2) + 4h + (r & 3) for r = 0 .. 15.
+__global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
+    const float* __restrict__ q, const float* __restrict__ kbuf, const float* __restrict__ vbuf,
+    const int32_t* __restrict__ positions, int T, int kv_len, __bf16* __restrict__ o) {
+  const int qb = blockIdx.x, i = blockIdx.y;
+  const int lane = threadIdx.x, c = lane & 31, h = lane >> 5;
+  const int t = qb * kQB + c;
+  const bool t_ok = t < T;
+  const int pos = t_ok ? positions[t] : -1;
+  const bool valid = pos >= 0 && pos < kv_len;
+  const int last = valid ? pos : -1;   // this query sees keys 0 .. last
+  int far = last;
+  for (int off = 32; off >= 1; off >>= 1) far = max(far, __shfl_xor(far, off));
+  const int nkb = (far + kKB) / kKB;   // key blocks the wave visits (0: no valid query)
+
+  // Q^T as the B operand: K-step ks holds dims 16 ks + 8h .. + 7 of query t
+  bf16x8 qv[kKSteps];
+  {
+    const float* qr = q + ((long)(t_ok ? t : 0) * kH + i) * kW + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qv[ks] = to_bf16x8(*(const float4*)(qr + 16 * ks), *(const float4*)(qr + 16 * ks + 4));
+  }
+  f32x16 acc[kDv / 32];   // O^T, dims 32 d .. 32 d + 31 x the 32 queries
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d) acc[d] = f32x16{};
+  float m = -INFINITY, l = 0.f;   // running max (log2 units) and sum of this lane's query
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int j0 = kb * kKB;
+    // S^T = K . Q^T: the A operand is key row j0 + c (rows past kv_len
+    // repeat the last one; they are masked below)
+    const float* kr = kbuf + ((long)min(j0 + c, kv_len - 1) * kH + i) * kW + 8 * h;
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8 a =
+          to_bf16x8(*(const float4*)(kr + 16 * ks), *(const float4*)(kr + 16 * ks + 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[ks], s, 0, 0, 0);
+    }
+    // causal mask and the block's max for this query (both lane halves)
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      s[r] = key <= last ? s[r] * kLog2e : -INFINITY;
+      bm = fmaxf(bm, s[r]);
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                       false, false);
+      bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mn = fmaxf(m, bm);
+    const float ref = mn == -INFINITY ? 0.f : mn;   // no key seen yet: all numerators 0
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
+      ps += s[r];
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
+                                                       false, false);
+      ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
+    // P^T as the B operand: K-step kap needs keys 16 kap + 8h .. + 7 of this
+    // lane's query.  A lane holds keys 4h .. 4h + 3 (+ 8, 16, 24); the lane
+    // 32 apart holds the other four of each eight.
+    uint32_t R[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) R[k] = pack2(s[2 * k], s[2 * k + 1]);
+#pragma unroll
+    for (int k = 0; k < 8; k += 4) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(R[k], R[k + 2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(R[k + 1], R[k + 3], false, false);
+      R[k] = s0[0];
+      R[k + 2] = s0[1];
+      R[k + 1] = s1[0];
+      R[k + 3] = s1[1];
+    }
+    const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{R[0], R[1], R[2], R[3]}),
+                          __builtin_bit_cast(bf16x8, u32x4{R[4], R[5], R[6], R[7]})};
+    // O^T += V^T . P^T: the A operand of dim tile d, K-step kap is dim
+    // 32 d + c of keys j0 + 16 kap + 8h .. + 7
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+      const float* vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vr[e] = vbuf + ((long)min(j0 + 16 * kap + 8 * h + e, kv_len - 1) * kH + i) * kDv + c;
+#pragma unroll
+      for (int d = 0; d < kDv / 32; ++d) {
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)vr[e][32 * d];
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kap], acc[d], 0, 0, 0);
+      }
+    }
+  }
+  if (!t_ok) return;
+  // lane (c, h) holds dims 32 d + 8 g + 4h .. + 3 (g = r >> 2) of query t
+  const float inv = valid ? 1.f / l : __builtin_nanf("");
+  __bf16* dst = o + ((long)t * kH + i) * kDv + 4 * h;
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(uint2*)(dst + 32 * d + 8 * g) =
+          uint2{pack2(acc[d][4 * g] * inv, acc[d][4 * g + 1] * inv),
+                pack2(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv)};
+}
+
+}  // namespace
+
+bool prefill_v2_supported(const Geo& g) {
+  return is_v2_fast(g) && g.d_h + g.d_r == kW && g.d_h == kDv && g.n_h == kH;
+}
+
+hipError_t attn_prefill_v2(const Geo& g, const float* q, const float* kbuf, const float* vbuf,
+                           const int32_t* positions, int T, int kv_len, void* o, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!prefill_v2_supported(g) || kv_len <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_prefill_v2_kernel, dim3((T + kQB - 1) / kQB, kH), dim3(64), 0, s, q,
+                     kbuf, vbuf, positions, T, kv_len, (__bf16*)o);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -914,6 +914,14 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                        0, w->W_UV, g.d_c, (long)g.d_h * g.d_c, p.vbuf,
                        (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f, s));
   // causal softmax attention with 192-d scores and 128-d values, then W_O
+  if (prefill_v2_supported(g)) {
+    // bf16 MFMA attention, o as bf16 rows; u = W_O o on the weight-streaming
+    // MFMA GEMM (one 64-row activation block per grid row, no K split)
+    MLA_TRY(attn_prefill_v2(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, p.o, s));
+    MLA_TRY(wgemm(GemmTile{5, 1}, T, g.d, g.n_h * g.d_h, p.o, (long)g.n_h * g.d_h, 0, 0, w->W_O,
+                  out, g.d, 0, false, 1.f, s, false, false, wt));
+    return MLA_OK;
+  }
   MLA_TRY(attn_prefill_generic(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, rope_len, p.o, s));
   MLA_TRY(gemm_generic(G_F32, Ty, Ty, b_layout(wt, false), T, g.d, g.n_h * g.d_h, p.o,
                        (long)g.n_h * g.d_h, 0, w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1,

@@ -160,6 +160,11 @@ hipError_t rope_inplace_heads(const Geo& g, float* q, int T, long ld_row, int of
 hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
                                 const float* vbuf, const int32_t* positions, int T, int kv_len,
                                 int rope_len, float* o, hipStream_t s);
+// The same causal attention on bf16 MFMA for the DeepSeek-V2 head shape (q,
+// k, v and p rounded to bf16, fp32 accumulation); o is bf16 [T][n_h * d_h].
+bool prefill_v2_supported(const Geo& g);
+hipError_t attn_prefill_v2(const Geo& g, const float* q, const float* kbuf, const float* vbuf,
+                           const int32_t* positions, int T, int kv_len, void* o, hipStream_t s);
 
 // Order-A backward pieces (k_backward.hip): P and dS [n_h][T][N] per (query,
 // head) from q [T][n_h][d_h + d_r], K, V [N][n_h][d_h], rows [N][row] and dO
