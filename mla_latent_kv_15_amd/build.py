@@ -41,7 +41,7 @@ MAX_SCRATCH = 256   # bytes per lane
 # ran 2x slower that way).
 NO_SCRATCH = {"k_attn_v2.hip": ("combine_v2", "qtile_pack"), "k_gemm_v2.hip": ("wgemm", "absorb"),
               "k_mha.hip": ("mha_decode",),
-              "k_prefill.hip": ("attn_prefill_v2",)}
+              "k_prefill.hip": ("attn_prefill_v2", "prefill_rows_v2", "prefill_rope_q_v2")}
 _SPILL_OPS = ("scratch_", "buffer_store", "buffer_load", "v_accvgpr_read", "v_accvgpr_write",
               "v_accvgpr_mov")
 

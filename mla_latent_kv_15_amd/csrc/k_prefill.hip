@@ -14,9 +14,9 @@
 // that every lane owns one query: its softmax statistics stay in the lane
 // apart from one permlane32 swap with the lane 32 apart, which holds the
 // other half of the block's keys.  Four more swaps turn the numerators into
-// the B operand of O^T[dim][query] += V^T . P^T, without LDS.  K, V and Q
-// arrive as fp32 and are rounded to bf16 in registers; accumulation is fp32
-// with an online softmax in the log2 domain.  Key blocks past the block's
+// the B operand of O^T[dim][query] += V^T . P^T, without LDS.  Q, K and V
+// arrive as bf16 (written so by the weight-streaming MFMA GEMMs);
+// accumulation is fp32 with an online softmax in the log2 domain.  Key blocks past the block's
 // furthest query position are skipped (causality).  o is written as bf16
 // rows [T][n_h * d_h], the input of the W_O product.
 #include <math.h>
@@ -40,19 +40,6 @@ constexpr int kKB = 32;    // keys per block
 constexpr int kKSteps = kW / 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline bf16x8 to_bf16x8(const float4 a, const float4 b) {
-  bf16x8 r;
-  r[0] = (__bf16)a.x;
-  r[1] = (__bf16)a.y;
-  r[2] = (__bf16)a.z;
-  r[3] = (__bf16)a.w;
-  r[4] = (__bf16)b.x;
-  r[5] = (__bf16)b.y;
-  r[6] = (__bf16)b.z;
-  r[7] = (__bf16)b.w;
-  return r;
-}
-
 __device__ inline uint32_t pack2(float x, float y) {
   return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
 }
@@ -62,7 +49,7 @@ __device__ inline uint32_t pack2(float x, float y) {
 // lane holds column n = c, k = 8h .. 8h + 7.  D[m][n]: lane holds column
 // n = c, rows 8 (r >> 2) + 4h + (r & 3) for r = 0 .. 15.
 __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
-    const float* __restrict__ q, const float* __restrict__ kbuf, const float* __restrict__ vbuf,
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kbuf, const __bf16* __restrict__ vbuf,
     const int32_t* __restrict__ positions, int T, int kv_len, __bf16* __restrict__ o) {
   const int qb = blockIdx.x, i = blockIdx.y;
   const int lane = threadIdx.x, c = lane & 31, h = lane >> 5;
@@ -78,10 +65,9 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
   // Q^T as the B operand: K-step ks holds dims 16 ks + 8h .. + 7 of query t
   bf16x8 qv[kKSteps];
   {
-    const float* qr = q + ((long)(t_ok ? t : 0) * kH + i) * kW + 8 * h;
+    const __bf16* qr = q + ((long)(t_ok ? t : 0) * kH + i) * kW + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qv[ks] = to_bf16x8(*(const float4*)(qr + 16 * ks), *(const float4*)(qr + 16 * ks + 4));
+    for (int ks = 0; ks < kKSteps; ++ks) qv[ks] = *(const bf16x8*)(qr + 16 * ks);
   }
   f32x16 acc[kDv / 32];   // O^T, dims 32 d .. 32 d + 31 x the 32 queries
 #pragma unroll
@@ -92,14 +78,12 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
     const int j0 = kb * kKB;
     // S^T = K . Q^T: the A operand is key row j0 + c (rows past kv_len
     // repeat the last one; they are masked below)
-    const float* kr = kbuf + ((long)min(j0 + c, kv_len - 1) * kH + i) * kW + 8 * h;
+    const __bf16* kr = kbuf + ((long)min(j0 + c, kv_len - 1) * kH + i) * kW + 8 * h;
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 a =
-          to_bf16x8(*(const float4*)(kr + 16 * ks), *(const float4*)(kr + 16 * ks + 4));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[ks], s, 0, 0, 0);
-    }
+    for (int ks = 0; ks < kKSteps; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + 16 * ks), qv[ks], s, 0, 0,
+                                                  0);
     // causal mask and the block's max for this query (both lane halves)
     float bm = -INFINITY;
 #pragma unroll
@@ -152,7 +136,7 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
     // 32 d + c of keys j0 + 16 kap + 8h .. + 7
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap) {
-      const float* vr[8];
+      const __bf16* vr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vr[e] = vbuf + ((long)min(j0 + 16 * kap + 8 * h + e, kv_len - 1) * kH + i) * kDv + c;
@@ -160,7 +144,7 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
       for (int d = 0; d < kDv / 32; ++d) {
         bf16x8 a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (__bf16)vr[e][32 * d];
+        for (int e = 0; e < 8; ++e) a[e] = vr[e][32 * d];
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kap], acc[d], 0, 0, 0);
       }
     }
@@ -178,18 +162,81 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
                 pack2(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv)};
 }
 
+
+// Cached rows [kv_len][576] (bf16, gathered through the page table; NaN
+// for a page id outside the cache) and the RoPE key part of every head's
+// k_ij = [W_UK,i c_j | k^R_j]: k[j][i][128 ..] = k^R_j.  One work-group per
+// row, 16 bytes per thread and store.
+__global__ __launch_bounds__(256) void prefill_rows_v2_kernel(
+    int page, const __bf16* __restrict__ cache, int num_pages, const int32_t* __restrict__ page_table,
+    __bf16* __restrict__ rows, __bf16* __restrict__ kbuf) {
+  constexpr int kRow = 576, kPieces = kRow / 8, kRope = (kW - kDv) / 8;   // 72, 8
+  const int j = blockIdx.x, tid = threadIdx.x;
+  const int pg = page_table[j / page];
+  const bool ok = pg >= 0 && pg < num_pages;
+  const uint4* src = (const uint4*)(cache + ((long)(ok ? pg : 0) * page + j % page) * kRow);
+  const uint4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  if (tid < kPieces) ((uint4*)(rows + (long)j * kRow))[tid] = ok ? src[tid] : nan4;
+  for (int e = tid; e < kH * kRope; e += 256) {
+    const int hd = e / kRope, pc = e % kRope;
+    ((uint4*)(kbuf + ((long)j * kH + hd) * kW + kDv))[pc] = ok ? src[kPieces - kRope + pc] : nan4;
+  }
+}
+
+// q[t][i][128 ..] = RoPE(qr[t][i][0 .. 64], p_t) as bf16 (qr fp32, already
+// scaled); NaN for a position outside the table.  One thread per pair.
+__global__ __launch_bounds__(256) void prefill_rope_q_v2_kernel(
+    const float* __restrict__ qr, const int32_t* __restrict__ positions, long n,
+    const float* __restrict__ rope, int rope_len, __bf16* __restrict__ q) {
+  constexpr int kHalf = (kW - kDv) / 2;   // 32 pairs per head
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int k = (int)(idx % kHalf);
+  const long ti = idx / kHalf;   // t * 128 + i
+  const int pos = positions[ti / kH];
+  const float2 x = *(const float2*)(qr + ti * (kW - kDv) + 2 * k);
+  float o0 = __builtin_nanf(""), o1 = __builtin_nanf("");
+  if (pos >= 0 && pos < rope_len) {
+    const float2 cs = *(const float2*)(rope + ((long)pos * kHalf + k) * 2);
+    o0 = x.x * cs.x - x.y * cs.y;
+    o1 = x.x * cs.y + x.y * cs.x;
+  }
+  *(uint32_t*)(q + ti * kW + kDv + 2 * k) = pack2(o0, o1);
+}
+
 }  // namespace
 
 bool prefill_v2_supported(const Geo& g) {
   return is_v2_fast(g) && g.d_h + g.d_r == kW && g.d_h == kDv && g.n_h == kH;
 }
 
-hipError_t attn_prefill_v2(const Geo& g, const float* q, const float* kbuf, const float* vbuf,
+hipError_t attn_prefill_v2(const Geo& g, const void* q, const void* kbuf, const void* vbuf,
                            const int32_t* positions, int T, int kv_len, void* o, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (!prefill_v2_supported(g) || kv_len <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prefill_v2_kernel, dim3((T + kQB - 1) / kQB, kH), dim3(64), 0, s, q,
-                     kbuf, vbuf, positions, T, kv_len, (__bf16*)o);
+  hipLaunchKernelGGL(attn_prefill_v2_kernel, dim3((T + kQB - 1) / kQB, kH), dim3(64), 0, s,
+                     (const __bf16*)q, (const __bf16*)kbuf, (const __bf16*)vbuf, positions, T,
+                     kv_len, (__bf16*)o);
+  return hipGetLastError();
+}
+
+hipError_t prefill_rows_v2(const Geo& g, const void* cache, int num_pages,
+                           const int32_t* page_table, int kv_len, void* rows, void* kbuf,
+                           hipStream_t s) {
+  if (kv_len <= 0) return hipSuccess;
+  if (!prefill_v2_supported(g)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_rows_v2_kernel, dim3(kv_len), dim3(256), 0, s, g.page,
+                     (const __bf16*)cache, num_pages, page_table, (__bf16*)rows, (__bf16*)kbuf);
+  return hipGetLastError();
+}
+
+hipError_t prefill_rope_q_v2(const Geo& g, const float* qr, const int32_t* positions, int T,
+                             const float* rope, int rope_len, void* q, hipStream_t s) {
+  const long n = (long)T * kH * ((kW - kDv) / 2);
+  if (n <= 0) return hipSuccess;
+  if (!prefill_v2_supported(g)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_rope_q_v2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     qr, positions, n, rope, rope_len, (__bf16*)q);
   return hipGetLastError();
 }
 

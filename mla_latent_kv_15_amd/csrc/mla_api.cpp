@@ -611,10 +611,18 @@ int mla_append_kv(const mla_config* cfg, const mla_weights* w, const void* h,
   const GType Ty = st(g);
   const bool wt = w->layout == MLA_LAYOUT_TILES;
   // c^KV_t = W_DKV h_t into columns [0, d_c); W_KR h_t into [d_c, d_c + d_r)
-  MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_c, g.d, h, g.d, 0, w->W_DKV,
-                       g.d, 0, y, g.row, 0, 1, 1.f, s));
-  MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_r, g.d, h, g.d, 0, w->W_KR,
-                       g.d, 0, y + g.d_c, g.row, 0, 1, 1.f, s));
+  if (is_v2_fast(g)) {
+    // the weight-streaming MFMA GEMM, fp32 out (64-row activation blocks)
+    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.d_c, g.d, h, g.d, 0, 0, w->W_DKV, y, g.row, 0, true, 1.f,
+                  s, false, false, wt));
+    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.d_r, g.d, h, g.d, 0, 0, w->W_KR, y + g.d_c, g.row, 0, true,
+                  1.f, s, false, false, wt));
+  } else {
+    MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_c, g.d, h, g.d, 0, w->W_DKV,
+                         g.d, 0, y, g.row, 0, 1, 1.f, s));
+    MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_r, g.d, h, g.d, 0, w->W_KR,
+                         g.d, 0, y + g.d_c, g.row, 0, 1, 1.f, s));
+  }
   MLA_TRY(append_finish(g, y, positions, slot_mapping, T, rope_table, rope_len, kv_cache,
                         num_pages, s));
   return MLA_OK;
@@ -892,6 +900,39 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
   const GType Ty = st(g);
   const bool wt = w->layout == MLA_LAYOUT_TILES;
   const long wq = (long)g.n_h * (g.d_h + g.d_r);
+  if (prefill_v2_supported(g)) {
+    // DeepSeek-V2 heads: bf16 intermediates, every product on the
+    // weight-streaming MFMA GEMM (64-row activation blocks, no K split), the
+    // attention on bf16 MFMA.  The fp32 buffers of the generic path hold them.
+    void* cq16 = p.cq;                                      // [T][d_cq]
+    void* q16 = p.q;                                        // [T][n_h][d_h + d_r]
+    float* qr = (float*)((char*)p.q + (size_t)T * wq * 2);  // [T][n_h][d_r], scaled
+    void* rows16 = p.rows;                                  // [kv_len][row]
+    void* k16 = p.kbuf;                                     // [kv_len][n_h][d_h + d_r]
+    void* v16 = p.vbuf;                                     // [kv_len][n_h][d_h]
+    void* o16 = p.o;                                        // [T][n_h d_h]
+    const long nq = (long)g.n_h * g.d_h;
+    // c^Q = W_DQ h; q^C_i = scale W_UQ,i c^Q into columns 0..127 of head i
+    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, cq16, g.d_cq, 0, false,
+                  1.f, s, false, false, wt));
+    MLA_TRY(wgemm(GemmTile{4, 1}, T, (int)nq, g.d_cq, cq16, g.d_cq, 0, 0, w->W_UQ, q16, wq, 0,
+                  false, g.scale, s, false, false, wt, g.d_h, g.d_h + g.d_r));
+    // scale W_QR,i c^Q in fp32, rotated and packed into columns 128..191
+    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, 0, 0, w->W_QR, qr,
+                  (long)g.n_h * g.d_r, 0, true, g.scale, s, false, false, wt));
+    MLA_TRY(prefill_rope_q_v2(g, qr, positions, T, rope_table, rope_len, q16, s));
+    // order A: k_ij = [W_UK,i c_j | k^R_j] and v_ij = W_UV,i c_j from the rows
+    MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, kv_len, rows16, k16, s));
+    MLA_TRY(wgemm(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, 0, 0, w->W_UK, k16, wq,
+                  0, false, 1.f, s, false, false, wt, g.d_h, g.d_h + g.d_r));
+    MLA_TRY(wgemm(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, 0, 0, w->W_UV, v16, nq,
+                  0, false, 1.f, s, false, false, wt));
+    // causal attention, then u = W_O o
+    MLA_TRY(attn_prefill_v2(g, q16, k16, v16, positions, T, kv_len, o16, s));
+    MLA_TRY(wgemm(GemmTile{5, 1}, T, g.d, (int)nq, o16, nq, 0, 0, w->W_O, out, g.d, 0, false, 1.f,
+                  s, false, false, wt));
+    return MLA_OK;
+  }
   // query: c^Q, then per head [q^C_i | q^R_i] (192-d at V2), RoPE on q^R
   MLA_TRY(gemm_generic(Ty, Ty, G_F32, b_layout(wt, false), T, g.d_cq, g.d, h, g.d, 0, w->W_DQ,
                        g.d, 0, p.cq, g.d_cq, 0, 1, 1.f, s));
@@ -914,14 +955,6 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                        0, w->W_UV, g.d_c, (long)g.d_h * g.d_c, p.vbuf,
                        (long)g.n_h * g.d_h, g.d_h, g.n_h, 1.f, s));
   // causal softmax attention with 192-d scores and 128-d values, then W_O
-  if (prefill_v2_supported(g)) {
-    // bf16 MFMA attention, o as bf16 rows; u = W_O o on the weight-streaming
-    // MFMA GEMM (one 64-row activation block per grid row, no K split)
-    MLA_TRY(attn_prefill_v2(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, p.o, s));
-    MLA_TRY(wgemm(GemmTile{5, 1}, T, g.d, g.n_h * g.d_h, p.o, (long)g.n_h * g.d_h, 0, 0, w->W_O,
-                  out, g.d, 0, false, 1.f, s, false, false, wt));
-    return MLA_OK;
-  }
   MLA_TRY(attn_prefill_generic(g, p.q, p.kbuf, p.vbuf, positions, T, kv_len, rope_len, p.o, s));
   MLA_TRY(gemm_generic(G_F32, Ty, Ty, b_layout(wt, false), T, g.d, g.n_h * g.d_h, p.o,
                        (long)g.n_h * g.d_h, 0, w->W_O, (long)g.n_h * g.d_h, 0, out, g.d, 0, 1,

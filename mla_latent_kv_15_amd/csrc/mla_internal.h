@@ -160,11 +160,21 @@ hipError_t rope_inplace_heads(const Geo& g, float* q, int T, long ld_row, int of
 hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
                                 const float* vbuf, const int32_t* positions, int T, int kv_len,
                                 int rope_len, float* o, hipStream_t s);
-// The same causal attention on bf16 MFMA for the DeepSeek-V2 head shape (q,
-// k, v and p rounded to bf16, fp32 accumulation); o is bf16 [T][n_h * d_h].
+// The same causal attention on bf16 MFMA for the DeepSeek-V2 head shape:
+// q [T][n_h][192], k [kv_len][n_h][192], v [kv_len][n_h][128] bf16 (p rounded
+// to bf16, fp32 accumulation); o is bf16 [T][n_h * d_h].
 bool prefill_v2_supported(const Geo& g);
-hipError_t attn_prefill_v2(const Geo& g, const float* q, const float* kbuf, const float* vbuf,
+hipError_t attn_prefill_v2(const Geo& g, const void* q, const void* kbuf, const void* vbuf,
                            const int32_t* positions, int T, int kv_len, void* o, hipStream_t s);
+// Its inputs besides the GEMM outputs: the cached rows [kv_len][576] bf16
+// gathered through the page table (NaN for a bad page id) with k^R_j
+// copied into every head's key, and RoPE of the scaled fp32 q^R into q
+// (NaN for a position outside the table).
+hipError_t prefill_rows_v2(const Geo& g, const void* cache, int num_pages,
+                           const int32_t* page_table, int kv_len, void* rows, void* kbuf,
+                           hipStream_t s);
+hipError_t prefill_rope_q_v2(const Geo& g, const float* qr, const int32_t* positions, int T,
+                             const float* rope, int rope_len, void* q, hipStream_t s);
 
 // Order-A backward pieces (k_backward.hip): P and dS [n_h][T][N] per (query,
 // head) from q [T][n_h][d_h + d_r], K, V [N][n_h][d_h], rows [N][row] and dO
