@@ -277,6 +277,69 @@ def backward_measure(args, T):
     }), flush=True)
 
 
+def prefill_measure(args, T):
+    """Append and causal prefill (mla_append_kv, mla_prefill) of one sequence
+    of T tokens at the V2 shape, positions 0..T-1, 64-token shuffled pages,
+    tiled weights.  Prints one JSON line: the prefill time and its algorithmic
+    flop rate against the bf16 MFMA peak (every product and the attention run
+    on bf16 MFMA)."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_15_amd import device, inputs, lib
+    s = inputs.V2
+    cfg = lib.make_config(s, 64, "bf16")
+    lib.load()
+    W = device.weights(inputs.make_weights(s, 5, "bf16"))
+    rows = lib.make_weights(W)
+    packed = device.workspace(lib.packed_weights_size(cfg))
+    wts = lib.pack_weights(cfg, rows, packed)
+    torch.cuda.synchronize()
+    del W, rows
+    h = device.tensor(inputs.make_hidden(T, s, 5, "bf16"))
+    paged = inputs.make_paged([T], 64, 5, shuffle=True)
+    cache = torch.zeros(paged.num_pages, 64, s.row, dtype=torch.bfloat16, device="cuda")
+    rope = torch.empty(T + 1, s.d_r // 2, 2, dtype=torch.float32, device="cuda")
+    lib.rope_table_init(cfg, T + 1, rope)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    slots = torch.from_numpy(paged.slots(0).astype(np.int32)).cuda()
+    pt = torch.from_numpy(paged.page_table[0].astype(np.int32)).cuda()
+    wsa = device.workspace(lib.workspace_size(cfg, lib.OP_APPEND, T))
+    ws = device.workspace(lib.workspace_size(cfg, lib.OP_PREFILL, T, T))
+    out = torch.empty(T, s.d, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(2, args.steps // 10)
+    append_ms = timed(lambda: lib.append_kv(cfg, wts, h, pos, slots, rope, cache, wsa), n)
+    ms = timed(lambda: lib.prefill(cfg, wts, h, pos, cache, pt, T, rope, ws, out), n)
+    d, hh, dh, dr, dc, dq = s.d, s.n_h, s.d_h, s.d_r, s.d_c, s.d_cq
+    pairs = T * (T + 1) // 2                      # causal (query, key) pairs
+    flop = 2.0 * (T * d * dq + T * dq * hh * (dh + dr)      # c^Q, q^C and q^R
+                  + 2 * T * dc * hh * dh                     # K^C and V of the T rows
+                  + pairs * hh * (dh + dr) + pairs * hh * dh  # scores, P V
+                  + T * hh * dh * d)                         # W_O
+    tflops = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "causal prefill (mla_prefill, order A)", "unit": "ms", "value": ms,
+        "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+        "append_ms": append_ms,
+        "config": {"workload": f"DeepSeek-V2 layer, one sequence of {T} tokens, positions "
+                               f"0..{T - 1}, 64-token shuffled pages, weights tiled"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "flop": flop},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +356,8 @@ def main():
     ap.add_argument("--baseline", choices=("mha",), default=None,
                     help="instead of the step: time decode attention over an MHA-equivalent "
                          "cache against MLA's on the same batch and exit")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="time append + causal prefill of one T-token sequence instead")
     ap.add_argument("--backward", type=int, default=0, metavar="T",
                     help="instead of the step: time the order-A attention backward for T "
                          "queries over T cached rows and exit")
@@ -328,6 +393,9 @@ def main():
         return
     if args.backward:
         backward_measure(args, args.backward)
+        return
+    if args.prefill:
+        prefill_measure(args, args.prefill)
         return
     cfg = lib.make_config(s, 64, "bf16")
     log(f"building {args.sets} buffer set(s) for workload {args.workload}")
