@@ -9,7 +9,8 @@
 // k_ij = [W_UK,i c_j | k^R_j], v_ij = W_UV,i c_j.  A query whose position
 // lies outside [0, kv_len) gets NaN.
 //
-// Design: one wave per (block of 32 queries, head).  The scores are formed
+// Design: one wave per (block of 32 queries, head), four such waves of one
+// head per work-group sharing each key block through LDS.  The scores are formed
 // transposed, S^T[key][query] = K . Q^T, with v_mfma_f32_32x32x16_bf16, so
 // that every lane owns one query: its softmax statistics stay in the lane
 // apart from one permlane32 swap with the lane 32 apart, which holds the
@@ -48,19 +49,37 @@ __device__ inline uint32_t pack2(float x, float y) {
 // h = l >> 5.  A[m][k]: lane holds row m = c, k = 8h .. 8h + 7.  B[k][n]:
 // lane holds column n = c, k = 8h .. 8h + 7.  D[m][n]: lane holds column
 // n = c, rows 8 (r >> 2) + 4h + (r & 3) for r = 0 .. 15.
-__global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
+//
+// A work-group of four waves takes 128 consecutive queries of one head; its
+// threads stage each block of 32 keys in LDS once for all four waves (K as
+// rows, V transposed to [dim][key]), double-buffered with one barrier per
+// block.  Rows are padded by 16 bytes to spread the banks.
+constexpr int kWQ = 4;                       // waves (query blocks) per work-group
+constexpr int kKRow = kW + 8;                // LDS K row: 192 + 8 bf16
+constexpr int kVRow = kKB + 8;               // LDS V^T row: 32 + 8 bf16
+constexpr int kKElems = kKB * kKRow;         // 6400
+constexpr int kBufElems = kKElems + kDv * kVRow;   // + 5120
+constexpr int kKPieces = kKB * kW / 8;       // 768 16-byte pieces of a K block
+constexpr int kVPieces = kKB * kDv / 8;      // 512 of a V block
+
+__global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kbuf, const __bf16* __restrict__ vbuf,
     const int32_t* __restrict__ positions, int T, int kv_len, __bf16* __restrict__ o) {
-  const int qb = blockIdx.x, i = blockIdx.y;
-  const int lane = threadIdx.x, c = lane & 31, h = lane >> 5;
-  const int t = qb * kQB + c;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][kBufElems];
+  __shared__ int s_far[kWQ];
+  const int i = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const int t = (blockIdx.x * kWQ + wave) * kQB + c;
   const bool t_ok = t < T;
   const int pos = t_ok ? positions[t] : -1;
   const bool valid = pos >= 0 && pos < kv_len;
   const int last = valid ? pos : -1;   // this query sees keys 0 .. last
-  int far = last;
+  int far = last;                      // the wave's furthest key
   for (int off = 32; off >= 1; off >>= 1) far = max(far, __shfl_xor(far, off));
-  const int nkb = (far + kKB) / kKB;   // key blocks the wave visits (0: no valid query)
+  if (lane == 0) s_far[wave] = far;
+  __syncthreads();
+  const int far_wg = max(max(s_far[0], s_far[1]), max(s_far[2], s_far[3]));
+  const int nkb = (far_wg + kKB) / kKB;   // key blocks the work-group stages
 
   // Q^T as the B operand: K-step ks holds dims 16 ks + 8h .. + 7 of query t
   bf16x8 qv[kKSteps];
@@ -69,85 +88,127 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qv[ks] = *(const bf16x8*)(qr + 16 * ks);
   }
-  f32x16 acc[kDv / 32];   // O^T, dims 32 d .. 32 d + 31 x the 32 queries
+  // staging: K pieces p = tid + 256 r (key p / 24, piece p % 24), V pieces
+  // (key p / 16, dims 8 (p % 16) ..); rows past kv_len repeat the last one.
+  // (Five named registers: an array here ends up in scratch.)
+  static_assert(kKPieces == 3 * 256 && kVPieces == 2 * 256, "staging assumes 3 + 2 pieces");
+  uint4 k0r, k1r, k2r, v0r, v1r;
+  auto kpiece = [&](int kb, int r) {
+    const int p = tid + 256 * r, key = p / (kW / 8), pc = p % (kW / 8);
+    return *(const uint4*)(kbuf + ((long)min(kb * kKB + key, kv_len - 1) * kH + i) * kW + 8 * pc);
+  };
+  auto vpiece = [&](int kb, int r) {
+    const int p = tid + 256 * r, key = p / (kDv / 8), pc = p % (kDv / 8);
+    return *(const uint4*)(vbuf + ((long)min(kb * kKB + key, kv_len - 1) * kH + i) * kDv + 8 * pc);
+  };
+  auto gload = [&](int kb) {
+    k0r = kpiece(kb, 0);
+    k1r = kpiece(kb, 1);
+    k2r = kpiece(kb, 2);
+    v0r = vpiece(kb, 0);
+    v1r = vpiece(kb, 1);
+  };
+  auto kstore = [&](__bf16* K, int r, uint4 x) {
+    const int p = tid + 256 * r, key = p / (kW / 8), pc = p % (kW / 8);
+    *(uint4*)(K + key * kKRow + 8 * pc) = x;
+  };
+  auto vstore = [&](__bf16* VT, int r, uint4 x) {
+    const int p = tid + 256 * r, key = p / (kDv / 8), pc = p % (kDv / 8);
+    const bf16x8 v = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) VT[(8 * pc + e) * kVRow + key] = v[e];
+  };
+  auto lstore = [&](int buf) {
+    __bf16* K = lds[buf];
+    kstore(K, 0, k0r);
+    kstore(K, 1, k1r);
+    kstore(K, 2, k2r);
+    vstore(K + kKElems, 0, v0r);
+    vstore(K + kKElems, 1, v1r);
+  };
+
+  f32x16 acc[kDv / 32];   // O^T, dims 32 d .. 32 d + 31 x the wave's 32 queries
 #pragma unroll
   for (int d = 0; d < kDv / 32; ++d) acc[d] = f32x16{};
   float m = -INFINITY, l = 0.f;   // running max (log2 units) and sum of this lane's query
 
+  if (nkb > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) gload(kb + 1);   // in flight during this block's products
+    const __bf16* K = lds[kb & 1];
+    const __bf16* VT = K + kKElems;
     const int j0 = kb * kKB;
-    // S^T = K . Q^T: the A operand is key row j0 + c (rows past kv_len
-    // repeat the last one; they are masked below)
-    const __bf16* kr = kbuf + ((long)min(j0 + c, kv_len - 1) * kH + i) * kW + 8 * h;
-    f32x16 s = {};
+    if (j0 <= far) {   // the wave has a query that sees a key of this block
+      // S^T = K . Q^T
+      f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + 16 * ks), qv[ks], s, 0, 0,
-                                                  0);
-    // causal mask and the block's max for this query (both lane halves)
-    float bm = -INFINITY;
+      for (int ks = 0; ks < kKSteps; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(K + c * kKRow + 16 * ks + 8 * h),
+                                                    qv[ks], s, 0, 0, 0);
+      // causal mask and the block's max for this query (both lane halves)
+      float bm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      s[r] = key <= last ? s[r] * kLog2e : -INFINITY;
-      bm = fmaxf(bm, s[r]);
-    }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
-                                                       false, false);
-      bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mn = fmaxf(m, bm);
-    const float ref = mn == -INFINITY ? 0.f : mn;   // no key seen yet: all numerators 0
-    const float alpha = __builtin_amdgcn_exp2f(m - ref);
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
-      ps += s[r];
-    }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
-                                                       false, false);
-      ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    l = l * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
-    // P^T as the B operand: K-step kap needs keys 16 kap + 8h .. + 7 of this
-    // lane's query.  A lane holds keys 4h .. 4h + 3 (+ 8, 16, 24); the lane
-    // 32 apart holds the other four of each eight.
-    uint32_t R[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) R[k] = pack2(s[2 * k], s[2 * k + 1]);
-#pragma unroll
-    for (int k = 0; k < 8; k += 4) {
-      const auto s0 = __builtin_amdgcn_permlane32_swap(R[k], R[k + 2], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(R[k + 1], R[k + 3], false, false);
-      R[k] = s0[0];
-      R[k + 2] = s0[1];
-      R[k + 1] = s1[0];
-      R[k + 3] = s1[1];
-    }
-    const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{R[0], R[1], R[2], R[3]}),
-                          __builtin_bit_cast(bf16x8, u32x4{R[4], R[5], R[6], R[7]})};
-    // O^T += V^T . P^T: the A operand of dim tile d, K-step kap is dim
-    // 32 d + c of keys j0 + 16 kap + 8h .. + 7
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-      const __bf16* vr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vr[e] = vbuf + ((long)min(j0 + 16 * kap + 8 * h + e, kv_len - 1) * kH + i) * kDv + c;
-#pragma unroll
-      for (int d = 0; d < kDv / 32; ++d) {
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = vr[e][32 * d];
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kap], acc[d], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        s[r] = key <= last ? s[r] * kLog2e : -INFINITY;
+        bm = fmaxf(bm, s[r]);
       }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm),
+                                                         __float_as_uint(bm), false, false);
+        bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mn = fmaxf(m, bm);
+      const float ref = mn == -INFINITY ? 0.f : mn;   // no key seen yet: all numerators 0
+      const float alpha = __builtin_amdgcn_exp2f(m - ref);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
+        ps += s[r];
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps),
+                                                         __float_as_uint(ps), false, false);
+        ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      l = l * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
+      // P^T as the B operand: K-step kap needs keys 16 kap + 8h .. + 7 of
+      // this lane's query.  A lane holds keys 4h .. 4h + 3 (+ 8, 16, 24); the
+      // lane 32 apart holds the other four of each eight.
+      uint32_t R[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) R[k] = pack2(s[2 * k], s[2 * k + 1]);
+#pragma unroll
+      for (int k = 0; k < 8; k += 4) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(R[k], R[k + 2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(R[k + 1], R[k + 3], false, false);
+        R[k] = s0[0];
+        R[k + 2] = s0[1];
+        R[k + 1] = s1[0];
+        R[k + 3] = s1[1];
+      }
+      const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{R[0], R[1], R[2], R[3]}),
+                            __builtin_bit_cast(bf16x8, u32x4{R[4], R[5], R[6], R[7]})};
+      // O^T += V^T . P^T: the A operand of dim tile d, K-step kap is dim
+      // 32 d + c of the block's keys 16 kap + 8h .. + 7
+#pragma unroll
+      for (int kap = 0; kap < 2; ++kap)
+#pragma unroll
+        for (int d = 0; d < kDv / 32; ++d)
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(const bf16x8*)(VT + (32 * d + c) * kVRow + 16 * kap + 8 * h), pb[kap], acc[d], 0,
+              0, 0);
     }
+    if (kb + 1 < nkb) lstore((kb + 1) & 1);   // that buffer was last read in block kb - 1
+    __syncthreads();
   }
   if (!t_ok) return;
   // lane (c, h) holds dims 32 d + 8 g + 4h .. + 3 (g = r >> 2) of query t
@@ -161,7 +222,6 @@ __global__ __launch_bounds__(64) void attn_prefill_v2_kernel(
           uint2{pack2(acc[d][4 * g] * inv, acc[d][4 * g + 1] * inv),
                 pack2(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv)};
 }
-
 
 // Cached rows [kv_len][576] (bf16, gathered through the page table; NaN
 // for a page id outside the cache) and the RoPE key part of every head's
@@ -214,7 +274,8 @@ hipError_t attn_prefill_v2(const Geo& g, const void* q, const void* kbuf, const 
                            const int32_t* positions, int T, int kv_len, void* o, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (!prefill_v2_supported(g) || kv_len <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prefill_v2_kernel, dim3((T + kQB - 1) / kQB, kH), dim3(64), 0, s,
+  hipLaunchKernelGGL(attn_prefill_v2_kernel, dim3((T + kWQ * kQB - 1) / (kWQ * kQB), kH),
+                     dim3(64 * kWQ), 0, s,
                      (const __bf16*)q, (const __bf16*)kbuf, (const __bf16*)vbuf, positions, T,
                      kv_len, (__bf16*)o);
   return hipGetLastError();
