@@ -200,7 +200,10 @@ int mla_decode_output(const mla_config* cfg, const mla_weights* w, const void* l
  * v_j = W_UV,i c^KV_j; query t (from h[t] at positions[t]) attends causally to
  * rows 0..positions[t] of the one sequence described by page_table (device
  * int32 [max_pages]) and kv_len; out: device [T][d].  Query rows with
- * positions outside [0, kv_len) get NaN outputs. */
+ * positions outside [0, kv_len) get NaN outputs.  At the DeepSeek-V2 bf16
+ * shape every product and the attention run on bf16 MFMA with fp32
+ * accumulation and bf16 intermediates (c^Q, q, k, v, o); other shapes use
+ * fp32 intermediates. */
 int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                 const int32_t* positions, const void* kv_cache, int num_pages,
                 const int32_t* page_table, int max_pages, int kv_len, int T,
