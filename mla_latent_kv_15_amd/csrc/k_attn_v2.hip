@@ -871,7 +871,7 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
 }
 
 // ---------------------------------------------------------------------------
-// the same merge for small batches: one work-group of two waves per
+// the same merge for small batches: one work-group of kRunWaves waves per
 // (sequence, head block n of 32, latent run of 32 dims).  Accumulator
 // x = 4 mb + n of the attention kernel's wave wo holds, in element 4a' + c at
 // lane (m32, hf), head 32n + m32 and dim 128 wo + 4 (8a' + 4 hf + c) + mb; the
@@ -879,18 +879,20 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
 // + 31, one contiguous run.  Sixteen times the work-groups of
 // combine_v2_kernel, so that a few sequences with many segments each still
 // spread over the GPU; within a work-group wave q sums the segments
-// s = q (mod 2), the first loads are issued before the softmax statistics are
-// formed, and the two waves' sums are added at the end.
+// s = q (mod kRunWaves), the first loads are issued before the softmax
+// statistics are formed, and the waves' sums are added at the end in a fixed
+// order.
 // ---------------------------------------------------------------------------
+constexpr int kRunWaves = 4;   // waves per merge work-group, each a share of the segments
 constexpr int kRunSegs = 264;   // (m, l) kept in LDS: every automatic plan (<= CUs + 1 segments)
 
-__global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
+__global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtrs plan,
                                                          const __bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          __bf16* __restrict__ lat_out) {
   __shared__ float2 s_ml[kRunSegs][32];   // (m, l), then the segment weights in .x
   __shared__ float s_M[32], s_inv[32];
-  __shared__ f32x4 s_acc[4][64];          // wave 1's sums
+  __shared__ f32x4 s_acc[kRunWaves - 1][4][64];   // the sums of waves 1 ..
   __shared__ __bf16 stage[32][32 + 8];
   const int b = blockIdx.x, n = blockIdx.y, wo = blockIdx.z >> 2, a = blockIdx.z & 3;
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
@@ -901,18 +903,18 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
     // no valid segment: NaN.  (More segments than kRunSegs come only from a
     // forced split count beyond the work-group budget; the host sends those
     // to combine_v2_kernel.)
-    for (int e = tid; e < 32 * 32; e += 128)
+    for (int e = tid; e < 32 * 32; e += 64 * kRunWaves)
       out[(e >> 5) * kDc + (e & 31)] = (__bf16)__builtin_nanf("");
     return;
   }
   const int hd_l = lane & 31;
-  // this wave's segments s = q, q + 2, ...: the first kU in flight now
+  // this wave's segments s = q, q + kRunWaves, ...: the first kU in flight now
   constexpr int kU = 8;
   uint2 v[kU][4];
   auto issue = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int su = min(s0 + 2 * u, cnt - 1);   // past the end: re-read, weight 0
+      const int su = min(s0 + kRunWaves * u, cnt - 1);   // past the end: re-read, weight 0
       const uint2* src =
           (const uint2*)(part_o + (long)(k0 + su) * kHeads * kDc) + wo * 64 + lane;
 #pragma unroll
@@ -920,7 +922,7 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
     }
   };
   issue(q);
-  for (int e = tid; e < cnt * 32; e += 128)
+  for (int e = tid; e < cnt * 32; e += 64 * kRunWaves)
     s_ml[e >> 5][e & 31] =
         *(const float2*)(part_ml + ((long)(k0 + (e >> 5)) * kHeads + n * 32 + (e & 31)) * 2);
   __syncthreads();
@@ -940,7 +942,7 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
     }
   }
   __syncthreads();
-  for (int e = tid; e < cnt * 32; e += 128) {
+  for (int e = tid; e < cnt * 32; e += 64 * kRunWaves) {
     const int s = e >> 5, hh = e & 31;
     s_ml[s][hh].x = __expf(s_ml[s][hh].x - s_M[hh]) * s_inv[hh];
   }
@@ -948,11 +950,11 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
   f32x4 acc[4];   // [mb]
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = f32x4{};
-  for (int s0 = q; s0 < cnt; s0 += 2 * kU) {
+  for (int s0 = q; s0 < cnt; s0 += kRunWaves * kU) {
     if (s0 != q) issue(s0);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int su = s0 + 2 * u;
+      const int su = s0 + kRunWaves * u;
       if (su >= cnt) continue;
       const float ws = s_ml[su][hd_l].x;
 #pragma unroll
@@ -963,13 +965,16 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
                               __uint_as_float(v[u][mb].y & 0xffff0000u)};
     }
   }
-  if (q == 1)
+  if (q > 0)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) s_acc[mb][lane] = acc[mb];
+    for (int mb = 0; mb < 4; ++mb) s_acc[q - 1][mb][lane] = acc[mb];
   __syncthreads();
   if (q == 0) {
+    // the waves' sums added in a fixed order
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] += s_acc[mb][lane];
+    for (int w = 0; w < kRunWaves - 1; ++w)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] += s_acc[w][mb][lane];
     // element c of acc[mb] at lane (m32, hf): head 32n + m32, dim
     // 32 a + 16 hf + 4 c + mb of this work-group's run
     const int hf = lane >> 5;
@@ -979,7 +984,7 @@ __global__ __launch_bounds__(128) void combine_v2_runs_kernel(PlanPtrs plan,
       for (int c = 0; c < 4; ++c) stage[hd_l][16 * hf + 4 * c + mb] = (__bf16)acc[mb][c];
   }
   __syncthreads();
-  {
+  if (tid < 128) {
     const int hh = tid >> 2, c8 = tid & 3;
     *(uint4*)(out + (long)hh * kDc + 8 * c8) = *(const uint4*)(&stage[hh][8 * c8]);
   }
@@ -1018,7 +1023,7 @@ hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const 
     hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan,
                        (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   else
-    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves), dim3(128), 0,
+    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves), dim3(64 * kRunWaves), 0,
                        s, plan, (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   return hipGetLastError();
 }
