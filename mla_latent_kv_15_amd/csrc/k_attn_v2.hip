@@ -349,7 +349,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         (void*)(q_abs + (long)b * kHeads * kRow), 0, kHeads * kRowBytes, kRsrcWord3);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, ks * step, 0));
+      qreg[ks] = __builtin_bit_cast(bf16x8,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rs, off, ks * step, 0));
   };
 
 
@@ -1023,8 +1024,8 @@ hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const 
     hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan,
                        (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   else
-    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves), dim3(64 * kRunWaves), 0,
-                       s, plan, (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
+    hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves),
+                       dim3(64 * kRunWaves), 0, s, plan, (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   return hipGetLastError();
 }
 

@@ -10,16 +10,17 @@
 // lies outside [0, kv_len) gets NaN.
 //
 // Design: one wave per (block of 32 queries, head), four such waves of one
-// head per work-group sharing each key block through LDS.  The scores are formed
-// transposed, S^T[key][query] = K . Q^T, with v_mfma_f32_32x32x16_bf16, so
-// that every lane owns one query: its softmax statistics stay in the lane
-// apart from one permlane32 swap with the lane 32 apart, which holds the
-// other half of the block's keys.  Four more swaps turn the numerators into
-// the B operand of O^T[dim][query] += V^T . P^T, without LDS.  Q, K and V
-// arrive as bf16 (written so by the weight-streaming MFMA GEMMs);
-// accumulation is fp32 with an online softmax in the log2 domain.  Key blocks past the block's
-// furthest query position are skipped (causality).  o is written as bf16
-// rows [T][n_h * d_h], the input of the W_O product.
+// head per work-group, which stages each block of 32 keys in LDS once for
+// all four.  The scores are formed transposed, S^T[key][query] = K . Q^T,
+// with v_mfma_f32_32x32x16_bf16, so that every lane owns one query: its
+// softmax statistics stay in the lane apart from one permlane32 swap with
+// the lane 32 apart, which holds the other half of the block's keys.  Four
+// more swaps turn the numerators into the B operand of
+// O^T[dim][query] += V^T . P^T in registers.  Q, K and V arrive as bf16
+// (written so by the weight-streaming MFMA GEMMs); accumulation is fp32 with
+// an online softmax in the log2 domain.  Key blocks past a wave's furthest
+// query position are skipped (causality).  o is written as bf16 rows
+// [T][n_h * d_h], the input of the W_O product.
 #include <math.h>
 
 #include "mla_internal.h"
@@ -147,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       f32x16 s = {};
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(K + c * kKRow + 16 * ks + 8 * h),
-                                                    qv[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)(K + c * kKRow + 16 * ks + 8 * h), qv[ks], s, 0, 0, 0);
       // causal mask and the block's max for this query (both lane halves)
       float bm = -INFINITY;
 #pragma unroll
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
 // k_ij = [W_UK,i c_j | k^R_j]: k[j][i][128 ..] = k^R_j.  One work-group per
 // row, 16 bytes per thread and store.
 __global__ __launch_bounds__(256) void prefill_rows_v2_kernel(
-    int page, const __bf16* __restrict__ cache, int num_pages, const int32_t* __restrict__ page_table,
-    __bf16* __restrict__ rows, __bf16* __restrict__ kbuf) {
+    int page, const __bf16* __restrict__ cache, int num_pages,
+    const int32_t* __restrict__ page_table, __bf16* __restrict__ rows, __bf16* __restrict__ kbuf) {
   constexpr int kRow = 576, kPieces = kRow / 8, kRope = (kW - kDv) / 8;   // 72, 8
   const int j = blockIdx.x, tid = threadIdx.x;
   const int pg = page_table[j / page];
