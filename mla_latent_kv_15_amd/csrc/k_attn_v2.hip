@@ -771,7 +771,7 @@ __global__ __launch_bounds__(256) void qtile_pack_kernel(const uint4* __restrict
 // ---------------------------------------------------------------------------
 constexpr int kCombSegs = 64;   // segments weighed per pass
 
-__global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
+__global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
                                                          const __bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          __bf16* __restrict__ lat_out) {
@@ -779,19 +779,21 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
   __shared__ float2 s_ml[kCombSegs][32];
   __shared__ float s_M[32], s_inv[32];
   __shared__ __bf16 stage[32][kDc + 8];
+  __shared__ f32x4 s_acc[16][256];   // the odd-segment half's sums
   const int b = blockIdx.x, n = blockIdx.y, t = threadIdx.x;
+  const int half = t >> 8, tt = t & 255;   // tt: the accumulator slot, as below
   const int cnt = plan.seq_seg_count[b];
   const int k0 = plan.seq_seg_start[b];
   __bf16* out = lat_out + ((long)b * kHeads + n * 32) * kDc;
   if (cnt == 0) {
-    for (int e = t; e < 32 * kDc; e += 256) out[e] = (__bf16)__builtin_nanf("");
+    for (int e = t; e < 32 * kDc; e += 512) out[e] = (__bf16)__builtin_nanf("");
     return;
   }
   // (m, l) of every segment of the head group: one parallel load into LDS
   // when they fit (else read in the loops below)
   const bool in_lds = cnt <= kCombSegs;
   if (in_lds)
-    for (int e = t; e < cnt * 32; e += 256)
+    for (int e = t; e < cnt * 32; e += 512)
       s_ml[e >> 5][e & 31] =
           *(const float2*)(part_ml + ((long)(k0 + (e >> 5)) * kHeads + n * 32 + (e & 31)) * 2);
   __syncthreads();
@@ -812,9 +814,10 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
     s_inv[t] = 1.f / L;
   }
   __syncthreads();
-  // thread t takes lane t & 63 of the attention kernel's wave wo = t >> 6,
-  // whose accumulators x = 4 mb + n hold latent dims [128 wo, 128 wo + 128)
-  const int lane = t & 63, wo = t >> 6;
+  // thread t takes lane tt & 63 of the attention kernel's wave wo = tt >> 6,
+  // whose accumulators x = 4 mb + n hold latent dims [128 wo, 128 wo + 128);
+  // the two halves of the work-group sum the even and the odd segments
+  const int lane = tt & 63, wo = tt >> 6;
   const int hd_l = lane & 31;
   f32x4 acc[16];   // [4 mb + a]
 #pragma unroll
@@ -822,20 +825,21 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
   for (int c0 = 0; c0 < cnt; c0 += kCombSegs) {
     const int nc = min(kCombSegs, cnt - c0);
     __syncthreads();
-    for (int e = t; e < nc * 32; e += 256) {
+    for (int e = t; e < nc * 32; e += 512) {
       const int s = e >> 5, hh = e & 31;
       w[s][hh] = __expf(ml_of(c0 + s, hh).x - s_M[hh]) * s_inv[hh];
     }
     __syncthreads();
-    // four segments' loads in flight at once; the sum still runs over the
+    // four segments' loads in flight per half at once; each half sums its
     // segments in order
     constexpr int kU = 4;
-    for (int s0 = 0; s0 < nc; s0 += kU) {
+    for (int s0 = half; s0 < nc; s0 += 2 * kU) {
       uint2 v[kU][16];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        if (s0 + u >= nc) break;
-        const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s0 + u) * kHeads * kDc) + t;
+        if (s0 + 2 * u >= nc) break;
+        const uint2* src =
+            (const uint2*)(part_o + (long)(k0 + c0 + s0 + 2 * u) * kHeads * kDc) + tt;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -843,8 +847,8 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        if (s0 + u >= nc) break;
-        const float ws = w[s0 + u][hd_l];
+        if (s0 + 2 * u >= nc) break;
+        const float ws = w[s0 + 2 * u][hd_l];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           acc[r] += ws * f32x4{__uint_as_float(v[u][r].x << 16),
@@ -854,18 +858,26 @@ __global__ __launch_bounds__(256) void combine_v2_kernel(PlanPtrs plan,
       }
     }
   }
-  // register order -> [head][dim]: element i = 4a + c of accumulator (mb, n)
-  // at lane (m32, hf) is head 32n + m32, dim 128 wo + 4 (8a + 4 hf + c) + mb
-  const int hf = lane >> 5;
+  if (half == 1)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        stage[hd_l][128 * wo + 4 * (8 * a + 4 * hf + c) + mb] = (__bf16)acc[4 * mb + a][c];
+    for (int r = 0; r < 16; ++r) s_acc[r][tt] = acc[r];
   __syncthreads();
-  for (int e = t; e < 32 * (kDc / 8); e += 256) {
+  if (half == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += s_acc[r][tt];
+    // register order -> [head][dim]: element i = 4a + c of accumulator
+    // (mb, n) at lane (m32, hf) is head 32n + m32, dim 128 wo + 4 (8a + 4 hf + c) + mb
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          stage[hd_l][128 * wo + 4 * (8 * a + 4 * hf + c) + mb] = (__bf16)acc[4 * mb + a][c];
+  }
+  __syncthreads();
+  for (int e = t; e < 32 * (kDc / 8); e += 512) {
     const int hh = e / (kDc / 8), c8 = e % (kDc / 8);
     *(uint4*)(out + (long)hh * kDc + 8 * c8) = *(const uint4*)(&stage[hh][8 * c8]);
   }
@@ -1021,7 +1033,7 @@ hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const 
   // one, num_splits)
   const int max_per_seq = num_splits > 0 ? num_splits : plan_dims(B, 0).max_wg + 1;
   if (B >= 32 || max_per_seq > kRunSegs)
-    hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(256), 0, s, plan,
+    hipLaunchKernelGGL(combine_v2_kernel, dim3(B, kHeads / 32), dim3(512), 0, s, plan,
                        (const __bf16*)part_o, part_ml, (__bf16*)lat_out);
   else
     hipLaunchKernelGGL(combine_v2_runs_kernel, dim3(B, kHeads / 32, 4 * kWaves),
