@@ -83,40 +83,73 @@ def build_set(s, B, lo, hi, cid, sub, device, inputs, lib, cfg, weights):
                 Hq=Hq, offs=offs)
 
 
+def host_info():
+    """CPU model, the BLAS library numpy calls and its thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", 1
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    except Exception:  # noqa: BLE001
+        pass
+    return model, blas, threads
+
+
 def cpu_baseline(s, st, budget_s, cid):
-    """The fp64 oracle (order A, the reference) on a bounded sample of the
-    same workload: whole sequences until the time budget is spent."""
+    """The fp64 oracle on a bounded sample of the same workload: whole
+    sequences until the time budget is spent, first in order A (the
+    reference: keys and values decompressed per head), then in order B (the
+    same algorithm as the GPU path: absorbed query, latent attention, one
+    decompression) on the same sequences."""
     import numpy as np
 
     import oracle
     from mla_latent_kv_15_amd import inputs
-    try:
-        import threadpoolctl
-        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
-    except Exception:  # noqa: BLE001
-        threads = 1
+    model, blas, threads = host_info()
     W64 = {k: v.f64() for k, v in inputs.make_weights(s, cid, "bf16").items()}
-    t0 = time.perf_counter()
-    done = 0
-    toks = 0
     sc = oracle.default_scale(s.d_h, s.d_r)
-    for b in range(len(st["L"])):
+    H64 = st["Hq"].f64()
+
+    def one(b, order):
         n = int(st["kv"][b])
         rows = inputs.make_cache_rows(n, s, 9000 + b, "bf16").f64()
-        q_c, q_r = oracle.query(st["Hq"].f64()[b], W64["W_DQ"], W64["W_UQ"], W64["W_QR"],
-                                int(st["L"][b]), s.n_h, 10000.0)
-        o = oracle.attend_order_a(q_c, q_r, rows[:, :s.d_c], rows[:, s.d_c:], W64["W_UK"],
-                                  W64["W_UV"], sc)
+        q_c, q_r = oracle.query(H64[b], W64["W_DQ"], W64["W_UQ"], W64["W_QR"], int(st["L"][b]),
+                                s.n_h, 10000.0)
+        fn = oracle.attend_order_a if order == "A" else oracle.attend_order_b
+        t0 = time.perf_counter()
+        o = fn(q_c, q_r, rows[:, :s.d_c], rows[:, s.d_c:], W64["W_UK"], W64["W_UV"], sc)
         oracle.integrate(o, W64["W_O"])
+        return time.perf_counter() - t0, n
+
+    spent, done, toks = 0.0, 0, 0
+    for b in range(len(st["L"])):
+        dt, n = one(b, "A")
+        spent += dt
         done += 1
         toks += n
-        if time.perf_counter() - t0 > budget_s:
+        if spent > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"order-A fp64 decode of the first {done} of the batch's sequences "
-                      f"({toks} cached rows) in {dt:.1f} s; each sequence yields one token"}
+    spent_b = sum(one(b, "B")[0] for b in range(done))
+    return {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
+            "sample": f"order-A fp64 decode (query projections, per-head decompressed "
+                      f"attention, W_O) of the first {done} of the batch's sequences "
+                      f"({toks} cached rows) in {spent:.1f} s; each sequence yields one token; "
+                      f"the time to generate the synthetic rows is not counted",
+            "order_b": {"value": done / spent_b, "unit": "tokens/s",
+                        "sample": f"order-B fp64 decode of the same {done} sequences in "
+                                  f"{spent_b:.2f} s"}}
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -422,7 +455,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timing")
-    lib.profile_enable(True)
+    # 1) the timed region: K steps back to back, nothing else on the stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -432,15 +465,33 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    attn_ms, launches = lib.profile_attention_ms()
-    lib.profile_enable(False)
     ms_step = total_ms / args.steps
+    # 2) the same K steps with an event between consecutive steps: the
+    # distribution of per-step times
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    # 3) the same K steps with the library's events around the attention
+    # kernel and its merge, on the stream they are launched on
+    lib.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    attn_ms, attn_merge_ms, launches = lib.profile_read()
+    lib.profile_enable(False)
     attn_avg = attn_ms / max(launches, 1)
+    am_avg = attn_merge_ms / max(launches, 1)
     # per-launch algorithmic work: the cached rows of the step's batch (sets alternate)
     toks = [int(st["kv"].sum()) for st in sets]
     toks_avg = sum(toks[i % len(sets)] for i in range(args.steps)) / args.steps
     cache_bytes = toks_avg * BYTES_PER_TOKEN
-    achieved = cache_bytes / (attn_avg * 1e-3) / 1e9
+    achieved = cache_bytes / (am_avg * 1e-3) / 1e9
+    achieved_k = cache_bytes / (attn_avg * 1e-3) / 1e9
     mfma_tflops = toks_avg * FLOP_PER_TOKEN / (attn_avg * 1e-3) / 1e12
     weight_bytes = st0["wbytes"]
     step_bytes = cache_bytes + weight_bytes
@@ -466,6 +517,9 @@ def main():
             "d": s.d, "n_h": s.n_h, "d_h": s.d_h, "d_c": s.d_c, "d_cq": s.d_cq, "d_r": s.d_r,
             "num_splits": args.splits, "buffer_sets": len(sets), "weights": args.weights,
         },
+        "ms_per_step_median": float(np.median(per)),
+        "ms_per_step_p10": float(np.percentile(per, 10)),
+        "ms_per_step_p90": float(np.percentile(per, 90)),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -473,9 +527,12 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": measured_traffic(args.workload),
-            "kernel": "attn_v2_kernel (paged latent-cache attention)",
-            "launch_ms": attn_avg,
+            "kernel": "attn_v2_kernel + combine_v2_kernel (paged latent-cache attention and "
+                      "the merge of its split partials)",
+            "launch_ms": am_avg,
             "bytes_per_launch": cache_bytes,
+            "kernel_only": {"kernel": "attn_v2_kernel", "launch_ms": attn_avg,
+                            "achieved": achieved_k, "frac": achieved_k / HBM_PEAK_GBPS},
         },
         "attention_mfma_tflops": mfma_tflops,
         "attention_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,

@@ -288,13 +288,18 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
                            float* dW_UV, float* dq, float* dC, void* stream);
 
 /* Kernel timing for measurement tools (not needed for computing).  While
- * enabled, every mla_decode / mla_decode_attention call records a HIP event
- * pair on its stream around its cache-streaming attention kernel.
- * mla_profile_attention_ms waits for the recorded events, returns the summed
- * kernel time in milliseconds and the number of launches, and clears the
- * record.  Host-thread-unsafe; enable from one thread.  Returns MLA_ERR_HIP
- * if an event call fails. */
+ * enabled, every mla_decode / mla_decode_attention call records three HIP
+ * events on its stream: before its cache-streaming attention kernel, after
+ * it, and after the merge of the split partials.  mla_profile_read waits for
+ * the recorded events and returns, summed over the recorded launches (at
+ * most 4096 between two reads; later ones are not recorded), the attention
+ * kernel's milliseconds, the milliseconds of attention plus merge, and the
+ * number of launches; then it clears the record.  mla_profile_attention_ms
+ * is the same read returning only the attention kernel's time.
+ * Host-thread-unsafe; enable from one thread.  Returns MLA_ERR_HIP if an
+ * event call fails, MLA_ERR_INVALID_ARG for a null pointer. */
 int mla_profile_enable(int enable);
+int mla_profile_read(double* attention_ms, double* attention_merge_ms, int* launches);
 int mla_profile_attention_ms(double* total_ms, int* launches);
 
 #ifdef __cplusplus

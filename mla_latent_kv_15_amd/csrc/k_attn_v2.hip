@@ -29,10 +29,12 @@
 //    the max of the segment's first 32 scores.  Later scores may exceed it by
 //    up to 64 (P <= 2^64, harmless in fp32/bf16), so the 256-register
 //    accumulator is never rescaled - VALU work on it would push the kernel
-//    out of its 512-register budget.  If any score in the work-group exceeds
-//    the reference by more than 64, the segment is redone once with the exact
-//    maximum, which the first pass tracks (correct for any input, essentially
-//    never taken).
+//    out of its 512-register budget.  If any score of any head in the
+//    work-group exceeds that head's reference by more than 64, the whole
+//    segment is redone once with each head's exact maximum, which the first
+//    pass tracks: every wave ORs its 32 heads' flags into one vote, and the
+//    work-group ORs the four waves' votes.  A numerator is then at most 1
+//    (essentially never taken on random inputs).
 //  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T.  Each
 //    lane reads 4 dims of 8 tokens (ds_read_b64) and transposes them with
 //    v_perm_b32 into the A operand; P^T comes from LDS.
@@ -614,8 +616,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // half) for all four waves.  The last sub-tile of a first pass
         // carries the wave's redo vote in the sign bit of lane 0's first
         // number: the numerators are never negative, and a redo discards
-        // everything they feed.
-        const bool vote = mode == 0 && j == nsub - 1 && over;
+        // everything they feed.  `over` is per head (per lane), so the vote
+        // is the OR over the wave's 64 lanes: any of its 32 heads may need
+        // the redo.
+        const bool vote = mode == 0 && j == nsub - 1 && __builtin_amdgcn_ballot_w64(over) != 0;
 #pragma unroll
         for (int kap = 0; kap < 2; ++kap) {
           bf16x8 p;

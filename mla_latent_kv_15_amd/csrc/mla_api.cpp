@@ -321,24 +321,27 @@ int run_query(const Geo& g, const mla_weights* w, const void* h, const int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// optional event pairs around the attention kernel (measurement only)
+// optional events around the attention kernel and its merge (measurement
+// only): event 3i before the attention kernel of launch i, 3i + 1 after it,
+// 3i + 2 after the merge
 // ---------------------------------------------------------------------------
 struct Profiler {
+  static constexpr int kMax = 4096;   // launches recorded between two reads
   bool on = false;
   int used = 0;
-  hipEvent_t ev[2 * 4096];
+  hipEvent_t ev[3 * kMax];
   int created = 0;
   hipError_t mark(int which, hipStream_t s) {
     if (!on) return hipSuccess;
-    int idx = 2 * used + which;
-    if (idx >= 2 * 4096) return hipSuccess;
+    const int idx = 3 * used + which;
+    if (idx >= 3 * kMax) return hipSuccess;
     if (idx >= created) {
       hipError_t e = hipEventCreate(&ev[idx]);
       if (e != hipSuccess) return e;
       created = idx + 1;
     }
     hipError_t e = hipEventRecord(ev[idx], s);
-    if (which == 1 && e == hipSuccess) ++used;
+    if (which == 2 && e == hipSuccess) ++used;
     return e;
   }
 };
@@ -360,7 +363,6 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
     carve_plan(a.plan, B, num_splits, &plan);
     MLA_TRY(launch_plan(plan, kv_lens, B, max_kv_len, max_pages, g.page, 64, num_splits, s));
   }
-  MLA_TRY(g_prof.mark(0, s));
   if (fast) {
     // the MFMA kernel writes every segment as a partial; its merge follows
     // the MFMA kernel loads the query in the query-tile layout
@@ -369,16 +371,19 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
       MLA_TRY(pack_query_tiles(q_abs, B, a.q_tiles, s));
       qt = a.q_tiles;
     }
+    MLA_TRY(g_prof.mark(0, s));
     MLA_TRY(attn_decode_v2(g, qt, cache, num_pages, page_table, max_pages, plan, a.max_wg,
                            a.part_o, a.part_ml, s));
     MLA_TRY(g_prof.mark(1, s));
     MLA_TRY(combine_decode_v2(plan, B, num_splits, a.part_o, a.part_ml, lat, s));
   } else {
+    MLA_TRY(g_prof.mark(0, s));
     MLA_TRY(attn_decode_generic(g, q_abs, cache, num_pages, page_table, max_pages, plan,
                                 a.max_segs, a.part_o, a.part_ml, lat, s));
     MLA_TRY(g_prof.mark(1, s));
     MLA_TRY(combine_partials(g, plan, B, a.part_o, a.part_ml, lat, s));
   }
+  MLA_TRY(g_prof.mark(2, s));
   return MLA_OK;
 }
 
@@ -499,20 +504,28 @@ int mla_profile_enable(int enable) {
   return MLA_OK;
 }
 
-int mla_profile_attention_ms(double* total_ms, int* launches) {
-  if (!total_ms || !launches) return MLA_ERR_INVALID_ARG;
-  double tot = 0.0;
+int mla_profile_read(double* attention_ms, double* attention_merge_ms, int* launches) {
+  if (!attention_ms || !attention_merge_ms || !launches) return MLA_ERR_INVALID_ARG;
+  double ta = 0.0, tm = 0.0;
   for (int i = 0; i < g_prof.used; ++i) {
-    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return MLA_ERR_HIP;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
+    if (hipEventSynchronize(g_prof.ev[3 * i + 2]) != hipSuccess) return MLA_ERR_HIP;
+    float a = 0.f, m = 0.f;
+    if (hipEventElapsedTime(&a, g_prof.ev[3 * i], g_prof.ev[3 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&m, g_prof.ev[3 * i], g_prof.ev[3 * i + 2]) != hipSuccess)
       return MLA_ERR_HIP;
-    tot += ms;
+    ta += a;
+    tm += m;
   }
-  *total_ms = tot;
+  *attention_ms = ta;
+  *attention_merge_ms = tm;
   *launches = g_prof.used;
   g_prof.used = 0;
   return MLA_OK;
+}
+
+int mla_profile_attention_ms(double* total_ms, int* launches) {
+  double merge_ms = 0.0;
+  return mla_profile_read(total_ms, &merge_ms, launches);
 }
 
 int mla_rope_table_init(const mla_config* cfg, int max_pos, float* d_table, void* stream) {

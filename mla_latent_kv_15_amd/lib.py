@@ -90,6 +90,8 @@ _SIGS = {
                                        _P, c_size_t, _P, _P, _P, _P, _P]),
     "mla_profile_enable": (c_int, [c_int]),
     "mla_profile_attention_ms": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
+    "mla_profile_read": (c_int, [ctypes.POINTER(c_double), ctypes.POINTER(c_double),
+                                 ctypes.POINTER(c_int)]),
     "mla_prefill": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, c_int, c_int, _P, c_int, _P,
                             c_size_t, _P, _P]),
 }
@@ -270,6 +272,16 @@ def attention_backward(cfg, weights, q, positions, kv_cache, page_table_row, kv_
 
 def profile_enable(on: bool):
     _check("mla_profile_enable", load().mla_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """(summed attention-kernel ms, summed attention + merge ms, launches)
+    since the last read."""
+    a, m = c_double(0.0), c_double(0.0)
+    n = c_int(0)
+    _check("mla_profile_read", load().mla_profile_read(ctypes.byref(a), ctypes.byref(m),
+                                                         ctypes.byref(n)))
+    return a.value, m.value, n.value
 
 
 def profile_attention_ms():
