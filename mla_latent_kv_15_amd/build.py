@@ -79,23 +79,28 @@ def _check_scratch(src: str, remarks: str):
 
 
 def _check_hot_blocks(src: str, asm: str):
-    """No spill code inside a basic block of the hot kernel that issues MFMAs."""
+    """No spill code inside a basic block of the hot kernel that issues MFMAs
+    (every instantiation of it)."""
     kernel = HOT_KERNELS[os.path.basename(src)]
     lines = asm.splitlines()
     code = [l.split(";")[0].rstrip() for l in lines]   # drop the assembler's comments
-    begin = next(i for i, c in enumerate(code)
-                 if c.endswith(":") and kernel in c and not c.startswith((".", "\t")))
-    block, label, bad = [], lines[begin], []
-    for l, c in zip(lines[begin + 1:], code[begin + 1:]):
-        if c.startswith(".Lfunc_end"):
-            break
-        is_label = (c.endswith(":") and c.startswith(".LBB")) or l.startswith("; %bb.")
-        if is_label:
-            if any("v_mfma" in x for x in block):
-                bad += [f"{label.split()[0]} {x.strip()}" for x in block if _is_spill(x)]
-            block, label = [], l
-        else:
-            block.append(l)
+    begins = [i for i, c in enumerate(code)
+              if c.endswith(":") and kernel in c and not c.startswith((".", "\t"))]
+    if not begins:
+        raise RuntimeError(f"{os.path.basename(src)}: {kernel} not found in the assembly")
+    bad = []
+    for begin in begins:
+        block, label = [], lines[begin]
+        for l, c in zip(lines[begin + 1:], code[begin + 1:]):
+            if c.startswith(".Lfunc_end"):
+                break
+            is_label = (c.endswith(":") and c.startswith(".LBB")) or l.startswith("; %bb.")
+            if is_label:
+                if any("v_mfma" in x for x in block):
+                    bad += [f"{label.split()[0]} {x.strip()}" for x in block if _is_spill(x)]
+                block, label = [], l
+            else:
+                block.append(l)
     if bad:
         raise RuntimeError(f"{os.path.basename(src)}: spill code in MFMA blocks of {kernel}:\n  "
                            + "\n  ".join(bad[:10]))

@@ -15,6 +15,14 @@
 //    accumulator that fills the 256 accumulation registers.  The waves swap
 //    their softmax numerators P through LDS, so each wave reads only its
 //    quarter of the latent tile for the second contraction.
+//  * with one wave per SIMD the instruction stream sets the pace: beside each
+//    32-cycle MFMA there is room for about two other instructions before the
+//    MFMA pipe idles.  So every LDS read is a per-lane base register plus an
+//    immediate offset (eight bases for the score reads, two for the
+//    accumulation reads, moved with the ring slot once per sub-tile), the
+//    cache operand of the second contraction comes straight from
+//    ds_read_b64_tr_b16 (no register shuffles), and the softmax is a max,
+//    an exp2 and a pack per score.
 //  * 32-token sub-tiles stream through a four-slot LDS ring with 16-byte
 //    direct-to-LDS buffer loads, two sub-tiles in flight while the scores of
 //    sub-tile j and the accumulation of sub-tile j-1 run.  A slot holds the
@@ -25,19 +33,20 @@
 //    address arithmetic to one or two instructions.
 //  * scores: S^T[token][head] = C[token][dims] . Q~^T[dims][head] with
 //    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~), 36 K-steps.
-//  * softmax numerators in the log2 domain against a per-segment reference:
-//    the max of the segment's first 32 scores.  Later scores may exceed it by
-//    up to 64 (P <= 2^64, harmless in fp32/bf16), so the 256-register
-//    accumulator is never rescaled - VALU work on it would push the kernel
-//    out of its 512-register budget.  If any score of any head in the
-//    work-group exceeds that head's reference by more than 64, the whole
-//    segment is redone once with each head's exact maximum, which the first
-//    pass tracks: every wave ORs its 32 heads' flags into one vote, and the
-//    work-group ORs the four waves' votes.  A numerator is then at most 1
-//    (essentially never taken on random inputs).
-//  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T.  Each
-//    lane reads 4 dims of 8 tokens (ds_read_b64) and transposes them with
-//    v_perm_b32 into the A operand; P^T comes from LDS.
+//    The absorption writes query tiles that carry a factor log2(e), so the
+//    scores come out in log2 units; tiles rearranged from a caller's rows
+//    are exact copies, and that variant multiplies in the exponent's fma.
+//  * softmax numerators 2^s with no reference at all in a first pass (exact
+//    softmax algebra while every numerator stays inside fp32/bf16 range), so
+//    the 256-register accumulator is never rescaled.  Each head's maximum is
+//    tracked; if any head of the work-group ends a segment with its maximum
+//    outside [-64, 64], the whole segment is redone once with each head's
+//    maximum as the reference (numerators <= 1): every wave ORs its 32
+//    heads' flags into one vote, and the work-group ORs the four votes.
+//  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T.  The
+//    token order inside a sub-tile is chosen so that the score registers are
+//    P^T's operand as they stand, and each transposing read fetches four
+//    tokens two rows apart (conflict-free under the XOR permutation).
 //  * the MFMA stream of an iteration interleaves the 36 score steps with the
 //    32 accumulation steps and the ring refill; sched_barrier pins the order.
 //  * a work-group walks the segments the plan assigns to it and writes each
@@ -59,6 +68,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 128;
 constexpr int kRow = 576;             // bf16 numbers per cached token
@@ -83,11 +93,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kKSteps = kRow / 16;    // 36 score K-steps of 16 dims
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 64.0f;        // allowed score excess over the reference (log2 units)
+constexpr float kLazy = 64.0f;        // largest |head maximum| a pass without reference takes (log2 units)
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) v4bf16 lds_v4bf16;
 
 __device__ __shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
 
@@ -162,39 +173,63 @@ __device__ inline void lds_store(int byte, T v) {
 }
 
 // One 32-token sub-tile in flight: rows [0, 32) of a page run starting at
-// the resource's base go to LDS slot `slot`.  Rows at or past nvalid
+// the descriptor's base go to LDS slot `slot`.  Rows at or past nvalid
 // (rmax = nvalid - 1) re-read row rmax: their scores are masked to zero
 // weight and the data stays finite, so 0 * row never turns into NaN.  Wave w
 // moves rows [8w, 8w+8): loads 0..7 the latent part of one row each, load 8
 // the RoPE parts of all eight.  Every wave issues exactly kInstsPerWave loads
 // per sub-tile whatever nvalid is; the ring's vmcnt bookkeeping relies on it.
 //
-// The loads are MUBUF (buffer_load ... lds) rather than global_load_lds: the
-// compiler treats an outstanding FLAT-encoded LDS load as an LDS access of
-// unknown order and then waits for every LDS read with lgkmcnt(0), which
-// would serialise the operand prefetch of the compute loop.
+// The loads are MUBUF direct-to-LDS loads written as inline asm.  The
+// compiler's own LDS-DMA tracking would otherwise treat them as possible
+// writers of every later LDS read it cannot disambiguate - the transposing
+// ds_read_b64_tr_b16 among them - and wait for all vector memory operations
+// (vmcnt(0)) before each such read, draining the ring.  The kernel orders
+// ring data itself: an explicit vmcnt wait for its own sub-tile, then a
+// barrier.  (The loads write no registers, so no register result of an asm
+// load is ever left in flight.)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct Refill {
-  __amdgpu_buffer_rsrc_t rs;
+  i32x4 rs;   // buffer descriptor (base, num_records) in scalar registers
   int slot;   // LDS byte offset of the ring slot
   int rmax;
 };
 
-__device__ inline void ring_load(const Refill& rf, int i, int wave, int lane) {
-  int w = wave, l = lane;
-  asm volatile("" : "+s"(w), "+v"(l));  // recompute per call: no live per-load state
+// raw buffer descriptor over [p, p + bytes)
+__device__ inline i32x4 make_rsrc(const void* p, int bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  return i32x4{(int)(unsigned)a, (int)((a >> 32) & 0xffffu), bytes, kRsrcWord3};
+}
+
+__device__ inline void lds_dma16(const i32x4& rs, int voff, int soff, int lds_byte) {
+  const int m0 = __builtin_amdgcn_readfirstlane(
+      (int)(uintptr_t)((lds_char*)g_lds + lds_byte));
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "s"(m0) : "m0");
+}
+
+// lat16: (lane ^ 8 (w & 1)) << 4, the lane's piece position of row 8w (the
+// XOR permutation of rows 8w + i differs from it by i); rope_off: this lane's
+// source offset in a full sub-tile's RoPE load
+__device__ inline void ring_load(const Refill& rf, int i, int wave, int lat16, int rope_off) {
   if (i < 8) {
-    const int r = 8 * w + i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rf.rs, (lds_void*)((lds_char*)g_lds + rf.slot + r * kLatBytes), 16,
-        (l << 4) ^ ((r & 15) << 4), min(r, rf.rmax) * kRowBytes, 0, 0);
+    const int r = 8 * wave + i;
+    lds_dma16(rf.rs, lat16 ^ (i << 4), min(r, rf.rmax) * kRowBytes, rf.slot + r * kLatBytes);
   } else {
-    const int r = 8 * w + (l >> 3);   // this lane's row; piece l & 7 of its RoPE part
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rf.rs, (lds_void*)((lds_char*)g_lds + rf.slot + kRopeOff + 8 * w * kRopeBytes), 16,
-        min(r, rf.rmax) * kRowBytes + kLatBytes + (((l & 7) ^ swz_rope(r)) << 4), 0, 0, 0);
+    int off = rope_off;
+    if (rf.rmax < kSub - 1) {   // a partial sub-tile: clamp each lane's row
+      const int lane = lane_here();
+      const int r = 8 * wave + (lane >> 3);
+      off = min(r, rf.rmax) * kRowBytes + kLatBytes + (((lane & 7) ^ swz_rope(r)) << 4);
+    }
+    lds_dma16(rf.rs, off, 0, rf.slot + kRopeOff + 8 * wave * kRopeBytes);
   }
 }
 
+// kQLog2e: the query tiles carry log2(e) (written so by the absorption, one
+// rounding from fp32); otherwise they are the caller's rows rearranged, and
+// each score is scaled by log2(e) inside the exponent's fma.
+template <bool kQLog2e>
 __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ cache, int num_pages,
     const int32_t* __restrict__ page_table, int max_pages, int page,
@@ -216,19 +251,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;     // lane half
   const int m32 = lane & 31;
-  const int head = wave * 32 + m32;
 
-  // Per-lane LDS byte offsets within a ring slot.
-  // scores, latent K-step ks: row m32, piece 2ks + h at position
-  // (2ks + h) ^ (m32 & 15)  ->  (qa ^ ((ks & 7) << 5)) + 256 (ks >> 3)
-  const int qa = m32 * kLatBytes + ((h ^ (m32 & 15)) << 4);
-  // scores, RoPE K-step 32 + r: row m32, RoPE piece 2r + h -> qra ^ (r << 5)
-  const int qra = kRopeOff + m32 * kRopeBytes + ((h ^ swz_rope(m32)) << 4);
-  // accumulation, element e = 4a + c of the 8 tokens of lane (m32, h): token
-  // row R = 16 kap + 8a + 4h + c, dims 4 m32 .. 4 m32 + 3 of this wave's 128,
-  // i.e. latent piece 16w + (m32 >> 1), half m32 & 1:
-  // (pa ^ ((8a + c) << 4)) + (16 kap + 8a + c) * 1024
-  const int pa = 4 * h * kLatBytes + 256 * wave + (((m32 >> 1) ^ (4 * h)) << 4) + 8 * (m32 & 1);
+  // ---- per-lane LDS byte offsets, relative to ring slot 0 and moved with
+  // the ring slot once per sub-tile (so every read below is a base register
+  // plus an immediate offset).
+  //
+  // Token order.  Score-MFMA row m = 16 kap + 8 b + 4 hm + r (kap, b, hm in
+  // {0, 1}, r < 4) reads sub-tile token rho(m) = 16 kap + 4 r + 2 b + hm.  The
+  // score registers of lane (head, hm) then hold, in register i = 8 kap + e,
+  // the token rho(16 kap + 8 (e / 4) + 4 hm + e % 4) - exactly the K index
+  // 16 kap + 8 hm + e of the latent accumulation's operands, so P needs no
+  // rearranging; and each transposing LDS read of the accumulation's cache
+  // operand fetches four tokens four rows apart, so that the 32 lanes it
+  // serves at once hit 16 distinct 16-byte bank groups under the XOR
+  // permutation (rows two apart would pair them up).
+  const int R = (m32 & 16) + 4 * (m32 & 3) + 2 * ((m32 >> 3) & 1) + ((m32 >> 2) & 1);
+  // scores, latent K-step ks = 8 a + b (16 dims): row R, 16-byte piece
+  // 2 ks + h at position (2 ks + h) ^ (R & 15) -> (qb ^ 32 b) + 256 a.  The
+  // score chain walks b-major (ks = 8 a + b for b = 0..7, a = 0..3), so each
+  // XOR-derived base serves four consecutive K-steps.
+  int qb = kRingOff + R * kLatBytes + ((h ^ (R & 15)) << 4);
+  // scores, RoPE K-step 32 + t: row R, RoPE piece 2 t + h -> qrb ^ (t << 5)
+  int qrb = kRingOff + kRopeOff + R * kRopeBytes + ((h ^ swz_rope(R)) << 4);
+  // accumulation operand (cache^T: 32 dims x 16 tokens) by ds_read_b64_tr_b16:
+  // in each 16-lane group gq, lane 4 rr + jj supplies 4 dims (chunk jj) of
+  // token row rr; output lane i then holds dim i of the four rows.  Dims
+  // block mb of this wave = dims 128 wave + 32 mb + [0, 32); K-step kap, read
+  // bb: token rows 16 kap + 4 rr + 2 bb + h.  Every bit of the position
+  // (chunk piece ^ row & 15) pairs a lane bit with mb or bb, so the address
+  // of (mb, bb, kap) is (tb ^ (32 bb + 64 mb)) + 1024 (16 kap + 2 bb).
+  int tb;
+  {
+    const int gq = lane >> 4, ii = lane & 15, rr = ii >> 2, jj = ii & 3;
+    tb = kRingOff + (4 * rr + h) * kLatBytes +
+         ((16 * wave + ((jj >> 1) ^ h) + 2 * (gq & 1) + 4 * (rr & 1) + 8 * (rr >> 1)) << 4) +
+         8 * (jj & 1);
+  }
+  // this lane's 16-byte column of a P buffer block: P of head block n, K-step
+  // kap sits at buffer + (2 n + kap) * 1024 + 16 lane
+  const int pl = 16 * lane;
+  // ring loads: this lane's piece position in row 8 wave, and its source
+  // offset in a full sub-tile's RoPE load
+  const int lat16 = (lane ^ (8 * (wave & 1))) << 4;
+  const int rope_off = (8 * wave + (lane >> 3)) * kRowBytes + kLatBytes +
+                       (((lane & 7) ^ swz_rope(8 * wave + (lane >> 3))) << 4);
+  int slot_cur = 0;   // ring slot the bases currently point into
+  auto move_bases = [&](int slot) {
+    const int d = (slot - slot_cur) * kSubBytes;
+    slot_cur = slot;
+    qb += d;
+    qrb += d;
+    tb += d;
+  };
   auto slot_off = [](int pos) { return kRingOff + (pos & (kSlots - 1)) * kSubBytes; };
 
   // Page ids, 64 pages per window: lane i holds the id of page w0 + i of
@@ -236,9 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   // loads: an outstanding scalar load would force a full LDS wait
   // (lgkmcnt(0)) at every use of an LDS read in the loop below.
   auto load_window = [&](int b, int w0) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int p = w0 + ln;
+    const int p = w0 + lane_here();
     return p < max_pages ? page_table[(long)b * max_pages + p] : -1;
   };
 
@@ -291,8 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       const bool ok = pg >= 0 && pg < num_pages;
       badm |= (ok ? 0u : 1u) << (rk & 31);
       const long row0 = ok ? (long)pg * page + rpo : 0;
-      rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
-                                                kRsrcWord3);
+      rf.rs = make_rsrc(cache + row0 * kRow, kSubBytes);
       rf.rmax = ok ? min(kSub, rt1 - rt) - 1 : 0;
       --rn;
       rt += kSub;
@@ -302,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         ++rpi;
       }
     } else {
-      rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, 0, kRsrcWord3);
+      rf.rs = make_rsrc(cache, 0);
       rf.rmax = 0;
     }
     return rf;
@@ -321,15 +392,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     const long row0 = ok ? (long)pg * page + (sn.t0 % page) + kSub * i : 0;
     Refill rf;
     rf.slot = slot_off(pos);
-    rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(cache + row0 * kRow), 0, kSubBytes,
-                                              kRsrcWord3);
+    rf.rs = make_rsrc(cache + row0 * kRow, kSubBytes);
     rf.rmax = ok ? min(kSub, sn.t1 - (sn.t0 + kSub * i)) - 1 : 0;
     return rf;
   };
   auto no_refill = [&](int pos) {
     Refill rf;
     rf.slot = slot_off(pos);
-    rf.rs = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, 0, kRsrcWord3);
+    rf.rs = make_rsrc(cache, 0);
     rf.rmax = 0;
     return rf;
   };
@@ -337,15 +407,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   bf16x8 qreg[kKSteps];    // absorbed query, B operand (lane = head, 8 dims per K-step half)
   auto load_q = [&](int b) {
     // The query arrives in the query-tile layout (qtile_index): each load
-    // reads 1 KB contiguously (in rows, 16 B from each of 64 rows 1152 B
-    // apart, the loads took several microseconds per segment).  A buffer
-    // resource on sequence b's tiles and a 32-bit per-lane offset formed
-    // here: a 64-bit per-lane address would be kept live across the sub-tile
-    // loop, spilled, and its reload would wait for every memory operation in
-    // flight.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int off = (wave * kKSteps * 64 + ln) * 16;
+    // reads 1 KB contiguously.  A buffer resource on sequence b's tiles and
+    // a 32-bit per-lane offset formed here: a 64-bit per-lane address would
+    // be kept live across the sub-tile loop, spilled, and its reload would
+    // wait for every memory operation in flight.
+    const int off = (wave * kKSteps * 64 + lane_here()) * 16;
     constexpr int step = 1024;   // bytes from one K-step to the next
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(q_abs + (long)b * kHeads * kRow), 0, kHeads * kRowBytes, kRsrcWord3);
@@ -355,12 +421,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
                                     __builtin_amdgcn_raw_buffer_load_b128(rs, off, ks * step, 0));
   };
 
-
   // the query must have landed before the sub-tile loop: a query load left in
-  // flight would make the compiler wait inside the loop behind ring loads
+  // flight would make the compiler wait inside the loop behind ring loads.
+  // Each register is read and rewritten by an empty asm statement, so that
+  // from here on its definition is that statement, not a load: the
+  // compiler then has no pending load to wait for inside the loop (where
+  // its vmcnt waits would also wait for the ring's loads, which it does not
+  // see).
   auto consume_q = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qreg[ks]));
+    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qreg[ks]));
   };
   int base = 0;   // ring position of sub-tile 0 of the segment being computed
   // a pass that loads its own first two positions (the work-group's first
@@ -373,10 +443,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     badm &= ~(1u << (k & 31));
     const Refill r0 = refill(base);
 #pragma unroll
-    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lat16, rope_off);
     const Refill r1 = refill(base + 1);
 #pragma unroll
-    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lat16, rope_off);
     load_q(b);
     consume_q();
   };
@@ -406,10 +476,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     cursor_begin(k, w);
     const Refill r0 = refill(base);
 #pragma unroll
-    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lane);
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r0, i, wave, lat16, rope_off);
     const Refill r1 = refill(base + 1);
 #pragma unroll
-    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lane);
+    for (int i = 0; i < kInstsPerWave; ++i) ring_load(r1, i, wave, lat16, rope_off);
     consume_q();
   }
   bool first_wait = true;   // iteration 0 of the first pass waits for its sub-tile
@@ -423,54 +493,55 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     const bool pf_next = has_next && nsub >= 2 && nxt.t1 - nxt.t0 > kSub;
 
     f32x16 acc[16];          // acc[4 mb + n]: dims block mb of this wave x head block n
-    // ---- latent accumulation, K-step kap (16 tokens) of the tile at LDS
-    // offset pvb - pa: 8 x ds_read_b64 -> 16 v_perm_b32 -> A operands of the
-    // 4 dims blocks; P^T of head block n from the P buffer at prd
-    u32x2 raw[8];
+    // ---- latent accumulation operands: A[mb] = cache^T of dims block mb for
+    // one K-step (two transposing reads of four tokens), B = P^T of one head
+    // block (written by wave n)
     bf16x8 A[4];
     bf16x8 B[2];
-    auto pv_read_at = [&](int pvb, int kap) {
-      static_for<0, 8>([&](auto ec) {
-        constexpr int e = decltype(ec)::value, a = e >> 2, c = e & 3;
-        raw[e] = lds_load<u32x2>(xor_here<(8 * a + c) << 4>(pvb) + (16 * kap + 8 * a + c) * kLatBytes);
+    // dslot: byte distance from the bases' slot to the accumulation slot
+    auto pv_read_into = [&](bf16x8(&dst)[4], int dslot, int kap) {
+      static_for<0, 4>([&](auto mc) {
+        constexpr int mb = decltype(mc)::value;
+        const int t = tb + dslot;
+        const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4bf16*)((lds_char*)g_lds + xor_here<64 * mb>(t) + kLatBytes * 16 * kap));
+        const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4bf16*)((lds_char*)g_lds + xor_here<32 + 64 * mb>(t) + kLatBytes * (16 * kap + 2)));
+        dst[mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       });
     };
-    auto pv_build = [&]() {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        u32x4 t;
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          t[f] = __builtin_amdgcn_perm(raw[2 * f + 1][mb >> 1], raw[2 * f][mb >> 1],
-                                       (mb & 1) ? 0x07060302u : 0x05040100u);
-        A[mb] = __builtin_bit_cast(bf16x8, t);
-      }
+    auto pv_read_at = [&](int dslot, int kap) { pv_read_into(A, dslot, kap); };
+    // P^T of head block n, K-step kap (written by wave n); pb = pl + buffer
+    auto p_read_at = [&](int pb, int kap, int n) {
+      return lds_load<bf16x8>(pb + (2 * n + kap) * 1024);
     };
-    // P^T of head block n, K-step kap (written by wave n)
-    auto p_read_at = [&](int prd, int kap, int n) {
-      int l = lane;
-      asm volatile("" : "+v"(l));
-      return lds_load<bf16x8>(prd + (2 * n + kap) * 1024 + 16 * l);
-    };
-    auto pv_mfma = [&](int mb, int n) {
+    auto pv_mfma_op = [&](const bf16x8(&op)[4], int mb, int n) {
       acc[4 * mb + n] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb], B[n & 1], acc[4 * mb + n], 0, 0, 0);
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[mb], B[n & 1], acc[4 * mb + n], 0, 0, 0);
     };
-    float m_ref = -INFINITY; // exponent reference (log2 units), fixed within a pass
+    auto pv_mfma = [&](int mb, int n) { pv_mfma_op(A, mb, n); };
+    // Softmax numerators 2^(s - m_ref) in the log2 domain (the query tiles
+    // carry log2 e).  A first pass takes m_ref = 0: no subtraction at all,
+    // which is exact softmax algebra as long as the numerators stay within
+    // fp32 and bf16 range.  The pass tracks each head's maximum m_seen; if
+    // any head of the work-group ends the segment with m_seen outside
+    // [-64, 64], the segment is redone with m_ref = m_seen (numerators <= 1).
+    float m_ref = 0.f;
     float l_run = 0.f;
-    // pass 0: reference = max of the first 32 tokens; every sub-tile's max is
-    // tracked, so after a pass-0 overflow the exact segment max is known and
-    // pass 1 redoes the segment with it as the reference
     int mode = 0;
     for (;;) {
       // opaque to the optimiser: one copy of the sub-tile loop serves both
       // passes (a scalar: the pass decides uniform control flow)
       asm volatile("" : "+s"(mode));
+      // the page windows are (re)defined here, before the loop: if the
+      // register allocator parked them in scratch around the partial's
+      // stores, their reload completes now, not at a page lookup inside the
+      // loop (where the wait would also wait for the ring's loads)
+      asm volatile("" : "+v"(pid), "+v"(pid_next));
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[x] = f32x16{};
       l_run = 0.f;
       float m_seen = -INFINITY;
-      bool over = false;
 
       // every wave is done with the previous pass's P buffers
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -478,9 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       {
         // P buffer 1 reads as the P of sub-tile -1 in iteration 0: zero it
         const u32x4 z = {};
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // the address is formed here, not kept across the loop
-        const int tl = wave * 64 + ln;
+        const int tl = wave * 64 + lane_here();   // formed here, not kept across the loop
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * tl, z);
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * (tl + kThreads), z);
       }
@@ -513,10 +582,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         lds_barrier();  // sub-tile j landed everywhere; position base+j-2's slot is free
 
         const int nvalid = min(kSub, cur.t1 - (cur.t0 + j * kSub));
-        const int sq = slot_off(base + j);                       // scores tile
-        const int sv = j == 0 ? sq : slot_off(base + j - 1);     // accumulation tile
-        const int prd = kPBufOff + ((j + 1) & 1) * kPBufBytes;   // P of sub-tile j-1
-        const int pwr = kPBufOff + (j & 1) * kPBufBytes;         // P of sub-tile j
+        const int sq_slot = (base + j) & (kSlots - 1);                    // scores tile
+        const int dv = j == 0 ? 0 : (((base + j - 1) & (kSlots - 1)) - sq_slot) * kSubBytes;
+        const int prd = pl + kPBufOff + ((j + 1) & 1) * kPBufBytes;   // P of sub-tile j-1
+        const int pwr = pl + kPBufOff + (j & 1) * kPBufBytes;         // P of sub-tile j
+        move_bases(sq_slot);
 
         // ---- scores for 32 tokens x 32 heads (inline asm with a VGPR
         // accumulator: with the builtin the compiler puts S in the
@@ -525,36 +595,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // states; the s_nop before the softmax covers MFMA-result -> VALU.
         f32x16 S;
         bf16x8 abuf[4];
-        const int qab = sq + qa, qrb = sq + qra;
-        auto a_read = [&](auto ksc) {
-          constexpr int ks = decltype(ksc)::value;
-          if constexpr (ks < 32)
-            return lds_load<bf16x8>(xor_here<(ks & 7) << 5>(qab) + 256 * (ks >> 3));
+        // region r < 32 runs latent K-step 8 (r & 3) + (r >> 2) (b-major),
+        // regions 32..35 the RoPE K-steps
+        auto ks_of = [](int r) { return r < 32 ? 8 * (r & 3) + (r >> 2) : r; };
+        auto a_read = [&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          if constexpr (r < 32)
+            return lds_load<bf16x8>(xor_here<32 * (r >> 2)>(qb) + 256 * (r & 3));
           else
-            return lds_load<bf16x8>(xor_here<(ks - 32) << 5>(qrb));
+            return lds_load<bf16x8>(xor_here<(r - 32) << 5>(qrb));
         };
         abuf[0] = a_read(ic<0>{});
         abuf[1] = a_read(ic<1>{});
         abuf[2] = a_read(ic<2>{});
         abuf[3] = a_read(ic<3>{});
-        auto qk = [&](auto ksc) {
-          constexpr int ks = decltype(ksc)::value;
+        auto qk = [&](auto rc) {
+          constexpr int r = decltype(rc)::value;
           // take this K-step's operand before its buffer slot is refilled (four
           // K-steps ahead: the LDS latency under four waves of reads)
-          const bf16x8 a = abuf[ks % 4];
-          if constexpr (ks + 4 < kKSteps) abuf[ks % 4] = a_read(ic<ks + 4>{});
-          if constexpr (ks == 0)
-            score_mfma_first(S, a, qreg[ks]);
+          const bf16x8 a = abuf[r % 4];
+          if constexpr (r + 4 < kKSteps) abuf[r % 4] = a_read(ic<r + 4>{});
+          if constexpr (r == 0)
+            score_mfma_first(S, a, qreg[ks_of(r)]);
           else
-            score_mfma(S, a, qreg[ks]);
+            score_mfma(S, a, qreg[ks_of(r)]);
         };
 
-        // ---- latent accumulation of sub-tile j-1 (tile at sv, P at prd)
-        const int pvb = sv + pa;
-        auto pv_read = [&](int kap) { pv_read_at(pvb, kap); };
+        // ---- latent accumulation of sub-tile j-1 (tile at dv from the
+        // scores' slot, P at prd)
         auto p_read = [&](int kap, int n) { return p_read_at(prd, kap, n); };
 
-        pv_read(0);
+        pv_read_at(dv, 0);
         B[0] = p_read(0, 0);
         // 36 regions, one score MFMA each; sched_barrier pins the interleave
         // (left alone, the scheduler clusters the builtin MFMAs away from the
@@ -564,9 +635,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         static_for<0, kKSteps>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
           qk(rc);
-          if constexpr (r < kInstsPerWave) ring_load(rf, r, wave, lane);
-          if constexpr (r == 2 || r == 19) pv_build();
-          if constexpr (r == 14) pv_read(1);
+          if constexpr (r < kInstsPerWave) ring_load(rf, r, wave, lat16, rope_off);
+          if constexpr (r == 19) pv_read_at(dv, 1);
           if constexpr (r >= 3 && r < 19) {
             constexpr int idx = r - 3, n = idx >> 2, mb = idx & 3;
             if constexpr (mb == 0) B[(n + 1) & 1] = n < 3 ? p_read(0, n + 1) : p_read(1, 0);
@@ -577,30 +647,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
 
         // ---- softmax numerators of sub-tile j (log2 domain), lane = head, 16
-        // of the 32 tokens; overlaps the rest of j-1's accumulation
+        // of the 32 tokens; overlaps the rest of j-1's accumulation.  Register
+        // i holds token 16 (i >> 3) + 4 (i & 3) + 2 ((i >> 2) & 1) + h.
         if (nvalid < kSub) {
+          const int hh = lane_here() >> 5;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int tok = 8 * (i >> 2) + 4 * h + (i & 3);
+            const int tok = 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
             S[i] = tok < nvalid ? S[i] : -INFINITY;
           }
         }
-        float mx[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(S[i], S[i + 8]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], mx[i + 4]);
-        float bm = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        float bm;
         {
+          float mx[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) mx[i] = fmaxf(fmaxf(S[3 * i], S[3 * i + 1]), S[3 * i + 2]);
+          bm = fmaxf(fmaxf(mx[0], mx[1]), mx[2]);
+          bm = fmaxf(fmaxf(bm, mx[3]), fmaxf(mx[4], S[15]));
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
                                                            false, false);
-          bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * kLog2e;
+          bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          if constexpr (!kQLog2e) bm *= kLog2e;
         }
         m_seen = fmaxf(m_seen, bm);
-        // pass 0 takes its reference from the first sub-tile (m_ref is -inf
-        // until then); the redo pass starts with the exact maximum
-        m_ref = (m_ref == -INFINITY) ? bm : m_ref;
-        over |= bm > m_ref + kLazy;
+        if constexpr (kQLog2e) {
+          if (mode != 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[i] -= m_ref;
+          }
+        }
+        // 2^(s log2 e - m_ref): the subtraction above, or one fma per score
+        auto num = [&](float x) {
+          if constexpr (kQLog2e)
+            return __builtin_amdgcn_exp2f(x);
+          else
+            return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -m_ref));
+        };
         // the numerators beside the first eight accumulation MFMAs, their
         // LDS write beside the last eight (which hides its latency before
         // the next barrier)
@@ -609,28 +691,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           const int n = idx >> 2, mb = idx & 3;
           if (mb == 0) B[(n + 1) & 1] = p_read(1, n + 1);
           pv_mfma(mb, n);
-          S[2 * idx] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx], kLog2e, -m_ref));
-          S[2 * idx + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * idx + 1], kLog2e, -m_ref));
+          S[2 * idx] = num(S[2 * idx]);
+          S[2 * idx + 1] = num(S[2 * idx + 1]);
         }
         // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
         // half) for all four waves.  The last sub-tile of a first pass
         // carries the wave's redo vote in the sign bit of lane 0's first
         // number: the numerators are never negative, and a redo discards
-        // everything they feed.  `over` is per head (per lane), so the vote
+        // everything they feed.  m_seen is per head (per lane), so the vote
         // is the OR over the wave's 64 lanes: any of its 32 heads may need
         // the redo.
-        const bool vote = mode == 0 && j == nsub - 1 && __builtin_amdgcn_ballot_w64(over) != 0;
+        const bool vote = mode == 0 && j == nsub - 1 &&
+                          __builtin_amdgcn_ballot_w64(!(fabsf(m_seen) <= kLazy)) != 0;
+        bf16x8 p[2];
 #pragma unroll
         for (int kap = 0; kap < 2; ++kap) {
-          bf16x8 p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = (__bf16)S[8 * kap + e];
-          if (kap == 0) {
-            u32x4 pb = __builtin_bit_cast(u32x4, p);
-            pb[0] |= (vote && lane == 0) ? 0x8000u : 0u;
-            p = __builtin_bit_cast(bf16x8, pb);
+          for (int e = 0; e < 8; ++e) p[kap][e] = (__bf16)S[8 * kap + e];
+          if (kap == 0 && vote) {   // uniform: taken once per pass at most
+            u32x4 pb = __builtin_bit_cast(u32x4, p[0]);
+            pb[0] |= lane_here() == 0 ? 0x8000u : 0u;
+            p[0] = __builtin_bit_cast(bf16x8, pb);
           }
-          lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024 + 16 * lane, p);
+          lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024, p[kap]);
         }
 #pragma unroll
         for (int idx = 8; idx < 16; ++idx) {
@@ -639,48 +722,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           pv_mfma(mb, n);
         }
         {
-          float sm[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sm[i] = S[i] + S[i + 8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm[i] += sm[i + 4];
-          l_run += (sm[0] + sm[1]) + (sm[2] + sm[3]);
+          // l over the rounded numerators the accumulation uses: pairs of
+          // bf16 dotted with (1, 1) into fp32 (the vote bit, if set, makes
+          // l negative; a redo discards it)
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          float s0 = l_run, s1 = 0.f;
+          static_for<0, 4>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_shufflevector(p[0], p[0], 2 * e, 2 * e + 1), one, s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_shufflevector(p[1], p[1], 2 * e, 2 * e + 1), one, s1, false);
+          });
+          l_run = s0 + s1;
         }
       }
-      // ---- drain: the latent accumulation of the last sub-tile.  The query
-      // registers are free from here on: the next segment's query loads now,
-      // under the accumulation and the partial's write.
+      // ---- drain: the latent accumulation of the last sub-tile.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_barrier();  // P of the last sub-tile (with the votes) is visible
-      if (has_next) load_q(nxt.b);
       {
-        const int pvb = slot_off(base + nsub - 1) + pa;
-        const int prd = kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
-        pv_read_at(pvb, 0);
+        const int dv = (((base + nsub - 1) & (kSlots - 1)) - slot_cur) * kSubBytes;
+        const int prd = pl + kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
+        // K-step 1's cache operands go to registers of their own (A1): they
+        // are read while K-step 0's MFMAs still consume A
+        bf16x8 A1[4];
+        pv_read_at(dv, 0);
         B[0] = p_read_at(prd, 0, 0);
-        pv_build();
         static_for<0, 16>([&](auto ic_) {
           constexpr int idx = decltype(ic_)::value, n = idx >> 2, mb = idx & 3;
           if constexpr (mb == 0)
             B[(n + 1) & 1] = n < 3 ? p_read_at(prd, 0, n + 1) : p_read_at(prd, 1, 0);
-          if constexpr (idx == 4) pv_read_at(pvb, 1);
+          if constexpr (idx == 4) pv_read_into(A1, dv, 1);
           pv_mfma(mb, n);
           __builtin_amdgcn_sched_barrier(0);
         });
-        pv_build();
         static_for<0, 16>([&](auto ic_) {
           constexpr int idx = decltype(ic_)::value, n = idx >> 2, mb = idx & 3;
           if constexpr (mb == 0 && n < 3) B[(n + 1) & 1] = p_read_at(prd, 1, n + 1);
-          pv_mfma(mb, n);
+          pv_mfma_op(A1, mb, n);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
-      // a score more than kLazy above the reference anywhere in the work-group
-      // (a vote in the P of the last sub-tile, visible since the drain's
-      // barrier): redo the segment with the exact maximum seen in
-      // this pass (rare).  The redo starts at the ring position after this
-      // pass, behind the loads in flight there (same slots, issued earlier by
-      // the same wave, so they land earlier).
+      // a head maximum outside [-64, 64] anywhere in the work-group (a vote
+      // in the P of the last sub-tile, visible since the drain's barrier):
+      // redo the segment with the exact maxima seen in this pass (rare).  The
+      // redo starts at the ring position after this pass, behind the loads
+      // in flight there (same slots, issued earlier by the same wave, so they
+      // land earlier).
       if (mode == 0) {
         const int pv = kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
         uint32_t v = 0;
@@ -699,6 +788,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       break;
     }
     base += nsub;
+
+    // The query registers are free from here on: the next segment's query
+    // loads now, under the partial's write.  (Issued here rather than in the
+    // drain: there, on the path that leaves the pass loop, the compiler's
+    // wait analysis would carry the loads as outstanding into the next
+    // pass's sub-tile loop and wait for them at every score step - waits
+    // that would also drain the ring.)
+    if (has_next) load_q(nxt.b);
 
     // the window of the segment after the next, issued before the partial's
     // stores so that waiting for it does not wait for the stores
@@ -758,8 +855,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   }
 }
 
-// Rows [B][128][576] -> query tiles (qtile_index): one 16-byte piece (eight
-// consecutive numbers of one row, which stay consecutive) per thread.
+// Rows [B][128][576] -> query tiles (qtile_index), values unchanged: one
+// 16-byte piece (eight consecutive numbers of one row, which stay
+// consecutive) per thread.
 __global__ __launch_bounds__(256) void qtile_pack_kernel(const uint4* __restrict__ rows, long n,
                                                          uint4* __restrict__ tiles) {
   const long p = (long)blockIdx.x * 256 + threadIdx.x;
@@ -870,7 +968,7 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] += s_acc[r][tt];
     // register order -> [head][dim]: element i = 4a + c of accumulator
-    // (mb, n) at lane (m32, hf) is head 32n + m32, dim 128 wo + 4 (8a + 4 hf + c) + mb
+    // (mb, n) at lane (m32, hf) is head 32n + m32, dim 128 wo + 32 mb + 8a + 4 hf + c
     const int hf = lane >> 5;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -878,7 +976,7 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          stage[hd_l][128 * wo + 4 * (8 * a + 4 * hf + c) + mb] = (__bf16)acc[4 * mb + a][c];
+          stage[hd_l][128 * wo + 32 * mb + 8 * a + 4 * hf + c] = (__bf16)acc[4 * mb + a][c];
   }
   __syncthreads();
   for (int e = t; e < 32 * (kDc / 8); e += 512) {
@@ -890,10 +988,10 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
 // ---------------------------------------------------------------------------
 // the same merge for small batches: one work-group of kRunWaves waves per
 // (sequence, head block n of 32, latent run of 32 dims).  Accumulator
-// x = 4 mb + n of the attention kernel's wave wo holds, in element 4a' + c at
-// lane (m32, hf), head 32n + m32 and dim 128 wo + 4 (8a' + 4 hf + c) + mb; the
-// work-group z = 4 wo + a takes a' = a of all four mb: dims 128 wo + 32 a ..
-// + 31, one contiguous run.  Sixteen times the work-groups of
+// x = 4 mb + n of the attention kernel's wave wo holds, in element 4a + c at
+// lane (m32, hf), head 32n + m32 and dim 128 wo + 32 mb + 8a + 4 hf + c; the
+// work-group z = 4 wo + mb takes all of accumulator (mb, n): dims
+// 128 wo + 32 mb .. + 31, one contiguous run.  Sixteen times the work-groups of
 // combine_v2_kernel, so that a few sequences with many segments each still
 // spread over the GPU; within a work-group wave q sums the segments
 // s = q (mod kRunWaves), the first loads are issued before the softmax
@@ -911,11 +1009,11 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
   __shared__ float s_M[32], s_inv[32];
   __shared__ f32x4 s_acc[kRunWaves - 1][4][64];   // the sums of waves 1 ..
   __shared__ __bf16 stage[32][32 + 8];
-  const int b = blockIdx.x, n = blockIdx.y, wo = blockIdx.z >> 2, a = blockIdx.z & 3;
+  const int b = blockIdx.x, n = blockIdx.y, wo = blockIdx.z >> 2, mz = blockIdx.z & 3;
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
   const int cnt = plan.seq_seg_count[b];
   const int k0 = plan.seq_seg_start[b];
-  __bf16* out = lat_out + ((long)b * kHeads + n * 32) * kDc + 128 * wo + 32 * a;
+  __bf16* out = lat_out + ((long)b * kHeads + n * 32) * kDc + 128 * wo + 32 * mz;
   if (cnt == 0 || cnt > kRunSegs) {
     // no valid segment: NaN.  (More segments than kRunSegs come only from a
     // forced split count beyond the work-group budget; the host sends those
@@ -935,7 +1033,7 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
       const uint2* src =
           (const uint2*)(part_o + (long)(k0 + su) * kHeads * kDc) + wo * 64 + lane;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) v[u][mb] = src[((4 * mb + n) * 4 + a) * kThreads];
+      for (int a = 0; a < 4; ++a) v[u][a] = src[((4 * mz + n) * 4 + a) * kThreads];
     }
   };
   issue(q);
@@ -964,7 +1062,7 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
     s_ml[s][hh].x = __expf(s_ml[s][hh].x - s_M[hh]) * s_inv[hh];
   }
   __syncthreads();
-  f32x4 acc[4];   // [mb]
+  f32x4 acc[4];   // [a]
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = f32x4{};
   for (int s0 = q; s0 < cnt; s0 += kRunWaves * kU) {
@@ -992,13 +1090,13 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
     for (int w = 0; w < kRunWaves - 1; ++w)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] += s_acc[w][mb][lane];
-    // element c of acc[mb] at lane (m32, hf): head 32n + m32, dim
-    // 32 a + 16 hf + 4 c + mb of this work-group's run
+    // element c of acc[a] at lane (m32, hf): head 32n + m32, dim
+    // 8 a + 4 hf + c of this work-group's run
     const int hf = lane >> 5;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) stage[hd_l][16 * hf + 4 * c + mb] = (__bf16)acc[mb][c];
+      for (int c = 0; c < 4; ++c) stage[hd_l][8 * a + 4 * hf + c] = (__bf16)acc[a][c];
   }
   __syncthreads();
   if (tid < 128) {
@@ -1009,14 +1107,21 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
 
 }  // namespace
 
-hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, const void* cache, int num_pages,
-                          const int32_t* page_table, int max_pages, const PlanPtrs& plan,
-                          int n_wg_launch, void* part_o, float* part_ml, hipStream_t s) {
+hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, bool q_log2e, const void* cache,
+                          int num_pages, const int32_t* page_table, int max_pages,
+                          const PlanPtrs& plan, int n_wg_launch, void* part_o, float* part_ml,
+                          hipStream_t s) {
   if (n_wg_launch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_v2_kernel, dim3(n_wg_launch), dim3(kThreads), 0, s,
-                     (const __bf16*)q_tiles, (const __bf16*)cache, num_pages, page_table,
-                     max_pages, g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
-                     (const Seg*)plan.segs, (__bf16*)part_o, part_ml);
+  if (q_log2e)
+    hipLaunchKernelGGL(attn_v2_kernel<true>, dim3(n_wg_launch), dim3(kThreads), 0, s,
+                       (const __bf16*)q_tiles, (const __bf16*)cache, num_pages, page_table,
+                       max_pages, g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
+                       (const Seg*)plan.segs, (__bf16*)part_o, part_ml);
+  else
+    hipLaunchKernelGGL(attn_v2_kernel<false>, dim3(n_wg_launch), dim3(kThreads), 0, s,
+                       (const __bf16*)q_tiles, (const __bf16*)cache, num_pages, page_table,
+                       max_pages, g.page, (const int*)plan.counts, (const int*)plan.wg_seg_start,
+                       (const Seg*)plan.segs, (__bf16*)part_o, part_ml);
   return hipGetLastError();
 }
 

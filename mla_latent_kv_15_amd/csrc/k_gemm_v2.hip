@@ -521,6 +521,7 @@ hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void
                      const float* rope, int rope_len, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(2 * 128, (M + kMT - 1) / kMT);
+  if (q_tiled) scale *= kQTileLog2e;   // query tiles hold scores in log2 units
   if (w_tiled)
     hipLaunchKernelGGL(absorb_kernel<true>, grid, dim3(256), 0, s, M, (const __bf16*)qc,
                        (const __bf16*)W_UK, (__bf16*)q_abs, (int)q_tiled, scale, q_r,

@@ -372,8 +372,8 @@ int run_attention(const Geo& g, const void* q_abs, const void* cache, int num_pa
       qt = a.q_tiles;
     }
     MLA_TRY(g_prof.mark(0, s));
-    MLA_TRY(attn_decode_v2(g, qt, cache, num_pages, page_table, max_pages, plan, a.max_wg,
-                           a.part_o, a.part_ml, s));
+    MLA_TRY(attn_decode_v2(g, qt, q_tiled, cache, num_pages, page_table, max_pages, plan,
+                           a.max_wg, a.part_o, a.part_ml, s));
     MLA_TRY(g_prof.mark(1, s));
     MLA_TRY(combine_decode_v2(plan, B, num_splits, a.part_o, a.part_ml, lat, s));
   } else {

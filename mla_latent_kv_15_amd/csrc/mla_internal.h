@@ -91,10 +91,13 @@ __host__ __device__ inline long tile_index(long r, long c, long C) {
 // Query tiles: the absorbed query of the V2 fast path (128 heads of 576
 // numbers per sequence) in the register order of the attention kernel's B
 // operand, so that each of its query loads reads 1 KB contiguously instead of
-// 16 B from each of 64 rows 1152 B apart.  Element (m, head, d) sits at
+// 16 B from each of 64 rows 1152 B apart.  Tiles the absorption writes hold
+// the query times kQTileLog2e, so that the kernel's scores come out in log2
+// units; tiles rearranged from a caller's rows hold the rows as they are.  Element (m, head, d) sits at
 // [m][head / 32][d / 16][lane][d % 8] with lane = head % 32 + 32 ((d / 8) % 2):
 // the 64 lanes of one wave's K-step of 16 numbers, 8 bf16 each.  A sequence's
 // tiles occupy the same 147,456 bytes as its rows.
+constexpr float kQTileLog2e = 1.4426950408889634f;
 __host__ __device__ inline long qtile_index(long m, int head, int d) {
   return (((m * 4 + (head >> 5)) * 36 + (d >> 4)) * 64 + (head & 31) + 32 * ((d >> 3) & 1)) * 8 +
          (d & 7);
@@ -199,10 +202,14 @@ hipError_t mha_decode(const Geo& g, const void* q, const void* cache, int num_pa
 // MFMA kernels for the V2 bf16 shape
 // ---------------------------------------------------------------------------
 // q_tiles: the absorbed query in the query-tile layout (qtile_index).
-hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, const void* cache, int num_pages,
-                          const int32_t* page_table, int max_pages, const PlanPtrs& plan,
-                          int n_wg_launch, void* part_o, float* part_ml, hipStream_t s);
-// Rows [B][128][576] (bf16) rearranged into the query-tile layout.
+// q_log2e: the tiles carry kQTileLog2e (as absorb_v2 writes them); else they
+// are a caller's rows rearranged (pack_query_tiles).
+hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, bool q_log2e, const void* cache,
+                          int num_pages, const int32_t* page_table, int max_pages,
+                          const PlanPtrs& plan, int n_wg_launch, void* part_o, float* part_ml,
+                          hipStream_t s);
+// Rows [B][128][576] (bf16) rearranged into the query-tile layout (values
+// unchanged).
 hipError_t pack_query_tiles(const void* rows, int B, void* tiles, hipStream_t s);
 // (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
 //  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
@@ -242,7 +249,8 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i and q_abs[b][i][512:576] =
 // scale * RoPE(q^R_i) (V2 geometry, bf16; W_UK row-major or tiled); q_tiled:
-// written in the query-tile layout (qtile_index) instead of rows.
+// written in the query-tile layout (qtile_index, times kQTileLog2e) instead
+// of rows.
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
                      bool q_tiled, float scale, const float* q_r, const int32_t* positions,
                      const float* rope, int rope_len, hipStream_t s);
