@@ -114,7 +114,9 @@ void carve_attn(Carver& c, const Geo& g, int B, int num_splits, AttnWs* w, bool 
   w->max_wg = pd.max_wg;
   w->plan = c.take(plan_bytes(B, num_splits));
   w->q_tiles = (q_rows && is_v2_fast(g)) ? c.take((size_t)B * g.n_h * g.row * g.esize()) : nullptr;
-  w->part_o = (float*)c.take(sizeof(float) * (size_t)pd.max_segs * g.n_h * g.d_c);
+  // partial o~ per segment: bf16 on the MFMA path, fp32 on the generic one
+  const size_t part_elem = is_v2_fast(g) ? 2 : sizeof(float);
+  w->part_o = (float*)c.take(part_elem * (size_t)pd.max_segs * g.n_h * g.d_c);
   w->part_ml = (float*)c.take(sizeof(float) * 2 * (size_t)pd.max_segs * g.n_h);
 }
 
