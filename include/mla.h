@@ -52,7 +52,8 @@ typedef enum {
   MLA_ERR_INVALID_ARG = -1,  /* null pointer, bad size or shape */
   MLA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
   MLA_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small */
-  MLA_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+  MLA_ERR_HIP = -4,          /* a HIP launch or runtime call failed */
+  MLA_ERR_SCRATCH_LIMIT = -5 /* mla_decode_noalloc: needs more than its fixed buffer */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
@@ -172,6 +173,25 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
                const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
                int max_kv_len, const float* rope_table, int rope_len, int num_splits,
                void* workspace, size_t ws_bytes, void* out, void* stream);
+
+/* mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, arguments and results, with the workspace taken from a fixed
+ * 64 MiB device array that the library holds on each GPU it runs on until
+ * the process ends (mla_decode's workspace at batch 64 with automatic
+ * splits is 57.3 MiB at the DeepSeek-V2 shape).  It allocates nothing and
+ * frees nothing; a request whose workspace (mla_workspace_size with
+ * MLA_OP_DECODE) exceeds 64 MiB returns MLA_ERR_SCRATCH_LIMIT before any HIP
+ * call.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (no part of it needs to start at zero): calls that overlap
+ * on one GPU - on two streams, or from two host threads - race; serialise
+ * them.  The first call on a device looks the array's address up once with
+ * that device current. */
+int mla_decode_noalloc(const mla_config* cfg, const mla_weights* w, const void* h,
+                       const int32_t* positions, const void* kv_cache, int num_pages,
+                       const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+                       int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+                       void* out, void* stream);
 
 /* Decode steps 1-3 of mla_decode ([formulas] eq. (12), (13); [walkthrough]
  * step 3 and §3 顺序 B): q_abs[b][i] = [W_UK,i^T q^C_i | RoPE(q^R_i)] * scale,

@@ -494,6 +494,8 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MLA_ERR_HIP: return "HIP launch or runtime error";
+    case MLA_ERR_SCRATCH_LIMIT:
+      return "the step needs more scratch than mla_decode_noalloc's fixed device buffer";
     default: return "unknown status";
   }
 }
@@ -702,21 +704,43 @@ int mla_decode_output(const mla_config* cfg, const mla_weights* w, const void* l
   return run_output(g, w, latent_out, B, workspace, out, (hipStream_t)stream);
 }
 
+}  // extern "C"
+
+// Host-side argument checks of mla_decode (no HIP call); MLA_OK, with *need
+// the workspace bytes, when the arguments describe a launchable step.
+int mla::decode_args_status(const mla_config* cfg, const mla_weights* w, const void* h,
+                            const int32_t* positions, const void* kv_cache, int num_pages,
+                            const int32_t* page_table, int max_pages, const int32_t* kv_lens,
+                            int B, int max_kv_len, const float* rope_table, int rope_len,
+                            int num_splits, const void* out, size_t* need) {
+  Geo g;
+  if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, false) || rope_len < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (int lr = layout_status(g, w)) return lr;
+  // h stands in for the (not yet computed) absorbed query in the checks
+  int r = check_attn_args(g, h, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
+                          num_splits);
+  if (r) return r;
+  if (B > 0 && (!h || !positions || !rope_table || rope_len == 0 || !out))
+    return MLA_ERR_INVALID_ARG;
+  *need = B > 0 ? ws_decode(g, B, num_splits) : 0;
+  return MLA_OK;
+}
+
+extern "C" {
+
 int mla_decode(const mla_config* cfg, const mla_weights* w, const void* h,
                const int32_t* positions, const void* kv_cache, int num_pages,
                const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
                int max_kv_len, const float* rope_table, int rope_len, int num_splits,
                void* workspace, size_t ws_bytes, void* out, void* stream) {
-  Geo g;
-  if (!resolve(cfg, &g) || !weights_ok(w, true, true, false, false) || rope_len < 0)
-    return MLA_ERR_INVALID_ARG;
-  if (int lr = layout_status(g, w)) return lr;
-  // q_abs stands in for the (not yet computed) absorbed query in the checks
-  int r = check_attn_args(g, h, kv_cache, num_pages, page_table, max_pages, kv_lens, B, max_kv_len,
-                          num_splits);
+  size_t need = 0;
+  int r = decode_args_status(cfg, w, h, positions, kv_cache, num_pages, page_table, max_pages,
+                             kv_lens, B, max_kv_len, rope_table, rope_len, num_splits, out, &need);
   if (r || B == 0) return r;
-  if (!h || !positions || !rope_table || rope_len == 0 || !out) return MLA_ERR_INVALID_ARG;
-  r = check_ws(workspace, ws_bytes, ws_decode(g, B, num_splits));
+  Geo g;
+  resolve(cfg, &g);
+  r = check_ws(workspace, ws_bytes, need);
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   Carver c(workspace);

@@ -254,6 +254,13 @@ hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stri
 hipError_t absorb_v2(int M, const void* qc, const void* W_UK, bool w_tiled, void* q_abs,
                      bool q_tiled, float scale, const float* q_r, const int32_t* positions,
                      const float* rope, int rope_len, hipStream_t s);
+// Host-side argument checks of mla_decode; *need = its workspace bytes.
+int decode_args_status(const mla_config* cfg, const mla_weights* w, const void* h,
+                       const int32_t* positions, const void* kv_cache, int num_pages,
+                       const int32_t* page_table, int max_pages, const int32_t* kv_lens, int B,
+                       int max_kv_len, const float* rope_table, int rope_len, int num_splits,
+                       const void* out, size_t* need);
+
 // Merge of the register-order partials attn_decode_v2 writes.
 hipError_t combine_decode_v2(const PlanPtrs& plan, int B, int num_splits, const void* part_o,
                              const float* part_ml, void* lat_out, hipStream_t s);

@@ -19,6 +19,7 @@ MLA_ERR_INVALID_ARG = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_WORKSPACE = -3
 MLA_ERR_HIP = -4
+MLA_ERR_SCRATCH_LIMIT = -5
 
 MLA_F32 = 0
 MLA_BF16 = 1
@@ -77,6 +78,8 @@ _SIGS = {
     "mla_append_kv": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, _P, c_size_t, _P]),
     "mla_decode": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, _P, c_int,
                            c_int, _P, c_size_t, _P, _P]),
+    "mla_decode_noalloc": (c_int, [_P, _P, _P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, _P,
+                                   c_int, c_int, _P, _P]),
     "mla_decode_query": (c_int, [_P, _P, _P, _P, c_int, _P, c_int, _P, c_size_t, _P, _P]),
     "mla_decode_attention": (c_int, [_P, _P, _P, c_int, _P, c_int, _P, c_int, c_int, c_int, _P,
                                      c_size_t, _P, _P]),
@@ -195,6 +198,16 @@ def decode(cfg, weights, h, positions, kv_cache, page_table, kv_lens, max_kv_len
         ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), _ptr(positions), _ptr(kv_cache),
         kv_cache.shape[0], _ptr(page_table), page_table.shape[1], _ptr(kv_lens), h.shape[0],
         max_kv_len, _ptr(rope_table), rope_table.shape[0], num_splits, wp, wn, _ptr(out),
+        _stream(stream)))
+
+
+def decode_noalloc(cfg, weights, h, positions, kv_cache, page_table, kv_lens, max_kv_len,
+                   rope_table, num_splits, out, stream=None):
+    """mla_decode with the library's fixed device scratch array (no workspace)."""
+    _check("mla_decode_noalloc", load().mla_decode_noalloc(
+        ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), _ptr(positions), _ptr(kv_cache),
+        kv_cache.shape[0], _ptr(page_table), page_table.shape[1], _ptr(kv_lens), h.shape[0],
+        max_kv_len, _ptr(rope_table), rope_table.shape[0], num_splits, _ptr(out),
         _stream(stream)))
 
 

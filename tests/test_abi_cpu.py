@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4):
-        assert lib.status_string(code)
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.status_string(code) and lib.status_string(code) != "unknown status"
     assert lib.status_string(7) == "unknown status"
     assert L.mla_version() >= 100
 
@@ -213,3 +213,27 @@ def test_backward_and_mha_reject_bad_arguments(L):
               ctypes.c_float(0.0), 0, p, 1 << 40, p, None) == lib.MLA_ERR_INVALID_ARG
     assert mh(ctypes.byref(c), p, p, 4, p, 2, p, 1, 100, ctypes.c_float(0.0), 0, p, 16, p,
               None) == lib.MLA_ERR_WORKSPACE
+
+
+def test_decode_noalloc_host_checks(L):
+    """mla_decode_noalloc validates its arguments and its scratch limit on the
+    host before any HIP call (this runs without a GPU)."""
+    c = _cfg()
+    p = ctypes.c_void_p(4096)
+    z = ctypes.c_void_p(0)
+    wf = lib.Weights(*([4096] * 8))
+    wn = lib.Weights(*([None] * 8))
+    # null weights, missing output
+    assert L.mla_decode_noalloc(ctypes.byref(c), ctypes.byref(wn), p, p, p, 300, p, 129, p, 4,
+                                8193, p, 8194, 0, p, None) == lib.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_noalloc(ctypes.byref(c), ctypes.byref(wf), p, p, p, 300, p, 129, p, 4,
+                                8193, p, 8194, 0, z, None) == lib.MLA_ERR_INVALID_ARG
+    # batch 128 with automatic splits needs more than the 64 MiB array
+    need = lib.workspace_size(c, lib.OP_DECODE, 128, 8193, 0)
+    assert need > 64 << 20
+    assert L.mla_decode_noalloc(ctypes.byref(c), ctypes.byref(wf), p, p, p, 300, p, 129, p, 128,
+                                8193, p, 8194, 0, p, None) == lib.MLA_ERR_SCRATCH_LIMIT
+    # batch 64 fits (the call would launch: not made here); an empty batch is a no-op
+    assert lib.workspace_size(c, lib.OP_DECODE, 64, 8193, 0) <= 64 << 20
+    assert L.mla_decode_noalloc(ctypes.byref(c), ctypes.byref(wf), p, p, p, 300, p, 129, p, 0,
+                                8193, p, 8194, 0, p, None) == lib.MLA_OK
