@@ -16,13 +16,14 @@
 //    their softmax numerators P through LDS, so each wave reads only its
 //    quarter of the latent tile for the second contraction.
 //  * with one wave per SIMD the instruction stream sets the pace: beside each
-//    32-cycle MFMA there is room for about two other instructions before the
+//    32-cycle MFMA there is room for about four other instructions before the
 //    MFMA pipe idles.  So every LDS read is a per-lane base register plus an
-//    immediate offset (eight bases for the score reads, two for the
-//    accumulation reads, moved with the ring slot once per sub-tile), the
+//    immediate offset (one XOR-derived base per four score reads, two for
+//    the accumulation reads, moved with the ring slot once per sub-tile), the
 //    cache operand of the second contraction comes straight from
-//    ds_read_b64_tr_b16 (no register shuffles), and the softmax is a max,
-//    an exp2 and a pack per score.
+//    ds_read_b64_tr_b16 (no register shuffles), the softmax is an exp2 and a
+//    pack per score in one branch-free block beside the accumulation MFMAs,
+//    and the ring refill between sub-tiles is a short run of scalar selects.
 //  * 32-token sub-tiles stream through a four-slot LDS ring with 16-byte
 //    direct-to-LDS buffer loads, two sub-tiles in flight while the scores of
 //    sub-tile j and the accumulation of sub-tile j-1 run.  A slot holds the
@@ -30,7 +31,9 @@
 //    16-byte pieces are XOR-permuted per row so that every LDS read pattern
 //    below is free of bank conflicts, and each ring load covers exactly one
 //    row's latent part (or the RoPE parts of eight rows), which keeps its
-//    address arithmetic to one or two instructions.
+//    address arithmetic to one or two instructions.  A descriptor's range is
+//    the sub-tile's valid rows, so a partial sub-tile needs no clamping: the
+//    rows past it arrive as zeros.
 //  * scores: S^T[token][head] = C[token][dims] . Q~^T[dims][head] with
 //    v_mfma_f32_32x32x16_bf16 (A = cache rows from LDS, B = Q~), 36 K-steps.
 //    The absorption writes query tiles that carry a factor log2(e), so the
@@ -41,12 +44,13 @@
 //    the 256-register accumulator is never rescaled.  Each head's maximum is
 //    tracked; if any head of the work-group ends a segment with its maximum
 //    outside [-64, 64], the whole segment is redone once with each head's
-//    maximum as the reference (numerators <= 1): every wave ORs its 32
-//    heads' flags into one vote, and the work-group ORs the four votes.
+//    maximum as the reference (numerators <= 1): after the segment every
+//    wave ORs its 32 heads' flags into one vote, and the work-group ORs the
+//    four votes through LDS.
 //  * latent accumulation: o~^T[dims][head] += C^T[dims][tokens] . P^T.  The
 //    token order inside a sub-tile is chosen so that the score registers are
 //    P^T's operand as they stand, and each transposing read fetches four
-//    tokens two rows apart (conflict-free under the XOR permutation).
+//    tokens four rows apart (conflict-free under the XOR permutation).
 //  * the MFMA stream of an iteration interleaves the 36 score steps with the
 //    32 accumulation steps and the ring refill; sched_barrier pins the order.
 //  * a work-group walks the segments the plan assigns to it and writes each
@@ -173,9 +177,11 @@ __device__ inline void lds_store(int byte, T v) {
 }
 
 // One 32-token sub-tile in flight: rows [0, 32) of a page run starting at
-// the descriptor's base go to LDS slot `slot`.  Rows at or past nvalid
-// (rmax = nvalid - 1) re-read row rmax: their scores are masked to zero
-// weight and the data stays finite, so 0 * row never turns into NaN.  Wave w
+// the descriptor's base go to LDS slot `slot`.  The descriptor's range covers
+// the sub-tile's nvalid rows only: a lane whose row lies at or past nvalid is
+// out of range, reads no memory and writes zeros to LDS (gfx950 range-checks
+// the whole offset, soffset included), so those rows hold zeros, whose
+// scores are masked to zero weight (0 * 0 never turns into NaN).  Wave w
 // moves rows [8w, 8w+8): loads 0..7 the latent part of one row each, load 8
 // the RoPE parts of all eight.  Every wave issues exactly kInstsPerWave loads
 // per sub-tile whatever nvalid is; the ring's vmcnt bookkeeping relies on it.
@@ -190,39 +196,37 @@ __device__ inline void lds_store(int byte, T v) {
 // load is ever left in flight.)
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct Refill {
-  i32x4 rs;   // buffer descriptor (base, num_records) in scalar registers
+  i32x4 rs;   // buffer descriptor (base, valid bytes) in scalar registers
   int slot;   // LDS byte offset of the ring slot
-  int rmax;
 };
 
-// raw buffer descriptor over [p, p + bytes)
+// raw buffer descriptor over [p, p + bytes) (uniform values; readfirstlane
+// keeps the words scalar where the compiler would hold one in a vector
+// register, which the loads' scalar operand cannot take)
 __device__ inline i32x4 make_rsrc(const void* p, int bytes) {
   const unsigned long long a = (unsigned long long)p;
-  return i32x4{(int)(unsigned)a, (int)((a >> 32) & 0xffffu), bytes, kRsrcWord3};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
 }
 
-__device__ inline void lds_dma16(const i32x4& rs, int voff, int soff, int lds_byte) {
+__device__ inline void lds_dma16(const i32x4& rs, int voff, int lds_byte) {
   const int m0 = __builtin_amdgcn_readfirstlane(
       (int)(uintptr_t)((lds_char*)g_lds + lds_byte));
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rs), "s"(soff), "s"(m0) : "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rs), "s"(m0) : "m0");
 }
 
 // lat16: (lane ^ 8 (w & 1)) << 4, the lane's piece position of row 8w (the
 // XOR permutation of rows 8w + i differs from it by i); rope_off: this lane's
-// source offset in a full sub-tile's RoPE load
+// source offset in the RoPE load (row 8w + lane / 8).  Each offset carries
+// its row, so the range check alone bounds a partial sub-tile.
 __device__ inline void ring_load(const Refill& rf, int i, int wave, int lat16, int rope_off) {
   if (i < 8) {
     const int r = 8 * wave + i;
-    lds_dma16(rf.rs, lat16 ^ (i << 4), min(r, rf.rmax) * kRowBytes, rf.slot + r * kLatBytes);
+    lds_dma16(rf.rs, (lat16 ^ (i << 4)) + r * kRowBytes, rf.slot + r * kLatBytes);
   } else {
-    int off = rope_off;
-    if (rf.rmax < kSub - 1) {   // a partial sub-tile: clamp each lane's row
-      const int lane = lane_here();
-      const int r = 8 * wave + (lane >> 3);
-      off = min(r, rf.rmax) * kRowBytes + kLatBytes + (((lane & 7) ^ swz_rope(r)) << 4);
-    }
-    lds_dma16(rf.rs, off, 0, rf.slot + kRopeOff + 8 * wave * kRopeBytes);
+    lds_dma16(rf.rs, rope_off, rf.slot + kRopeOff + 8 * wave * kRopeBytes);
   }
 }
 
@@ -319,9 +323,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   // slot pos mod 4.  Each computing iteration consumes one position and loads
   // the one two ahead, so near a segment's end the cursor walks into the
   // next segment and that segment's first sub-tiles arrive while this one is
-  // still computed.  Cursor: segment rk (sequence rb), next token rt, end rt1,
-  // rn sub-tiles left, at offset rpo of page rpi, page window wb / pid.
-  int rk = k_begin, rb = 0, rt = 0, rt1 = 0, rn = 0, rpi = 0, rpo = 0, wb = 0, pid = 0;
+  // still computed.  Cursor: sequence rb, rrem tokens left, at byte offset
+  // rpo_b of page rpi, page window wb / pid; seg_bit marks the cursor's
+  // segment in badm.
+  int rb = 0, rrem = 0, rpi = 0, rpo_b = 0, wb = 0, pid = 0;
+  unsigned seg_bit = 0;
   int k = k_begin;      // the segment being computed
   int pid_next = 0;     // window of segment k + 1's first pages (loaded ahead)
   unsigned badm = 0;    // bit s & 31: segment s met a page id out of range
@@ -334,73 +340,76 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   };
   auto cursor_begin = [&](int kk, int w) {
     const Seg sg = seg_at(kk);
-    rk = kk;
+    seg_bit = 1u << (kk & 31);
     rb = sg.b;
-    rt = sg.t0;
-    rt1 = sg.t1;
-    rn = (sg.t1 - sg.t0 + kSub - 1) / kSub;
+    rrem = __builtin_amdgcn_readfirstlane(sg.t1 - sg.t0);   // scalar: a uniform count
     wb = sg.t0 / page;
     rpi = wb;
-    rpo = sg.t0 - wb * page;
+    rpo_b = (sg.t0 - wb * page) * kRowBytes;
     pid = w;
+  };
+  // one sub-tile on: the next page after the last one of a page
+  auto cursor_step = [&]() {
+    rrem -= kSub;
+    const bool wrap = rpo_b + kSub * kRowBytes == page * kRowBytes;
+    rpo_b = wrap ? 0 : rpo_b + kSub * kRowBytes;
+    rpi += wrap ? 1 : 0;
   };
   // the cursor's next sub-tile, for ring position pos (sub-tiles never
   // straddle a page: page is a multiple of 64 and segments start on 64-token
   // boundaries or at 0)
-  auto refill = [&](int pos) {
+  // The cursor's next sub-tile (rrem > 0), for ring position pos: selects
+  // only, no branch but the rare window change.  A page id out of range
+  // gives a descriptor of zero bytes and marks the segment.
+  auto refill_at = [&](int pos) {
+    if (rpi - wb >= 64) {  // next window (segments longer than 64 pages)
+      wb += 64 * ((rpi - wb) >> 6);
+      pid = load_window(rb, wb);
+      // consume here: a page-id load left in flight into the loop would
+      // make the compiler wait for all vector memory operations (vmcnt(0))
+      // before each later page lookup, draining the ring
+      asm volatile("" ::"v"(pid));
+    }
+    const int pg = __builtin_amdgcn_readlane(pid, rpi - wb);
+    const bool ok = (unsigned)pg < (unsigned)num_pages;
+    badm |= ok ? 0u : seg_bit;
+    const unsigned long long off =
+        (unsigned long long)(unsigned)(ok ? pg : 0) * (unsigned)(page * kRowBytes) + (unsigned)rpo_b;
     Refill rf;
     rf.slot = slot_off(pos);
-    if (rn > 0) {
-      if (rpi - wb >= 64) {  // next window (segments longer than 64 pages)
-        wb += 64 * ((rpi - wb) >> 6);
-        pid = load_window(rb, wb);
-        // consume here: a page-id load left in flight into the loop would
-        // make the compiler wait for all vector memory operations (vmcnt(0))
-        // before each later page lookup, draining the ring
-        asm volatile("" ::"v"(pid));
-      }
-      const int pg = __builtin_amdgcn_readlane(pid, rpi - wb);
-      const bool ok = pg >= 0 && pg < num_pages;
-      badm |= (ok ? 0u : 1u) << (rk & 31);
-      const long row0 = ok ? (long)pg * page + rpo : 0;
-      rf.rs = make_rsrc(cache + row0 * kRow, kSubBytes);
-      rf.rmax = ok ? min(kSub, rt1 - rt) - 1 : 0;
-      --rn;
-      rt += kSub;
-      rpo += kSub;
-      if (rpo == page) {
-        rpo = 0;
-        ++rpi;
-      }
-    } else {
-      rf.rs = make_rsrc(cache, 0);
-      rf.rmax = 0;
-    }
+    rf.rs = make_rsrc((const char*)cache + off, ok ? min(kSub, rrem) * kRowBytes : 0);
+    cursor_step();
     return rf;
   };
-  // past the stream, or a position that must stay unloaded: a resource of zero
-  // bytes, so each of its loads is out of range and moves no data.  Issuing
-  // them keeps the count of ring loads per sub-tile fixed, which the vmcnt
-  // immediates below rely on.
+  auto refill = [&](int pos) {
+    if (rrem > 0) return refill_at(pos);
+    Refill rf;
+    rf.slot = slot_off(pos);
+    rf.rs = make_rsrc(cache, 0);
+    return rf;
+  };
   // sub-tile i (0 or 1) of segment k + 1 (descriptor sn), from the window
   // loaded ahead: a segment starts on a 64-token boundary, so both lie in
   // its first page
   auto refill_next = [&](int pos, const Seg& sn, int i) {
     const int pg = __builtin_amdgcn_readfirstlane(pid_next);
-    const bool ok = pg >= 0 && pg < num_pages;
+    const bool ok = (unsigned)pg < (unsigned)num_pages;
     badm |= (ok ? 0u : 1u) << ((k + 1) & 31);
     const long row0 = ok ? (long)pg * page + (sn.t0 % page) + kSub * i : 0;
     Refill rf;
     rf.slot = slot_off(pos);
-    rf.rs = make_rsrc(cache + row0 * kRow, kSubBytes);
-    rf.rmax = ok ? min(kSub, sn.t1 - (sn.t0 + kSub * i)) - 1 : 0;
+    rf.rs = make_rsrc(cache + row0 * kRow,
+                      ok ? min(kSub, sn.t1 - (sn.t0 + kSub * i)) * kRowBytes : 0);
     return rf;
   };
+  // past the stream, or a position that must stay unloaded: a descriptor of
+  // zero bytes, so each of its loads is out of range, reads no memory and
+  // writes zeros.  Issuing them keeps the count of ring loads per sub-tile
+  // fixed, which the vmcnt immediates below rely on.
   auto no_refill = [&](int pos) {
     Refill rf;
     rf.slot = slot_off(pos);
     rf.rs = make_rsrc(cache, 0);
-    rf.rmax = 0;
     return rf;
   };
 
@@ -454,13 +463,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
   // the cursor of a segment whose sub-tiles 0 and 1 the previous one loaded
   auto cursor_after_prefetch = [&]() {
     cursor_begin(k, pid_next);
-    rn -= 2;
-    rt += 2 * kSub;
-    rpo += 2 * kSub;
-    if (rpo == page) {
-      rpo = 0;
-      ++rpi;
-    }
+    cursor_step();
+    cursor_step();
   };
   // work-group start: both descriptors, both page windows and the query in
   // flight together, then the first two sub-tiles (landing behind the query:
@@ -548,7 +552,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       lds_barrier();
       {
         // P buffer 1 reads as the P of sub-tile -1 in iteration 0: zero it
-        const u32x4 z = {};
+        // (the zeros formed here: a constant the compiler keeps for the whole
+        // kernel is spilled, and its reload would wait for the ring's loads)
+        uint32_t z0;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+        const u32x4 z = {z0, z0, z0, z0};
         const int tl = wave * 64 + lane_here();   // formed here, not kept across the loop
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * tl, z);
         lds_store<u32x4>(kPBufOff + kPBufBytes + 16 * (tl + kThreads), z);
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // scalar set-up of the ring loads (issued below), ahead of the waits
         Refill rf;
         if (j + 2 < nsub)
-          rf = refill(base + j + 2);
+          rf = refill_at(base + j + 2);
         else if (pf_next)
           rf = refill_next(base + j + 2, nxt, j + 2 - nsub);
         else
@@ -598,12 +606,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
         // region r < 32 runs latent K-step 8 (r & 3) + (r >> 2) (b-major),
         // regions 32..35 the RoPE K-steps
         auto ks_of = [](int r) { return r < 32 ? 8 * (r & 3) + (r >> 2) : r; };
+        // the four reads of one b share one XOR-derived base, formed at the
+        // first of them
+        int xq = qb;
         auto a_read = [&](auto rc) {
           constexpr int r = decltype(rc)::value;
-          if constexpr (r < 32)
-            return lds_load<bf16x8>(xor_here<32 * (r >> 2)>(qb) + 256 * (r & 3));
-          else
+          if constexpr (r < 32) {
+            if constexpr ((r & 3) == 0) xq = xor_here<32 * (r >> 2)>(qb);
+            return lds_load<bf16x8>(xq + 256 * (r & 3));
+          } else {
             return lds_load<bf16x8>(xor_here<(r - 32) << 5>(qrb));
+          }
         };
         abuf[0] = a_read(ic<0>{});
         abuf[1] = a_read(ic<1>{});
@@ -644,11 +657,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           }
           __builtin_amdgcn_sched_barrier(0);
         });
+        // ---- the rest of j-1's accumulation (K-step 1) with the softmax
+        // numerators of sub-tile j in its shadow.  Accumulation region idx
+        // runs head block idx / 4, dims block idx % 4.  The first two do not
+        // read S: they cover the wait for the last score MFMA's result.
+        auto tail_mfma = [&](int idx) {
+          const int n = idx >> 2, mb = idx & 3;
+          if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
+          pv_mfma(mb, n);
+        };
+        tail_mfma(0);
+        tail_mfma(1);
+        __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
+        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- softmax numerators of sub-tile j (log2 domain), lane = head, 16
-        // of the 32 tokens; overlaps the rest of j-1's accumulation.  Register
-        // i holds token 16 (i >> 3) + 4 (i & 3) + 2 ((i >> 2) & 1) + h.
+        // Register i of lane (head, h) holds token 16 (i >> 3) + 4 (i & 3) +
+        // 2 ((i >> 2) & 1) + h.  Uniform branches, both rare (a segment's
+        // last, partial sub-tile; a redo pass), ahead of the block below so
+        // that it stays one basic block.
         if (nvalid < kSub) {
           const int hh = lane_here() >> 5;
 #pragma unroll
@@ -657,20 +684,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
             S[i] = tok < nvalid ? S[i] : -INFINITY;
           }
         }
-        float bm;
-        {
-          float mx[5];
-#pragma unroll
-          for (int i = 0; i < 5; ++i) mx[i] = fmaxf(fmaxf(S[3 * i], S[3 * i + 1]), S[3 * i + 2]);
-          bm = fmaxf(fmaxf(mx[0], mx[1]), mx[2]);
-          bm = fmaxf(fmaxf(bm, mx[3]), fmaxf(mx[4], S[15]));
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
-                                                           false, false);
-          bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-          if constexpr (!kQLog2e) bm *= kLog2e;
-        }
-        m_seen = fmaxf(m_seen, bm);
         if constexpr (kQLog2e) {
+          // a redo pass's reference (its maxima are not used)
           if (mode != 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) S[i] -= m_ref;
@@ -683,64 +698,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           else
             return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -m_ref));
         };
-        // the numerators beside the first eight accumulation MFMAs, their
-        // LDS write beside the last eight (which hides its latency before
-        // the next barrier)
-#pragma unroll
-        for (int idx = 0; idx < 8; ++idx) {
-          const int n = idx >> 2, mb = idx & 3;
-          if (mb == 0) B[(n + 1) & 1] = p_read(1, n + 1);
-          pv_mfma(mb, n);
-          S[2 * idx] = num(S[2 * idx]);
-          S[2 * idx + 1] = num(S[2 * idx + 1]);
-        }
-        // P of sub-tile j (B operand layout: lane = head, 8 tokens per K-step
-        // half) for all four waves.  The last sub-tile of a first pass
-        // carries the wave's redo vote in the sign bit of lane 0's first
-        // number: the numerators are never negative, and a redo discards
-        // everything they feed.  m_seen is per head (per lane), so the vote
-        // is the OR over the wave's 64 lanes: any of its 32 heads may need
-        // the redo.
-        const bool vote = mode == 0 && j == nsub - 1 &&
-                          __builtin_amdgcn_ballot_w64(!(fabsf(m_seen) <= kLazy)) != 0;
+        // Regions 2..15: the head maximum (for the pass's redo test), two
+        // numerators per region from region 3, their bf16 rounding and LDS
+        // write once eight are done, and the l sums over the rounded values.
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float mx[5], l_part = 0.f;
         bf16x8 p[2];
+        static_for<2, 16>([&](auto ic_) {
+          constexpr int idx = decltype(ic_)::value;
+          if constexpr (idx == 2) {
 #pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[kap][e] = (__bf16)S[8 * kap + e];
-          if (kap == 0 && vote) {   // uniform: taken once per pass at most
-            u32x4 pb = __builtin_bit_cast(u32x4, p[0]);
-            pb[0] |= lane_here() == 0 ? 0x8000u : 0u;
-            p[0] = __builtin_bit_cast(bf16x8, pb);
+            for (int i = 0; i < 5; ++i) mx[i] = fmaxf(fmaxf(S[3 * i], S[3 * i + 1]), S[3 * i + 2]);
           }
-          lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024, p[kap]);
-        }
+          if constexpr (idx == 3) {
+            float bm = fmaxf(fmaxf(mx[0], mx[1]), mx[2]);
+            bm = fmaxf(fmaxf(bm, mx[3]), fmaxf(mx[4], S[15]));
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm),
+                                                             __float_as_uint(bm), false, false);
+            bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            if constexpr (!kQLog2e) bm *= kLog2e;
+            m_seen = fmaxf(m_seen, bm);
+          }
+          if constexpr (idx >= 3 && idx < 11) {
+            constexpr int e = 2 * (idx - 3);
+            S[e] = num(S[e]);
+            S[e + 1] = num(S[e + 1]);
+          }
+          // P of sub-tile j (B operand layout: lane = head, 8 tokens per
+          // K-step half) for all four waves, and l over the rounded numbers
+          // the accumulation uses (pairs of bf16 dotted with (1, 1))
+          if constexpr (idx == 7 || idx == 11) {
+            constexpr int kap = idx == 7 ? 0 : 1;
 #pragma unroll
-        for (int idx = 8; idx < 16; ++idx) {
-          const int n = idx >> 2, mb = idx & 3;
-          if (mb == 0 && n < 3) B[(n + 1) & 1] = p_read(1, n + 1);
-          pv_mfma(mb, n);
-        }
-        {
-          // l over the rounded numerators the accumulation uses: pairs of
-          // bf16 dotted with (1, 1) into fp32 (the vote bit, if set, makes
-          // l negative; a redo discards it)
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-          float s0 = l_run, s1 = 0.f;
-          static_for<0, 4>([&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            s0 = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_shufflevector(p[0], p[0], 2 * e, 2 * e + 1), one, s0, false);
-            s1 = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_shufflevector(p[1], p[1], 2 * e, 2 * e + 1), one, s1, false);
-          });
-          l_run = s0 + s1;
-        }
+            for (int e = 0; e < 8; ++e) p[kap][e] = (__bf16)S[8 * kap + e];
+            lds_store<bf16x8>(pwr + (2 * wave + kap) * 1024, p[kap]);
+          }
+          if constexpr (idx == 8 || idx == 12) {
+            constexpr int kap = idx == 8 ? 0 : 1;
+            static_for<0, 4>([&](auto ec) {
+              constexpr int e = decltype(ec)::value;
+              l_part = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_shufflevector(p[kap], p[kap], 2 * e, 2 * e + 1), one, l_part, false);
+            });
+          }
+          if constexpr (idx == 13) l_run += l_part;
+          tail_mfma(idx);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       // ---- drain: the latent accumulation of the last sub-tile.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_barrier();  // P of the last sub-tile (with the votes) is visible
+      lds_barrier();  // P of the last sub-tile is visible
       {
         const int dv = (((base + nsub - 1) & (kSlots - 1)) - slot_cur) * kSubBytes;
         const int prd = pl + kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
@@ -764,19 +773,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           __builtin_amdgcn_sched_barrier(0);
         });
       }
-      // a head maximum outside [-64, 64] anywhere in the work-group (a vote
-      // in the P of the last sub-tile, visible since the drain's barrier):
-      // redo the segment with the exact maxima seen in this pass (rare).  The
-      // redo starts at the ring position after this pass, behind the loads
-      // in flight there (same slots, issued earlier by the same wave, so they
-      // land earlier).
+      // A head maximum outside [-64, 64] anywhere in the work-group: redo
+      // the segment with the exact maxima seen in this pass (rare).  Each
+      // wave votes for its 32 heads (m_seen is per head, so the OR over its
+      // lanes) in P buffer nsub & 1, which no wave reads after the drain's
+      // barrier (its last reader was iteration nsub - 1).  The redo starts at
+      // the ring position after this pass, behind the loads in flight there
+      // (same slots, issued earlier by the same wave, so they land earlier).
       if (mode == 0) {
-        const int pv = kPBufOff + ((nsub + 1) & 1) * kPBufBytes;
-        uint32_t v = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) v |= lds_load<uint32_t>(pv + 2 * w * 1024);
-        // the same word in every lane: a uniform decision
-        if (__builtin_amdgcn_readfirstlane(v) & 0x8000u) {
+        const int pv = kPBufOff + (nsub & 1) * kPBufBytes;
+        const bool mine = __builtin_amdgcn_ballot_w64(!(fabsf(m_seen) <= kLazy)) != 0;
+        if (lane_here() == 0) lds_store<uint32_t>(pv + 4 * wave, mine ? 1u : 0u);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        const u32x4 votes = lds_load<u32x4>(pv);
+        // the same words in every lane: a uniform decision
+        if (__builtin_amdgcn_readfirstlane(votes[0] | votes[1] | votes[2] | votes[3]) != 0) {
           m_ref = m_seen;
           mode = 1;
           base += nsub;
