@@ -903,6 +903,26 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
     for (int e = t; e < 32 * kDc; e += 512) out[e] = (__bf16)__builtin_nanf("");
     return;
   }
+  // thread t takes lane tt & 63 of the attention kernel's wave wo = tt >> 6,
+  // whose accumulators x = 4 mb + n hold latent dims [128 wo, 128 wo + 128);
+  // the two halves of the work-group sum the even and the odd segments, four
+  // segments' loads in flight per half at once
+  constexpr int kU = 4;
+  uint2 v[kU][16];
+  auto load_round = [&](int c0, int s0, int nc) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + 2 * u >= nc) break;
+      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s0 + 2 * u) * kHeads * kDc) + tt;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) v[u][4 * mb + a] = src[((4 * mb + n) * 4 + a) * kThreads];
+    }
+  };
+  // the first round's partials go out before the softmax statistics, which
+  // they do not depend on: their memory round trip overlaps that of (m, l)
+  load_round(0, half, min(kCombSegs, cnt));
   // (m, l) of every segment of the head group: one parallel load into LDS
   // when they fit (else read in the loops below)
   const bool in_lds = cnt <= kCombSegs;
@@ -928,9 +948,6 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
     s_inv[t] = 1.f / L;
   }
   __syncthreads();
-  // thread t takes lane tt & 63 of the attention kernel's wave wo = tt >> 6,
-  // whose accumulators x = 4 mb + n hold latent dims [128 wo, 128 wo + 128);
-  // the two halves of the work-group sum the even and the odd segments
   const int lane = tt & 63, wo = tt >> 6;
   const int hd_l = lane & 31;
   f32x4 acc[16];   // [4 mb + a]
@@ -944,21 +961,9 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
       w[s][hh] = __expf(ml_of(c0 + s, hh).x - s_M[hh]) * s_inv[hh];
     }
     __syncthreads();
-    // four segments' loads in flight per half at once; each half sums its
-    // segments in order
-    constexpr int kU = 4;
+    // each half sums its segments in order
     for (int s0 = half; s0 < nc; s0 += 2 * kU) {
-      uint2 v[kU][16];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (s0 + 2 * u >= nc) break;
-        const uint2* src =
-            (const uint2*)(part_o + (long)(k0 + c0 + s0 + 2 * u) * kHeads * kDc) + tt;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int a = 0; a < 4; ++a) v[u][4 * mb + a] = src[((4 * mb + n) * 4 + a) * kThreads];
-      }
+      if (c0 > 0 || s0 != half) load_round(c0, s0, nc);
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         if (s0 + 2 * u >= nc) break;

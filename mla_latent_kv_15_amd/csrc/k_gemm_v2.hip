@@ -135,8 +135,13 @@ __device__ __forceinline__ void wgemm_wg(const int bx, const int by, MLA_WGEMM_P
     // flight waits for it
     __builtin_amdgcn_sched_barrier(0);
   };
+  // one K-step after the other: interleaved, waiting for step 0's operands
+  // would also wait for parts of the later steps
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(d, d);
+  for (int d = 0; d < DEPTH; ++d) {
+    load(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (NS > 0) {
     // straight-line code: the compiler waits for exactly the step it needs
 #pragma unroll
@@ -282,22 +287,22 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
   const int nmb = min(4, (M - m0 + 15) >> 4);
   const int c0 = 256 * ch + 64 * wave + 4 * r16;
   // RoPE part, rows 32 ch .. 32 ch + 31 of the block: row m, rotation pair k
-  // of q^R_i (NaN for a position outside the table); four per thread, loaded
-  // before everything else and stored last
+  // of q^R_i (NaN for a position outside the table); four per thread, stored
+  // last.  The positions and q^R go out together first; the table entries
+  // the positions select go out behind the W_UK loads (a position's load and
+  // its table entry's load back to back would cost a memory round trip each).
   constexpr int kPer = 32 * 32 / 256;
   float2 x[kPer], cs[kPer];
-  int mm[kPer];
+  int mm[kPer], pos[kPer];
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
     const int e = threadIdx.x + 256 * it;
     const int m = min(m0 + 32 * ch + (e >> 5), M - 1), k = e & 31;
     mm[it] = m0 + 32 * ch + (e >> 5);
     x[it] = *(const float2*)(q_r + ((long)m * 128 + head) * 64 + 2 * k);
-    const int pos = positions[m];
-    const bool ok = pos >= 0 && pos < rope_len;
-    cs[it] = *(const float2*)(rope + ((long)(ok ? pos : 0) * 32 + k) * 2);
-    if (!ok) cs[it] = float2{__builtin_nanf(""), __builtin_nanf("")};
+    pos[it] = positions[m];
   }
+  __builtin_amdgcn_sched_barrier(0);
   // row d of W_UK,i, columns c0 .. c0 + 3
   const __bf16* wh = W_UK + (long)head * 128 * 512;
   auto wrow = [&](int d) -> const u32x2* {
@@ -317,6 +322,14 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
       const int m = min(m0 + mb * 16 + r16, M - 1);
       a[ks][mb] = *(const bf16x8*)(qc + (long)m * 16384 + head * 128 + 32 * ks + 8 * g);
     }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int k = (threadIdx.x + 256 * it) & 31;
+    const bool ok = pos[it] >= 0 && pos[it] < rope_len;
+    cs[it] = *(const float2*)(rope + ((long)(ok ? pos[it] : 0) * 32 + k) * 2);
+    if (!ok) cs[it] = float2{__builtin_nanf(""), __builtin_nanf("")};
+  }
   f32x4 acc[4][4];   // [mb][j]
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
