@@ -80,7 +80,9 @@ typedef struct mla_config {
   int d_cq;           /* query latent dim */
   int d_r;            /* decoupled RoPE dim (cached once per token), even */
   int page_size;      /* tokens per cache page */
-  mla_dtype dtype;    /* storage dtype of weights, activations and cache */
+  int dtype;          /* an mla_dtype: storage dtype of weights, activations and
+                         cache (a plain int, so that any value a caller passes
+                         reaches the library's check as a value) */
   float softmax_scale;/* <= 0 selects 1/sqrt(d_h + d_r) */
   double rope_base;   /* <= 0 selects 10000 */
 } mla_config;

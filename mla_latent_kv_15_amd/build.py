@@ -140,5 +140,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# The host code (the C ABI and its argument checks, mla_api.cpp) under
+# AddressSanitizer and UndefinedBehaviorSanitizer, linked with the kernels'
+# ordinary objects.  Host-only flags: device code is never built with them.
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libmla_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of the toolchain's clang (to preload into an
+    uninstrumented interpreter)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin",
+                         "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return path
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """libmla with mla_api.cpp compiled under ASan + UBSan (into _build/san)."""
+    host_src = os.path.join(CSRC, "mla_api.cpp")
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD, os.path.basename(p) + ".o") for p in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    san_obj = os.path.join(SAN_DIR, "mla_api.cpp.o")
+    cmd = [HIPCC, *CFLAGS, *SAN_FLAGS, "-c", host_src, "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB, *objs, san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB} (host code under ASan + UBSan)", file=sys.stderr)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    build_sanitized() if "--sanitized" in sys.argv else build()

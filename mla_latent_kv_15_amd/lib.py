@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# the in-tree build, or another build of the same library named by MLA_LIBRARY
+# (the sanitized host build, for instance)
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = -1
