@@ -33,6 +33,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) v4bf16 lds_v4bf16;
 
 constexpr int kH = 128;    // heads
 constexpr int kW = 192;    // query and key width
@@ -52,14 +55,17 @@ __device__ inline uint32_t pack2(float x, float y) {
 // n = c, rows 8 (r >> 2) + 4h + (r & 3) for r = 0 .. 15.
 //
 // A work-group of four waves takes 128 consecutive queries of one head; its
-// threads stage each block of 32 keys in LDS once for all four waves (K as
-// rows, V transposed to [dim][key]), double-buffered with one barrier per
-// block.  Rows are padded by 16 bytes to spread the banks.
+// threads stage each block of 32 keys in LDS once for all four waves (K and V
+// as rows, 16-byte stores), double-buffered with one barrier per block.  The
+// V^T operand of the second product comes from transposing LDS reads
+// (ds_read_b64_tr_b16).  K rows are padded by 16 bytes to spread the banks;
+// V rows by 64 bytes, so that the four rows one transposing read serves to
+// 32 lanes at once start 64 banks apart.
 constexpr int kWQ = 4;                       // waves (query blocks) per work-group
 constexpr int kKRow = kW + 8;                // LDS K row: 192 + 8 bf16
-constexpr int kVRow = kKB + 8;               // LDS V^T row: 32 + 8 bf16
+constexpr int kVRow = kDv + 32;              // LDS V row: 128 + 32 bf16
 constexpr int kKElems = kKB * kKRow;         // 6400
-constexpr int kBufElems = kKElems + kDv * kVRow;   // + 5120
+constexpr int kBufElems = kKElems + kKB * kVRow;   // + 5120
 constexpr int kKPieces = kKB * kW / 8;       // 768 16-byte pieces of a K block
 constexpr int kVPieces = kKB * kDv / 8;      // 512 of a V block
 
@@ -113,11 +119,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const int p = tid + 256 * r, key = p / (kW / 8), pc = p % (kW / 8);
     *(uint4*)(K + key * kKRow + 8 * pc) = x;
   };
-  auto vstore = [&](__bf16* VT, int r, uint4 x) {
+  auto vstore = [&](__bf16* V, int r, uint4 x) {
     const int p = tid + 256 * r, key = p / (kDv / 8), pc = p % (kDv / 8);
-    const bf16x8 v = __builtin_bit_cast(bf16x8, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) VT[(8 * pc + e) * kVRow + key] = v[e];
+    *(uint4*)(V + key * kVRow + 8 * pc) = x;
   };
   auto lstore = [&](int buf) {
     __bf16* K = lds[buf];
@@ -126,6 +130,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     kstore(K, 2, k2r);
     vstore(K + kKElems, 0, v0r);
     vstore(K + kKElems, 1, v1r);
+  };
+
+  // The V^T operand of dim tile d, K-step kap (keys 16 kap + 8h .. + 7 of dim
+  // 32 d + c for lane (c, h)) by two transposing reads of four keys each.
+  // In each 16-lane group, lane s supplies the 8-byte chunk of row
+  // k0 + s / 4, dims D0 + 4 (s % 4) .. + 3, and output lane i receives, as
+  // its element r, element i % 4 of lane 4 r + i / 4's chunk: dim D0 + i of
+  // row k0 + r.  Byte offset of this lane's chunk in buffer 0, at d = kap = 0:
+  const int vt_base = 2 * (kKElems + (8 * h + ((lane & 15) >> 2)) * kVRow +
+                           16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto vt_read = [&](int buf, int kap, int d) {
+    const int b = buf * 2 * kBufElems + vt_base + 2 * (16 * kap * kVRow + 32 * d);
+    const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_v4bf16*)((lds_char*)lds + b));
+    const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_v4bf16*)((lds_char*)lds + b + 2 * 4 * kVRow));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   f32x16 acc[kDv / 32];   // O^T, dims 32 d .. 32 d + 31 x the wave's 32 queries
@@ -141,7 +162,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + 1 < nkb) gload(kb + 1);   // in flight during this block's products
     const __bf16* K = lds[kb & 1];
-    const __bf16* VT = K + kKElems;
     const int j0 = kb * kKB;
     if (j0 <= far) {   // the wave has a query that sees a key of this block
       // S^T = K . Q^T
@@ -204,9 +224,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
         for (int d = 0; d < kDv / 32; ++d)
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *(const bf16x8*)(VT + (32 * d + c) * kVRow + 16 * kap + 8 * h), pb[kap], acc[d], 0,
-              0, 0);
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_read(kb & 1, kap, d), pb[kap],
+                                                           acc[d], 0, 0, 0);
     }
     if (kb + 1 < nkb) lstore((kb + 1) & 1);   // that buffer was last read in block kb - 1
     __syncthreads();
