@@ -299,10 +299,19 @@ int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* k
  * scaled; scale = cfg->softmax_scale or 1/sqrt(d_h+d_r)); dO: device fp32
  * [T][n_h][d_h]; positions: device int32 [T]; cache and page_table as
  * mla_prefill; W_UK, W_UV from w in either layout; outputs device fp32.
- * A query whose position is outside [0, kv_len) makes every gradient NaN.
- * Workspace: mla_workspace_size(cfg, MLA_OP_ATTENTION_BACKWARD, T, kv_len, 0),
- * which holds [n_h][T][kv_len] probabilities twice (a training-step check,
- * not a long-context kernel).  Generic fp32 kernels. */
+ * A query whose position is outside [0, kv_len) makes dW_UK, dW_UV, dC and
+ * its own row of dq NaN.
+ * Workspace: mla_workspace_size(cfg, MLA_OP_ATTENTION_BACKWARD, T, kv_len, 0).
+ * At the DeepSeek-V2 head shape with a bf16 cache and weights (n_h 128, d_h
+ * 128, d_r 64, d_c 512): q (times scale) and dO are rounded to bf16 on
+ * entry, k and v per head are formed in bf16 as mla_prefill forms them, the
+ * attention's gradients run flash style on bf16 MFMA (the probabilities are
+ * recomputed per block of 32 queries x 32 keys and never stored; fp32 sums),
+ * and dW_UK, dW_UV and dC come from bf16 MFMA GEMMs over dk^C and dv rounded
+ * to bf16; the workspace grows with (T + kv_len) and holds both
+ * up-projections transposed (32 MB).  Other shapes: generic fp32 kernels,
+ * with [n_h][T][kv_len] probabilities held twice in the workspace (a
+ * training-step check, not a long-context kernel). */
 int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const float* q,
                            const int32_t* positions, const void* kv_cache, int num_pages,
                            const int32_t* page_table, int max_pages, int kv_len, int T,

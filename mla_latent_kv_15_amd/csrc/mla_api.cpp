@@ -218,8 +218,42 @@ void carve_bwd(Carver& c, const Geo& g, int T, int N, BwdWs* w) {
   w->lat_k = (float*)c.take(sizeof(float) * (size_t)N * g.d_c);
   w->lat_v = (float*)c.take(sizeof(float) * (size_t)N * g.d_c);
 }
+// the same at the DeepSeek-V2 head shape (bf16 MFMA, no T x N arrays): the
+// gathered rows, k and v per head, the bf16 query and dO, LSE and D, the
+// query blocks' furthest keys, dk^C and dv as rows and key-contiguous, the
+// latent rows and both up-projections transposed, dk^R per head, and the
+// two K halves of the latent gradient
+struct BwdWsV2 {
+  void *rows16, *k16, *v16, *q16, *do16, *dkv16, *dkT16, *dvT16, *cT16, *wT16;
+  float *lse, *dd, *dkr, *lat;
+  int* qblk_far;
+};
+void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
+  const size_t hd = (size_t)g.n_h * g.d_h, wq = (size_t)g.n_h * (g.d_h + g.d_r);
+  const size_t Np = (size_t)attn_bwd_v2_npad(N);
+  w->rows16 = c.take(2 * (size_t)N * g.row);
+  w->k16 = c.take(2 * (size_t)N * wq);
+  w->v16 = c.take(2 * (size_t)N * hd);
+  w->q16 = c.take(2 * (size_t)T * wq);
+  w->do16 = c.take(2 * (size_t)T * hd);
+  w->lse = (float*)c.take(sizeof(float) * (size_t)g.n_h * T);
+  w->dd = (float*)c.take(sizeof(float) * (size_t)g.n_h * T);
+  w->qblk_far = (int*)c.take(sizeof(int) * (size_t)((T + 31) / 32));
+  w->dkv16 = c.take(2 * (size_t)N * 2 * hd);
+  w->dkT16 = c.take(2 * hd * Np);
+  w->dvT16 = c.take(2 * hd * Np);
+  w->cT16 = c.take(2 * (size_t)g.d_c * Np);
+  w->wT16 = c.take(2 * (size_t)g.d_c * 2 * hd);
+  w->dkr = (float*)c.take(sizeof(float) * (size_t)g.n_h * N * g.d_r);
+  w->lat = (float*)c.take(sizeof(float) * 2 * (size_t)N * g.d_c);
+}
 size_t ws_bwd(const Geo& g, int T, int N) {
   Carver c(nullptr);
+  if (attn_bwd_v2_supported(g)) {
+    BwdWsV2 w;
+    carve_bwd_v2(c, g, T, N, &w);
+    return c.used;
+  }
   BwdWs w;
   carve_bwd(c, g, T, N, &w);
   return c.used;
@@ -872,11 +906,40 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   Carver c(workspace);
-  BwdWs b;
-  carve_bwd(c, g, T, kv_len, &b);
   const GType Ty = st(g);
   const bool wt = w->layout == MLA_LAYOUT_TILES;
   const int N = kv_len, dqw = g.d_h + g.d_r;
+  if (attn_bwd_v2_supported(g)) {
+    // DeepSeek-V2 heads: k and v per head in bf16 as the prefill makes them,
+    // the attention's gradients flash style on bf16 MFMA, then the weight
+    // and latent gradients as bf16 MFMA GEMMs with fp32 results
+    BwdWsV2 b;
+    carve_bwd_v2(c, g, T, N, &b);
+    const int nq = g.n_h * g.d_h, Np = attn_bwd_v2_npad(N);
+    MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, N, b.rows16, b.k16, s));
+    MLA_TRY(wgemm(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, 0, 0, w->W_UK, b.k16,
+                  (long)g.n_h * dqw, 0, false, 1.f, s, false, false, wt, g.d_h, dqw));
+    MLA_TRY(wgemm(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, 0, 0, w->W_UV, b.v16, nq, 0,
+                  false, 1.f, s, false, false, wt));
+    MLA_TRY(attn_bwd_v2(g, N, T, q, dO, positions, b.k16, b.v16, b.q16, b.do16, b.lse, b.dd,
+                        b.qblk_far, dq, b.dkv16, b.dkT16, b.dvT16, b.dkr, s));
+    // dW_UK,i = sum_j dk^C_ij c_j^T (rows [head, dim], contraction over keys)
+    MLA_TRY(transpose16(b.rows16, g.row, false, g.d_c, N, Np, b.cT16, Np, 0, s));
+    MLA_TRY(wgemm(GemmTile{4, 1}, nq, g.d_c, Np, b.dkT16, Np, 0, 0, b.cT16, dW_UK, g.d_c, 0,
+                  true, 1.f, s));
+    MLA_TRY(wgemm(GemmTile{4, 1}, nq, g.d_c, Np, b.dvT16, Np, 0, 0, b.cT16, dW_UV, g.d_c, 0,
+                  true, 1.f, s));
+    // dc_j = [dk^C_j | dv_j] . [W_UK ; W_UV] in two K halves, summed with
+    // the heads' dk^R into dC
+    MLA_TRY(transpose16(w->W_UK, g.d_c, wt, g.d_c, nq, nq, b.wT16, 2L * nq, 0, s));
+    MLA_TRY(transpose16(w->W_UV, g.d_c, wt, g.d_c, nq, nq, b.wT16, 2L * nq, nq, s));
+    MLA_TRY(wgemm(GemmTile{4, 2}, N, g.d_c, 2 * nq, b.dkv16, 2L * nq, 0, 0, b.wT16, b.lat, g.d_c,
+                  (long)N * g.d_c, true, 1.f, s));
+    MLA_TRY(attn_bwd_dc(g, N, b.lat, b.lat + (size_t)N * g.d_c, b.dkr, dC, s));
+    return MLA_OK;
+  }
+  BwdWs b;
+  carve_bwd(c, g, T, kv_len, &b);
   const long hd = (long)g.n_h * g.d_h, TN = (long)T * N;
   // the forward's pieces: cached rows, K^C = W_UK,i c_j and V = W_UV,i c_j
   MLA_TRY(gather_rows_f32(g, kv_cache, num_pages, page_table, max_pages, N, b.rows, s));
