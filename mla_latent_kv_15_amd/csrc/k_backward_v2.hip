@@ -52,23 +52,90 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) v4bf16 lds_v4bf16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr int kH = 128;          // heads
 constexpr int kW = 192;          // query and key width
 constexpr int kDv = 128;         // value width
-constexpr int kB = 32;           // queries or keys per wave tile
+constexpr int kB = 32;           // queries or keys per wave tile (and per block)
 constexpr int kWv = 4;           // waves per work-group
 constexpr int kQK = kW / 16;     // K-steps of the 192-wide products (12)
 constexpr int kVK = kDv / 16;    // K-steps of the 128-wide products (8)
 constexpr float kLog2e = 1.4426950408889634f;
-// LDS rows: 192-wide rows padded to 200 bf16 (the 16 rows a row read serves
-// at once start at distinct 16-byte bank groups); 128-wide rows read only
-// as rows padded to 136; 128-wide rows read mostly by transposing reads
-// padded to 160 (the four rows such a read serves at once start 64 banks
-// apart).
-constexpr int kRow192 = kW + 8;
-constexpr int kRowRd = kDv + 8;
-constexpr int kRowTr = kDv + 32;
+constexpr int kVmcnt0 = 0x0f70;  // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone)
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, gfx9 family
+constexpr int kOob = 1 << 30;            // a source offset past every range
+
+// Blocks of 32 rows (keys, or queries) of one head stream through a ring of
+// LDS slots, kSlots - 1 blocks in flight, by direct-to-LDS loads: each load
+// moves 64 16-byte units, one per lane, to 1 KB of consecutive LDS.  In HBM
+// consecutive rows of one head lie kStrideW (192-wide) or kStrideV (128-wide)
+// bytes apart.  In a slot the 192-wide rows come first, 24 units each, then
+// the 128-wide rows, 16 units each.
+constexpr int kStrideW = kH * kW * 2;
+constexpr int kStrideV = kH * kDv * 2;
+constexpr int kUnitsW = kB * kW / 8;    // 768
+constexpr int kUnitsV = kB * kDv / 8;   // 512
+constexpr int kSlots = 4;
+constexpr int kLoadsA = (kUnitsW + kUnitsV) / 64 / kWv;   // 5 loads per wave per block
+constexpr int kLoadsB = kLoadsA + 1;                       // + records (wave 0) or padding
+constexpr int kSlotA = (kUnitsW + kUnitsV) * 16;           // 20 KB
+constexpr int kSlotB = kSlotA + kWv * 1024;                // 24 KB
+static_assert(kLoadsA * kWv * 64 == kUnitsW + kUnitsV, "whole loads per block");
+static_assert(kLoadsB * (kSlots - 2) < 64, "vmcnt range");
+
+// A row's units are XOR-permuted so that the 16 rows one row read serves at
+// once (lanes c = 0 .. 15, one unit each) and the 4 rows x 4 units that the
+// 32 lanes of a transposing read served at once touch land on distinct
+// banks (64 banks of 4 bytes).  192-wide rows (24 units, 96 banks apart from
+// row to row): a 3-bit function of j >> 1 whose bit 2 follows bit 1 of j,
+// so that rows two apart take complementary halves of each 8-unit group.
+// 128-wide rows (16 units, 64 banks apart): a 4-bit function of j whose bits
+// 2 and 3 follow j's two lowest bits, so that 4 consecutive rows take
+// distinct 4-unit groups.
+__device__ inline int sw24(int j) {
+  const int v = (j >> 1) & 7;
+  return ((v & 1) << 2) | ((v >> 1) & 3);
+}
+__device__ inline int sw16(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
+__device__ inline int unit24(int j, int p) { return j * 24 + (p ^ sw24(j)); }
+__device__ inline int unit16(int j, int p) { return kUnitsW + j * 16 + (p ^ sw16(j)); }
+
+// The source offset (from the block's first row) of the unit that lane
+// `lane` of load r of a block carries: LDS unit u = 64 r + lane holds unit
+// (u mod row units) ^ sw(j) of row j.
+__device__ inline int src_off(int r, int lane) {
+  const int u = 64 * r + lane;
+  if (u < kUnitsW) {
+    const int j = u / 24;
+    return j * kStrideW + 16 * ((u % 24) ^ sw24(j));
+  }
+  const int v = u - kUnitsW, j = v / 16;
+  return j * kStrideV + 16 * ((v % 16) ^ sw16(j));
+}
+
+// A buffer resource over [p, p + bytes): a lane whose offset falls outside
+// reads no memory and writes zeros to LDS, so a block's missing rows (past N
+// or T) hold zeros and a padding load (bytes = 0) only writes zeros.
+__device__ inline i32x4 make_rsrc(const void* p, int bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
+}
+// One direct-to-LDS load (inline asm: it writes only LDS, no register is left
+// in flight; the ring's waits count these loads by hand).
+__device__ inline void dma16(const i32x4& rs, int voff, lds_char* dst) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+               "s"(rs), "s"(m0)
+               : "m0", "memory");
+}
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ inline uint32_t pack2(float x, float y) {
   return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
@@ -100,21 +167,77 @@ __device__ inline void rows_as_b(const f32x16& X, bf16x8 (&pb)[2]) {
   pb[1] = __builtin_bit_cast(bf16x8, u32x4{R[4], R[5], R[6], R[7]});
 }
 
-// The A operand "columns D0 .. D0 + 31 of rows k0 + 8h .. + 7" of a
-// row-major LDS block (byte base `base`, `pitch` bf16 per row), transposed:
-// lane (c, h) receives column D0 + c of those eight rows.  Two transposing
-// reads of four rows each: in each 16-lane group lane s supplies the 8-byte
-// chunk of row k0 + 8h + s / 4, columns D0 + 16 (group & 1) + 4 (s % 4), and
-// output lane i receives, as its element r, element i % 4 of lane
-// 4 r + i / 4's chunk.
-__device__ inline bf16x8 tr_operand(lds_char* lds, int base, int pitch, int k0, int D0) {
-  const int lane = threadIdx.x & 63;
-  const int row = k0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = D0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int b = base + 2 * (row * pitch + col);
-  const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(lds + b));
-  const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(lds + b + 2 * 4 * pitch));
+// The A operand "columns D0 .. D0 + 31 of rows k0 + 8h .. + 7" of a slot's
+// block, transposed: lane (c, h) receives column D0 + c of those eight rows.
+// Two transposing reads of four rows each: in each 16-lane group lane s
+// supplies the 8-byte piece of row k0 + 8h + s / 4 at columns D0 + 16 (group
+// & 1) + 4 (s % 4), and output lane i receives, as its element r, element
+// i % 4 of lane 4 r + i / 4's piece.  W24: the 192-wide rows, else the
+// 128-wide ones.
+template <bool W24>
+__device__ inline bf16x8 tr_operand(const lds_char* slot, int lane, int k0, int D0) {
+  const int j = k0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int p = D0 / 8 + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int half = 8 * (lane & 1);
+  const int u0 = W24 ? unit24(j, p) : unit16(j, p);
+  const int u1 = W24 ? unit24(j + 4, p) : unit16(j + 4, p);
+  const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(slot + 16 * u0 + half));
+  const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(slot + 16 * u1 + half));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Row reads: lane (c, h) gets unit 2 ks + h of row c (an A operand).
+__device__ inline bf16x8 row24(const lds_char* slot, int lane, int ks) {
+  const int c = lane & 31, h = lane >> 5;
+  return *(const lds_bf16x8*)(slot + 16 * unit24(c, 2 * ks + h));
+}
+__device__ inline bf16x8 row16(const lds_char* slot, int lane, int ks) {
+  const int c = lane & 31, h = lane >> 5;
+  return *(const lds_bf16x8*)(slot + 16 * unit16(c, 2 * ks + h));
+}
+
+
+// The score products S and dP as inline-asm MFMAs with VGPR accumulators:
+// with the builtin the compiler keeps them in the accumulation registers,
+// which the long-lived dq, dK and dV sums fill, and copies registers between
+// the two files every block.  Back-to-back accumulation into the same
+// registers needs no wait states; mfma_drain's 24 wait states cover the last
+// product's result before VALU reads it.
+// (Not volatile: the scheduler may then hoist the LDS reads that feed them.
+// Their operands come from LDS reads and from registers loaded once, never
+// from a VALU write just before.)
+__device__ __forceinline__ void mfma_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain(f32x16& s, f32x16& dp) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s), "+v"(dp));
+}
+// The long-lived sums (dq; dK and dV) stay in the accumulation registers:
+// inline-asm MFMAs with an AGPR accumulator (with the builtin the compiler
+// moved them between the register files every block).  Their hazards are
+// covered by hand: a VALU write of a B operand (the bf16 numerators) or of
+// the zeroed sums is followed by more than the 2 wait states an MFMA read
+// of it needs (settle), and mfma_drain_acc waits out the last product before
+// the sums are read.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void settle(bf16x8 (&x)[2]) {
+  asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]));
+}
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+a"(acc[k]));
+  asm volatile("s_nop 4" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void mfma_drain_acc(f32x16 (&acc)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+a"(acc[k]));
 }
 
 __device__ inline float swap_max(float v) {
@@ -131,19 +254,21 @@ __device__ inline float swap_sum(float v) {
 // ---------------------------------------------------------------------------
 // query side: LSE, D and dq
 // ---------------------------------------------------------------------------
-constexpr int kKElemsA = kB * kRow192;             // K block
-constexpr int kBufA = kKElemsA + kB * kRowRd;      // + V block (rows)
-
+// rec[i * T + t] = {LSE (log2 units), D, lim, 0} of query t and head i, lim
+// (an int's bits) one past the last key the query sees: a key j takes part
+// iff j < lim.  Zeros (a query past T) take no part.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
     const __bf16* __restrict__ q16, const __bf16* __restrict__ do16,
     const __bf16* __restrict__ k16, const __bf16* __restrict__ v16,
-    const int32_t* __restrict__ positions, int T, int N, float scale, float* __restrict__ lse_out,
-    float* __restrict__ d_out, int* __restrict__ qblk_far, float* __restrict__ dq) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][kBufA];
+    const int32_t* __restrict__ positions, int T, int N, float scale, f32x4* __restrict__ rec,
+    int* __restrict__ qblk_far, float* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) char ring[kSlots * kSlotA];
   __shared__ int s_far[kWv];
+  lds_char* const lds = (lds_char*)ring;
   const int i = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
-  const int qb = blockIdx.x * kWv + wave;   // this wave's block of 32 queries
+  // the last query blocks see the most keys: dispatch them first
+  const int qb = (gridDim.x - 1 - blockIdx.x) * kWv + wave;   // this wave's 32 queries
   const int t = qb * kB + c;
   const bool t_ok = t < T;
   const int pos = t_ok ? positions[t] : -1;
@@ -156,10 +281,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
     s_far[wave] = far;
     if (i == 0 && qb * kB < T) qblk_far[qb] = far;
   }
-  __syncthreads();
-  const int far_wg = max(max(s_far[0], s_far[1]), max(s_far[2], s_far[3]));
-  const int nkb = (far_wg + kB) / kB;   // key blocks the work-group stages
-
   // Q^T and dO^T as B operands: K-step ks holds dims 16 ks + 8h .. + 7
   bf16x8 qv[kQK], dv[kVK];
   {
@@ -170,67 +291,54 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
     for (int ks = 0; ks < kVK; ++ks)
       dv[ks] = *(const bf16x8*)(do16 + row * kDv + 16 * ks + 8 * h);
   }
-  // staging: K pieces p = tid + 256 r (key p / 24, piece p % 24), V pieces
-  // (key p / 16, dims 8 (p % 16) ..); keys past N repeat the last one
-  uint4 k0r, k1r, k2r, v0r, v1r;
-  auto kpiece = [&](int kb, int r) {
-    const int p = tid + 256 * r, key = p / (kW / 8), pc = p % (kW / 8);
-    return *(const uint4*)(k16 + ((long)min(kb * kB + key, N - 1) * kH + i) * kW + 8 * pc);
-  };
-  auto vpiece = [&](int kb, int r) {
-    const int p = tid + 256 * r, key = p / (kDv / 8), pc = p % (kDv / 8);
-    return *(const uint4*)(v16 + ((long)min(kb * kB + key, N - 1) * kH + i) * kDv + 8 * pc);
-  };
-  auto gload = [&](int kb) {
-    k0r = kpiece(kb, 0);
-    k1r = kpiece(kb, 1);
-    k2r = kpiece(kb, 2);
-    v0r = vpiece(kb, 0);
-    v1r = vpiece(kb, 1);
-  };
-  auto lstore = [&](int buf) {
-    __bf16* K = lds[buf];
-    auto ks_ = [&](int r, uint4 x) {
-      const int p = tid + 256 * r, key = p / (kW / 8), pc = p % (kW / 8);
-      *(uint4*)(K + key * kRow192 + 8 * pc) = x;
-    };
-    auto vs_ = [&](int r, uint4 x) {
-      const int p = tid + 256 * r, key = p / (kDv / 8), pc = p % (kDv / 8);
-      *(uint4*)(K + kKElemsA + key * kRowRd + 8 * pc) = x;
-    };
-    ks_(0, k0r);
-    ks_(1, k1r);
-    ks_(2, k2r);
-    vs_(0, v0r);
-    vs_(1, v1r);
-  };
-  // S^T = K Q^T and dP^T = V dO^T of key block kb (rows: keys, column: query)
-  auto scores = [&](const __bf16* K, f32x16& s, f32x16& dp) {
-    s = f32x16{};
-    dp = f32x16{};
+  // the ring below counts its own loads: none other may be in flight
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  const int far_wg = max(max(s_far[0], s_far[1]), max(s_far[2], s_far[3]));
+  const int nkb = (far_wg + kB) / kB;   // key blocks the work-group streams (per pass)
+
+  // The two passes stream the same key blocks: sequence element b < nkb is
+  // block b of pass 1, nkb <= b < 2 nkb block b - nkb of pass 2; past that a
+  // padding load.  Load k of wave w carries units 64 (w + 4k) .. of a block:
+  // K rows for k < 3, V rows after.
+  int voff[kLoadsA];
 #pragma unroll
-    for (int ks = 0; ks < kQK; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *(const bf16x8*)(K + c * kRow192 + 16 * ks + 8 * h), qv[ks], s, 0, 0, 0);
+  for (int k = 0; k < kLoadsA; ++k) voff[k] = src_off(wave + 4 * k, lane);
+  const int nseq = 2 * nkb;
+  auto issue = [&](int b) {
+    const bool real = b < nseq;
+    const int kb = real ? (b < nkb ? b : b - nkb) : 0;
+    const int nv = real ? min(kB, N - kb * kB) : 0;
+    const i32x4 rk = make_rsrc(k16 + ((long)kb * kB * kH + i) * kW, nv * kStrideW);
+    const i32x4 rv = make_rsrc(v16 + ((long)kb * kB * kH + i) * kDv, nv * kStrideV);
+    lds_char* slot = lds + (b % kSlots) * kSlotA + wave * 1024;
 #pragma unroll
-    for (int ks = 0; ks < kVK; ++ks)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *(const bf16x8*)(K + kKElemsA + c * kRowRd + 16 * ks + 8 * h), dv[ks], dp, 0, 0, 0);
+    for (int k = 0; k < kLoadsA; ++k) dma16(k < 3 ? rk : rv, voff[k], slot + 4096 * k);
+  };
+  // S^T = K Q^T and dP^T = V dO^T of a block (rows: keys, column: query)
+  auto scores = [&](const lds_char* slot, int ln, f32x16& s, f32x16& dp) {
+    mfma_first(s, row24(slot, ln, 0), qv[0]);
+#pragma unroll
+    for (int ks = 1; ks < kQK; ++ks) mfma_acc(s, row24(slot, ln, ks), qv[ks]);
+    mfma_first(dp, row16(slot, ln, 0), dv[0]);
+#pragma unroll
+    for (int ks = 1; ks < kVK; ++ks) mfma_acc(dp, row16(slot, ln, ks), dv[ks]);
+    mfma_drain(s, dp);
   };
 
+#pragma unroll
+  for (int b = 0; b < kSlots - 1; ++b) issue(b);
+  int b = 0;
   // ---- pass 1: m, l, z of this lane's query (log2 units)
   float m = -INFINITY, l = 0.f, z = 0.f;
-  if (nkb > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) gload(kb + 1);
+  for (int kb = 0; kb < nkb; ++kb, ++b) {
+    wait_vm<kLoadsA*(kSlots - 2)>();   // this wave's loads of block b
+    __syncthreads();                     // everyone's; slot (b - 1) is free
+    issue(b + kSlots - 1);
     const int j0 = kb * kB;
     if (j0 <= far) {
       f32x16 s, dp;
-      scores(lds[kb & 1], s, dp);
+      scores(lds + (b % kSlots) * kSlotA, lane, s, dp);
       float bm = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -252,32 +360,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
       z = z * alpha + swap_sum(zs);
       m = mn;
     }
-    if (kb + 1 < nkb) lstore((kb + 1) & 1);
-    __syncthreads();
   }
   const float nanv = __builtin_nanf("");
   const float lse = valid ? m + __log2f(l) : nanv;
   const float dd = valid ? z / l : nanv;
-  if (t_ok && h == 0) {
-    lse_out[(long)i * T + t] = lse;
-    d_out[(long)i * T + t] = dd;
-  }
 
   // ---- pass 2: dQ^T += K^T dS^T
   f32x16 acc[kW / 32];
 #pragma unroll
   for (int dt = 0; dt < kW / 32; ++dt) acc[dt] = f32x16{};
-  if (nkb > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) gload(kb + 1);
+  settle_acc(acc);
+  for (int kb = 0; kb < nkb; ++kb, ++b) {
+    wait_vm<kLoadsA*(kSlots - 2)>();
+    __syncthreads();
+    issue(b + kSlots - 1);
     const int j0 = kb * kB;
     if (j0 <= far) {
+      const lds_char* slot = lds + (b % kSlots) * kSlotA;
+      const int ln = lane;
       f32x16 s, dp;
-      scores(lds[kb & 1], s, dp);
+      scores(slot, ln, s, dp);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -286,19 +388,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
       }
       bf16x8 pb[2];
       rows_as_b(s, pb);
-      const int base = (kb & 1) * 2 * kBufA;
+      settle(pb);
 #pragma unroll
       for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
         for (int dt = 0; dt < kW / 32; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_operand((lds_char*)lds, base, kRow192, 16 * kap, 32 * dt), pb[kap], acc[dt], 0,
-              0, 0);
+          mfma_agpr(acc[dt], tr_operand<true>(slot, ln, 16 * kap, 32 * dt), pb[kap]);
     }
-    if (kb + 1 < nkb) lstore((kb + 1) & 1);
-    __syncthreads();
   }
+  mfma_drain_acc(acc);
+  wait_vm<0>();   // the ring's padding loads still write LDS
   if (!t_ok) return;
+  if (h == 0) rec[(long)i * T + t] = f32x4{lse, dd, __int_as_float(last + 1), 0.f};
   // lane (c, h) holds dims 32 dt + 8 g + 4h .. + 3 (g = r >> 2) of query t
   float* dst = dq + ((long)t * kH + i) * kW + 4 * h;
 #pragma unroll
@@ -313,24 +414,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
 // ---------------------------------------------------------------------------
 // key side: dK (its latent part per head, its RoPE part per head) and dV
 // ---------------------------------------------------------------------------
-constexpr int kQElemsB = kB * kRow192;             // Q block
-constexpr int kBufB = kQElemsB + kB * kRowTr;      // + dO block
-constexpr int kMaxQbLds = 1024;                    // query blocks whose far key sits in LDS
+constexpr int kMaxQb = 2048;                       // query blocks (their far keys sit in LDS)
 constexpr int kTrPitch = kB + 8;                   // keys per LDS row of the transposed tiles
-static_assert(kWv * kDv * kTrPitch * 2 <= 2 * kBufB * 2, "transposed tiles fit the ring");
+static_assert(kWv * kDv * kTrPitch * 2 <= kSlots * kSlotB, "transposed tiles fit the ring");
 
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
     const __bf16* __restrict__ q16, const __bf16* __restrict__ do16,
     const __bf16* __restrict__ k16, const __bf16* __restrict__ v16,
-    const int32_t* __restrict__ positions, const float* __restrict__ lse_in,
-    const float* __restrict__ d_in, const int* __restrict__ qblk_far, int T, int N, int Npad,
+    const f32x4* __restrict__ rec, const int* __restrict__ qblk_far, int T, int N, int Npad,
     __bf16* __restrict__ dkv16, __bf16* __restrict__ dkT16, __bf16* __restrict__ dvT16,
     float* __restrict__ dkr) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][kBufB];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][kB];
-  __shared__ __attribute__((aligned(16))) float s_d[2][kB];
-  __shared__ __attribute__((aligned(16))) int s_last[2][kB];
-  __shared__ int s_qf[kMaxQbLds];
+  __shared__ __attribute__((aligned(16))) char ring[kSlots * kSlotB];
+  __shared__ int s_qf[kMaxQb];
+  lds_char* const lds = (lds_char*)ring;
   const int i = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wg_j0 = blockIdx.x * kWv * kB;
@@ -347,61 +443,39 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
 #pragma unroll
     for (int ks = 0; ks < kVK; ++ks) vv[ks] = *(const bf16x8*)(v16 + row * kDv + 16 * ks + 8 * h);
   }
-  // staging of query block qb: Q pieces (query p / 24, piece p % 24), dO
-  // pieces (query p / 16, dims 8 (p % 16) ..), queries past T repeat the
-  // last one; per query LSE, D and the last key it sees (-1 past T)
-  uint4 q0r, q1r, q2r, d0r, d1r;
-  float lse_r = 0.f, d_r = 0.f;
-  int last_r = -1;
-  auto qpiece = [&](int qb, int r) {
-    const int p = tid + 256 * r, qq = p / (kW / 8), pc = p % (kW / 8);
-    return *(const uint4*)(q16 + ((long)min(qb * kB + qq, T - 1) * kH + i) * kW + 8 * pc);
+  // the query blocks that see at least one key of the work-group; the
+  // decision is the same for every thread (qblk_far is per query block).
+  // The blocks' far keys are read once into LDS (nqb <= kMaxQb), so that the
+  // scan below costs no memory round trips.
+  const int nqb = (T + kB - 1) / kB;
+  for (int e = tid; e < nqb; e += 256) s_qf[e] = qblk_far[e];
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);   // the ring below counts its own loads
+  __syncthreads();
+  auto qfar = [&](int qb) { return s_qf[qb]; };
+  auto next_active = [&](int qb) {
+    while (qb < nqb && qfar(qb) < wg_j0) ++qb;
+    return qb;
   };
-  auto dpiece = [&](int qb, int r) {
-    const int p = tid + 256 * r, qq = p / (kDv / 8), pc = p % (kDv / 8);
-    return *(const uint4*)(do16 + ((long)min(qb * kB + qq, T - 1) * kH + i) * kDv + 8 * pc);
-  };
-  auto gload = [&](int qb) {
-    q0r = qpiece(qb, 0);
-    q1r = qpiece(qb, 1);
-    q2r = qpiece(qb, 2);
-    d0r = dpiece(qb, 0);
-    d1r = dpiece(qb, 1);
-    if (tid < kB) {
-      const int t = qb * kB + tid;
-      if (t < T) {
-        const int p = positions[t];
-        const bool valid = p >= 0 && p < N;
-        last_r = valid ? p : N - 1;
-        lse_r = lse_in[(long)i * T + t];
-        d_r = d_in[(long)i * T + t];
-      } else {
-        last_r = -1;
-        lse_r = 0.f;
-        d_r = 0.f;
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    __bf16* Q = lds[buf];
-    auto qs_ = [&](int r, uint4 x) {
-      const int p = tid + 256 * r, qq = p / (kW / 8), pc = p % (kW / 8);
-      *(uint4*)(Q + qq * kRow192 + 8 * pc) = x;
-    };
-    auto ds_ = [&](int r, uint4 x) {
-      const int p = tid + 256 * r, qq = p / (kDv / 8), pc = p % (kDv / 8);
-      *(uint4*)(Q + kQElemsB + qq * kRowTr + 8 * pc) = x;
-    };
-    qs_(0, q0r);
-    qs_(1, q1r);
-    qs_(2, q2r);
-    ds_(0, d0r);
-    ds_(1, d1r);
-    if (tid < kB) {
-      s_lse[buf][tid] = lse_r;
-      s_d[buf][tid] = d_r;
-      s_last[buf][tid] = last_r;
-    }
+
+  // A slot: the block's Q rows, dO rows, then 32 records (wave 0's sixth
+  // load; the other waves' sixth load is padding).
+  int voff[kLoadsB];
+#pragma unroll
+  for (int k = 0; k < kLoadsA; ++k) voff[k] = src_off(wave + 4 * k, lane);
+  voff[kLoadsA] = wave == 0 && lane < kB ? 16 * lane : kOob;
+  int qi = next_active(0);   // the next block to load
+  auto issue = [&](int b) {
+    const bool real = qi < nqb;
+    const int qb = real ? qi : 0;
+    const int nv = real ? min(kB, T - qb * kB) : 0;
+    const i32x4 rq = make_rsrc(q16 + ((long)qb * kB * kH + i) * kW, nv * kStrideW);
+    const i32x4 ro = make_rsrc(do16 + ((long)qb * kB * kH + i) * kDv, nv * kStrideV);
+    const i32x4 rs = make_rsrc(rec + (long)i * T + qb * kB, nv * 16);
+    lds_char* slot = lds + (b % kSlots) * kSlotB + wave * 1024;
+#pragma unroll
+    for (int k = 0; k < kLoadsB; ++k)
+      dma16(k < 3 ? rq : (k < kLoadsA ? ro : rs), voff[k], slot + 4096 * k);
+    if (real) qi = next_active(qi + 1);
   };
 
   f32x16 accK[kW / 32], accV[kDv / 32];
@@ -409,81 +483,63 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
   for (int dt = 0; dt < kW / 32; ++dt) accK[dt] = f32x16{};
 #pragma unroll
   for (int dt = 0; dt < kDv / 32; ++dt) accV[dt] = f32x16{};
-
-  // the query blocks that see at least one key of the work-group; the
-  // decision is the same for every thread (qblk_far is per query block).
-  // The first kMaxQbLds blocks' far keys are read once into LDS, so that the
-  // scan below costs no memory round trips.
-  const int nqb = (T + kB - 1) / kB;
-  for (int e = tid; e < min(nqb, kMaxQbLds); e += 256) s_qf[e] = qblk_far[e];
-  __syncthreads();
-  auto qfar = [&](int qb) { return qb < kMaxQbLds ? s_qf[qb] : qblk_far[qb]; };
-  auto next_active = [&](int qb) {
-    while (qb < nqb && qfar(qb) < wg_j0) ++qb;
-    return qb;
-  };
+  settle_acc(accK);
+  settle_acc(accV);
+#pragma unroll
+  for (int b = 0; b < kSlots - 1; ++b) issue(b);
   int qb = next_active(0);
-  if (qb < nqb) {
-    gload(qb);
-    lstore(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (qb < nqb) {
-    const int qn = next_active(qb + 1);
-    if (qn < nqb) gload(qn);
+  for (int b = 0; qb < nqb; ++b) {
+    wait_vm<kLoadsB*(kSlots - 2)>();   // this wave's loads of block b
+    __syncthreads();                     // everyone's; slot (b - 1) is free
+    issue(b + kSlots - 1);
     if (qfar(qb) >= j0) {   // this wave's keys: some query of the block sees one
-      const __bf16* Q = lds[buf];
+      const lds_char* slot = lds + (b % kSlots) * kSlotB;
+      const int ln = lane;
       // S = Q K^T and dP = dO V^T (rows: queries, column: key c)
-      f32x16 s = {}, dp = {};
+      f32x16 s, dp;
+      mfma_first(s, row24(slot, ln, 0), kv[0]);
 #pragma unroll
-      for (int ks = 0; ks < kQK; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)(Q + c * kRow192 + 16 * ks + 8 * h), kv[ks], s, 0, 0, 0);
+      for (int ks = 1; ks < kQK; ++ks) mfma_acc(s, row24(slot, ln, ks), kv[ks]);
+      mfma_first(dp, row16(slot, ln, 0), vv[0]);
 #pragma unroll
-      for (int ks = 0; ks < kVK; ++ks)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)(Q + kQElemsB + c * kRowTr + 16 * ks + 8 * h), vv[ks], dp, 0, 0, 0);
-      // rows 8 g + 4h .. + 3: the statistics of those four queries
+      for (int ks = 1; ks < kVK; ++ks) mfma_acc(dp, row16(slot, ln, ks), vv[ks]);
+      mfma_drain(s, dp);
+      // rows 8 g + 4h + e: the records of those four queries
       f32x16 ds;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)&s_lse[buf][8 * g + 4 * h];
-        const f32x4 d4 = *(const f32x4*)&s_d[buf][8 * g + 4 * h];
-        const i32x4 t4 = *(const i32x4*)&s_last[buf][8 * g + 4 * h];
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
+          const f32x4 st =
+              *(const lds_f32x4*)(slot + 16 * (kUnitsW + kUnitsV + 8 * g + 4 * h + e));
           // (a key past N stays exactly zero even beside a NaN query row)
-          const bool seen = key_ok && key <= t4[e];
-          const float p = seen ? __builtin_amdgcn_exp2f(fmaf(s[r], kLog2e, -l4[e])) : 0.f;
-          s[r] = p;                                   // P
-          ds[r] = seen ? p * (dp[r] - d4[e]) : 0.f;   // dS
+          const bool seen = key_ok && key < __float_as_int(st[2]);
+          const float p = seen ? __builtin_amdgcn_exp2f(fmaf(s[r], kLog2e, -st[0])) : 0.f;
+          s[r] = p;                                  // P
+          ds[r] = seen ? p * (dp[r] - st[1]) : 0.f;  // dS
         }
-      }
       bf16x8 pbP[2], pbS[2];
       rows_as_b(s, pbP);
       rows_as_b(ds, pbS);
-      const int base = buf * 2 * kBufB;
+      settle(pbP);
+      settle(pbS);
 #pragma unroll
       for (int kap = 0; kap < 2; ++kap) {
 #pragma unroll
         for (int dt = 0; dt < kDv / 32; ++dt)
-          accV[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_operand((lds_char*)lds, base + 2 * kQElemsB, kRowTr, 16 * kap, 32 * dt),
-              pbP[kap], accV[dt], 0, 0, 0);
+          mfma_agpr(accV[dt], tr_operand<false>(slot, ln, 16 * kap, 32 * dt), pbP[kap]);
 #pragma unroll
         for (int dt = 0; dt < kW / 32; ++dt)
-          accK[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_operand((lds_char*)lds, base, kRow192, 16 * kap, 32 * dt), pbS[kap], accK[dt],
-              0, 0, 0);
+          mfma_agpr(accK[dt], tr_operand<true>(slot, ln, 16 * kap, 32 * dt), pbS[kap]);
       }
     }
-    if (qn < nqb) lstore(buf ^ 1);   // that buffer was last read one block ago
-    __syncthreads();
-    buf ^= 1;
-    qb = qn;
+    qb = next_active(qb + 1);
   }
+  mfma_drain_acc(accK);
+  mfma_drain_acc(accV);
+  wait_vm<0>();      // the padding loads still write LDS
+  __syncthreads();   // and every wave is done with the ring
   // lane (c, h) holds dims 32 dt + 8 g + 4h .. + 3 (g = r >> 2) of key `key`
   if (key_ok) {
     __bf16* rowk = dkv16 + (long)key * (2 * kH * kDv) + i * kDv + 4 * h;
@@ -589,24 +645,30 @@ __global__ __launch_bounds__(256) void bwd_inputs_v2_kernel(const float* __restr
 
 bool attn_bwd_v2_supported(const Geo& g) { return prefill_v2_supported(g); }
 
+int attn_bwd_v2_max_queries() { return kMaxQb * kB; }
+
+// a block's byte offsets (rows of all heads) stay within 32 bits
+int attn_bwd_v2_max_keys() { return 65536; }
+
 int attn_bwd_v2_npad(int N) { return (N + kWv * kB - 1) / (kWv * kB) * (kWv * kB); }
 
 hipError_t attn_bwd_v2(const Geo& g, int N, int T, const float* q, const float* dO,
                        const int32_t* positions, const void* k16, const void* v16, void* q16,
-                       void* do16, float* lse, float* dd, int* qblk_far, float* dq, void* dkv16,
-                       void* dkT16, void* dvT16, float* dkr, hipStream_t s) {
+                       void* do16, void* rec, int* qblk_far, float* dq, void* dkv16, void* dkT16,
+                       void* dvT16, float* dkr, hipStream_t s) {
   if (N <= 0 || T <= 0) return hipSuccess;
-  if (!attn_bwd_v2_supported(g)) return hipErrorInvalidValue;
+  if (!attn_bwd_v2_supported(g) || T > attn_bwd_v2_max_queries() || N > attn_bwd_v2_max_keys())
+    return hipErrorInvalidValue;
   const long nq = (long)T * kH * kW, nd = (long)T * kH * kDv;
   hipLaunchKernelGGL(bwd_inputs_v2_kernel, dim3((unsigned)((nq / 4 + 255) / 256)), dim3(256), 0, s,
                      q, dO, nq, nd, g.scale, (__bf16*)q16, (__bf16*)do16);
   hipLaunchKernelGGL(attn_bwd_dq_v2_kernel, dim3((T + kWv * kB - 1) / (kWv * kB), kH),
                      dim3(64 * kWv), 0, s, (const __bf16*)q16, (const __bf16*)do16,
-                     (const __bf16*)k16, (const __bf16*)v16, positions, T, N, g.scale, lse, dd,
+                     (const __bf16*)k16, (const __bf16*)v16, positions, T, N, g.scale, (f32x4*)rec,
                      qblk_far, dq);
   hipLaunchKernelGGL(attn_bwd_dkv_v2_kernel, dim3(attn_bwd_v2_npad(N) / (kWv * kB), kH),
                      dim3(64 * kWv), 0, s, (const __bf16*)q16, (const __bf16*)do16,
-                     (const __bf16*)k16, (const __bf16*)v16, positions, lse, dd, qblk_far, T, N,
+                     (const __bf16*)k16, (const __bf16*)v16, (const f32x4*)rec, qblk_far, T, N,
                      attn_bwd_v2_npad(N), (__bf16*)dkv16, (__bf16*)dkT16, (__bf16*)dvT16, dkr);
   return hipGetLastError();
 }

@@ -224,8 +224,8 @@ void carve_bwd(Carver& c, const Geo& g, int T, int N, BwdWs* w) {
 // latent rows and both up-projections transposed, dk^R per head, and the
 // two K halves of the latent gradient
 struct BwdWsV2 {
-  void *rows16, *k16, *v16, *q16, *do16, *dkv16, *dkT16, *dvT16, *cT16, *wT16;
-  float *lse, *dd, *dkr, *lat;
+  void *rows16, *k16, *v16, *q16, *do16, *rec, *dkv16, *dkT16, *dvT16, *cT16, *wT16;
+  float *dkr, *lat;
   int* qblk_far;
 };
 void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
@@ -236,8 +236,7 @@ void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
   w->v16 = c.take(2 * (size_t)N * hd);
   w->q16 = c.take(2 * (size_t)T * wq);
   w->do16 = c.take(2 * (size_t)T * hd);
-  w->lse = (float*)c.take(sizeof(float) * (size_t)g.n_h * T);
-  w->dd = (float*)c.take(sizeof(float) * (size_t)g.n_h * T);
+  w->rec = c.take(16 * (size_t)g.n_h * T);
   w->qblk_far = (int*)c.take(sizeof(int) * (size_t)((T + 31) / 32));
   w->dkv16 = c.take(2 * (size_t)N * 2 * hd);
   w->dkT16 = c.take(2 * hd * Np);
@@ -247,9 +246,13 @@ void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
   w->dkr = (float*)c.take(sizeof(float) * (size_t)g.n_h * N * g.d_r);
   w->lat = (float*)c.take(sizeof(float) * 2 * (size_t)N * g.d_c);
 }
+bool use_bwd_v2(const Geo& g, int T, int N) {
+  return attn_bwd_v2_supported(g) && T <= attn_bwd_v2_max_queries() &&
+         N <= attn_bwd_v2_max_keys();
+}
 size_t ws_bwd(const Geo& g, int T, int N) {
   Carver c(nullptr);
-  if (attn_bwd_v2_supported(g)) {
+  if (use_bwd_v2(g, T, N)) {
     BwdWsV2 w;
     carve_bwd_v2(c, g, T, N, &w);
     return c.used;
@@ -909,7 +912,7 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
   const GType Ty = st(g);
   const bool wt = w->layout == MLA_LAYOUT_TILES;
   const int N = kv_len, dqw = g.d_h + g.d_r;
-  if (attn_bwd_v2_supported(g)) {
+  if (use_bwd_v2(g, T, N)) {
     // DeepSeek-V2 heads: k and v per head in bf16 as the prefill makes them,
     // the attention's gradients flash style on bf16 MFMA, then the weight
     // and latent gradients as bf16 MFMA GEMMs with fp32 results
@@ -921,7 +924,7 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
                   (long)g.n_h * dqw, 0, false, 1.f, s, false, false, wt, g.d_h, dqw));
     MLA_TRY(wgemm(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, 0, 0, w->W_UV, b.v16, nq, 0,
                   false, 1.f, s, false, false, wt));
-    MLA_TRY(attn_bwd_v2(g, N, T, q, dO, positions, b.k16, b.v16, b.q16, b.do16, b.lse, b.dd,
+    MLA_TRY(attn_bwd_v2(g, N, T, q, dO, positions, b.k16, b.v16, b.q16, b.do16, b.rec,
                         b.qblk_far, dq, b.dkv16, b.dkT16, b.dvT16, b.dkr, s));
     // dW_UK,i = sum_j dk^C_ij c_j^T (rows [head, dim], contraction over keys)
     MLA_TRY(transpose16(b.rows16, g.row, false, g.d_c, N, Np, b.cT16, Np, 0, s));

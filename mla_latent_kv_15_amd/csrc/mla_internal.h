@@ -190,17 +190,21 @@ hipError_t attn_bwd_dc(const Geo& g, int N, const float* lat_k, const float* lat
 // The same gradients for the DeepSeek-V2 head shape on bf16 MFMA, flash style
 // (k_backward_v2.hip).  Inputs: q [T][128][192] and dO [T][128][128] fp32, k16
 // [N][128][192] and v16 [N][128][128] bf16.  Scratch: q16, do16 (the bf16
-// scaled query and dO), lse, dd [128][T], qblk_far [ceil(T / 32)].  Outputs:
+// scaled query and dO), rec [128][T] x 16 bytes (LSE, D and the keys seen per
+// query and head), qblk_far [ceil(T / 32)].  Outputs:
 // dq [T][128][192] fp32 (final), dkr [128][N][64] fp32 (per head), and dk^C,
 // dv in bf16 as rows dkv16 [N][2 * 128 * 128] (all heads' dk^C, then all
 // heads' dv) and key-contiguous dkT16, dvT16 [128 * 128][Npad] with zeros past
-// N (Npad = attn_bwd_v2_npad(N)).
+// N (Npad = attn_bwd_v2_npad(N)); T <= attn_bwd_v2_max_queries(), N <=
+// attn_bwd_v2_max_keys().
 bool attn_bwd_v2_supported(const Geo& g);
+int attn_bwd_v2_max_queries();
+int attn_bwd_v2_max_keys();
 int attn_bwd_v2_npad(int N);
 hipError_t attn_bwd_v2(const Geo& g, int N, int T, const float* q, const float* dO,
                        const int32_t* positions, const void* k16, const void* v16, void* q16,
-                       void* do16, float* lse, float* dd, int* qblk_far, float* dq, void* dkv16,
-                       void* dkT16, void* dvT16, float* dkr, hipStream_t s);
+                       void* do16, void* rec, int* qblk_far, float* dq, void* dkv16, void* dkT16,
+                       void* dvT16, float* dkr, hipStream_t s);
 // dst[c][dst_off + r] = src(r, c) (bf16) for r < R, zero for R <= r < Rpad, c
 // < C; src row-major with ld_src, or tiled (tile_index with C columns).
 // C and Rpad multiples of 64.
