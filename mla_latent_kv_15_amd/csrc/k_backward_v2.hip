@@ -240,6 +240,19 @@ __device__ __forceinline__ void mfma_drain_acc(f32x16 (&acc)[N]) {
   for (int k = 0; k < N; ++k) asm volatile("" : "+a"(acc[k]));
 }
 
+// Work-groups are dispatched round-robin over the eight XCDs (linear index
+// L = blockIdx.y * gridDim.x + blockIdx.x goes to XCD L % 8).  Each XCD takes
+// whole heads: its s-th work-group runs block xb = s % gridDim.x of head
+// 8 (s / gridDim.x) + L % 8, so all work-groups of one head stream its blocks
+// through one L2.  (gridDim.y = 128 heads.)
+__device__ inline void xcd_head_block(int& head, int& xb) {
+  const int gx = gridDim.x;
+  const int L = blockIdx.y * gx + blockIdx.x;
+  const int s = L >> 3;
+  xb = s % gx;
+  head = (s / gx) * 8 + (L & 7);
+}
+
 __device__ inline float swap_max(float v) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
@@ -265,10 +278,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
   __shared__ __attribute__((aligned(16))) char ring[kSlots * kSlotA];
   __shared__ int s_far[kWv];
   lds_char* const lds = (lds_char*)ring;
-  const int i = blockIdx.y, tid = threadIdx.x;
+  int i, xb;
+  xcd_head_block(i, xb);
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
   // the last query blocks see the most keys: dispatch them first
-  const int qb = (gridDim.x - 1 - blockIdx.x) * kWv + wave;   // this wave's 32 queries
+  const int qb = (gridDim.x - 1 - xb) * kWv + wave;   // this wave's 32 queries
   const int t = qb * kB + c;
   const bool t_ok = t < T;
   const int pos = t_ok ? positions[t] : -1;
@@ -427,9 +442,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
   __shared__ __attribute__((aligned(16))) char ring[kSlots * kSlotB];
   __shared__ int s_qf[kMaxQb];
   lds_char* const lds = (lds_char*)ring;
-  const int i = blockIdx.y, tid = threadIdx.x;
+  int i, xb;
+  xcd_head_block(i, xb);
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
-  const int wg_j0 = blockIdx.x * kWv * kB;
+  const int wg_j0 = xb * kWv * kB;   // the first key blocks see the most queries
   const int j0 = wg_j0 + wave * kB;   // this wave's block of 32 keys
   const int key = j0 + c;
   const bool key_ok = key < N;
