@@ -62,6 +62,19 @@ __device__ inline uint32_t pack2(float x, float y) {
 // V rows by 64 bytes, so that the four rows one transposing read serves to
 // 32 lanes at once start 64 banks apart.
 constexpr int kWQ = 4;                       // waves (query blocks) per work-group
+
+// Work-groups are dispatched round-robin over the eight XCDs (linear index
+// L = blockIdx.y * gridDim.x + blockIdx.x goes to XCD L % 8).  Each XCD takes
+// whole heads: its s-th work-group runs block xb = s % gridDim.x of head
+// 8 (s / gridDim.x) + L % 8, so all work-groups of one head stream its key
+// blocks through one L2.  (gridDim.y = 128 heads.)
+__device__ inline void xcd_head_block(int& head, int& xb) {
+  const int gx = gridDim.x;
+  const int L = blockIdx.y * gx + blockIdx.x;
+  const int s = L >> 3;
+  xb = s % gx;
+  head = (s / gx) * 8 + (L & 7);
+}
 constexpr int kKRow = kW + 8;                // LDS K row: 192 + 8 bf16
 constexpr int kVRow = kDv + 32;              // LDS V row: 128 + 32 bf16
 constexpr int kKElems = kKB * kKRow;         // 6400
@@ -74,9 +87,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const int32_t* __restrict__ positions, int T, int kv_len, __bf16* __restrict__ o) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][kBufElems];
   __shared__ int s_far[kWQ];
-  const int i = blockIdx.y, tid = threadIdx.x;
+  int i, xb;
+  xcd_head_block(i, xb);
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
-  const int t = (blockIdx.x * kWQ + wave) * kQB + c;
+  // the last query blocks see the most keys: dispatch them first
+  const int t = ((gridDim.x - 1 - xb) * kWQ + wave) * kQB + c;
   const bool t_ok = t < T;
   const int pos = t_ok ? positions[t] : -1;
   const bool valid = pos >= 0 && pos < kv_len;
