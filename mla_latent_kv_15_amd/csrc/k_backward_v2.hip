@@ -36,24 +36,15 @@
 // fp32 accumulation throughout.
 #include <math.h>
 
+#include "lds_stream.h"
 #include "mla_internal.h"
 
 namespace mla {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) v4bf16 lds_v4bf16;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+using namespace dev;
+
 
 constexpr int kH = 128;          // heads
 constexpr int kW = 192;          // query and key width
@@ -63,9 +54,6 @@ constexpr int kWv = 4;           // waves per work-group
 constexpr int kQK = kW / 16;     // K-steps of the 192-wide products (12)
 constexpr int kVK = kDv / 16;    // K-steps of the 128-wide products (8)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kVmcnt0 = 0x0f70;  // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone)
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, gfx9 family
-constexpr int kOob = 1 << 30;            // a source offset past every range
 
 // Blocks of 32 rows (keys, or queries) of one head stream through a ring of
 // LDS slots, kSlots - 1 blocks in flight, by direct-to-LDS loads: each load
@@ -115,27 +103,6 @@ __device__ inline int src_off(int r, int lane) {
   return j * kStrideV + 16 * ((v % 16) ^ sw16(j));
 }
 
-// A buffer resource over [p, p + bytes): a lane whose offset falls outside
-// reads no memory and writes zeros to LDS, so a block's missing rows (past N
-// or T) hold zeros and a padding load (bytes = 0) only writes zeros.
-__device__ inline i32x4 make_rsrc(const void* p, int bytes) {
-  const unsigned long long a = (unsigned long long)p;
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
-               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
-               __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
-}
-// One direct-to-LDS load (inline asm: it writes only LDS, no register is left
-// in flight; the ring's waits count these loads by hand).
-__device__ inline void dma16(const i32x4& rs, int voff, lds_char* dst) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
-               "s"(rs), "s"(m0)
-               : "m0", "memory");
-}
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 __device__ inline uint32_t pack2(float x, float y) {
   return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
@@ -214,30 +181,11 @@ __device__ __forceinline__ void mfma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_drain(f32x16& s, f32x16& dp) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s), "+v"(dp));
 }
-// The long-lived sums (dq; dK and dV) stay in the accumulation registers:
-// inline-asm MFMAs with an AGPR accumulator (with the builtin the compiler
-// moved them between the register files every block).  Their hazards are
-// covered by hand: a VALU write of a B operand (the bf16 numerators) or of
-// the zeroed sums is followed by more than the 2 wait states an MFMA read
-// of it needs (settle), and mfma_drain_acc waits out the last product before
-// the sums are read.
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
+// The dq, dK and dV sums take mfma_agpr (AGPR accumulators); their B operands
+// are the bf16 numerators, a VALU write just before: settle puts more than the
+// 2 wait states an MFMA read of them needs in between.
 __device__ __forceinline__ void settle(bf16x8 (&x)[2]) {
   asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]));
-}
-template <int N>
-__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
-#pragma unroll
-  for (int k = 0; k < N; ++k) asm volatile("" : "+a"(acc[k]));
-  asm volatile("s_nop 4" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void mfma_drain_acc(f32x16 (&acc)[N]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-  for (int k = 0; k < N; ++k) asm volatile("" : "+a"(acc[k]));
 }
 
 // Work-groups are dispatched round-robin over the eight XCDs (linear index

@@ -890,6 +890,25 @@ int mla_mha_decode_attention(const mla_config* cfg, const void* q, const void* k
   return MLA_OK;
 }
 
+namespace mla {
+namespace {
+// Y = alpha * X . W^T over M rows: the tiled MFMA GEMM from 128 rows on, the
+// weight-streaming one (tile t) below that or where no tile fits the shape.
+constexpr int kTiledGemmRows = 128;
+hipError_t gemm_rows(GemmTile t, int M, int N, int K, const void* X, long ldx, const void* W,
+                     bool wt, void* Y, long ldy, bool out_f32, float alpha, hipStream_t s,
+                     int y_grp = 0, long y_grp_stride = 0) {
+  if (M >= kTiledGemmRows) {
+    const hipError_t e = tgemm(M, N, K, X, ldx, W, wt, Y, ldy, out_f32, alpha, s, y_grp,
+                               y_grp_stride);
+    if (e != hipErrorNotSupported) return e;
+  }
+  return wgemm(t, M, N, K, X, ldx, 0, 0, W, Y, ldy, 0, out_f32, alpha, s, false, false, wt, y_grp,
+               y_grp_stride);
+}
+}  // namespace
+}  // namespace mla
+
 int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const float* q,
                            const int32_t* positions, const void* kv_cache, int num_pages,
                            const int32_t* page_table, int max_pages, int kv_len, int T,
@@ -920,18 +939,18 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
     carve_bwd_v2(c, g, T, N, &b);
     const int nq = g.n_h * g.d_h, Np = attn_bwd_v2_npad(N);
     MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, N, b.rows16, b.k16, s));
-    MLA_TRY(wgemm(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, 0, 0, w->W_UK, b.k16,
-                  (long)g.n_h * dqw, 0, false, 1.f, s, false, false, wt, g.d_h, dqw));
-    MLA_TRY(wgemm(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, 0, 0, w->W_UV, b.v16, nq, 0,
-                  false, 1.f, s, false, false, wt));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, w->W_UK, wt, b.k16,
+                      (long)g.n_h * dqw, false, 1.f, s, g.d_h, dqw));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, N, nq, g.d_c, b.rows16, g.row, w->W_UV, wt, b.v16, nq,
+                      false, 1.f, s));
     MLA_TRY(attn_bwd_v2(g, N, T, q, dO, positions, b.k16, b.v16, b.q16, b.do16, b.rec,
                         b.qblk_far, dq, b.dkv16, b.dkT16, b.dvT16, b.dkr, s));
     // dW_UK,i = sum_j dk^C_ij c_j^T (rows [head, dim], contraction over keys)
     MLA_TRY(transpose16(b.rows16, g.row, false, g.d_c, N, Np, b.cT16, Np, 0, s));
-    MLA_TRY(wgemm(GemmTile{4, 1}, nq, g.d_c, Np, b.dkT16, Np, 0, 0, b.cT16, dW_UK, g.d_c, 0,
-                  true, 1.f, s));
-    MLA_TRY(wgemm(GemmTile{4, 1}, nq, g.d_c, Np, b.dvT16, Np, 0, 0, b.cT16, dW_UV, g.d_c, 0,
-                  true, 1.f, s));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, nq, g.d_c, Np, b.dkT16, Np, b.cT16, false, dW_UK, g.d_c,
+                      true, 1.f, s));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, nq, g.d_c, Np, b.dvT16, Np, b.cT16, false, dW_UV, g.d_c,
+                      true, 1.f, s));
     // dc_j = [dk^C_j | dv_j] . [W_UK ; W_UV] in two K halves, summed with
     // the heads' dk^R into dC
     MLA_TRY(transpose16(w->W_UK, g.d_c, wt, g.d_c, nq, nq, b.wT16, 2L * nq, 0, s));
@@ -1018,24 +1037,24 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
     void* o16 = p.o;                                        // [T][n_h d_h]
     const long nq = (long)g.n_h * g.d_h;
     // c^Q = W_DQ h; q^C_i = scale W_UQ,i c^Q into columns 0..127 of head i
-    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.d_cq, g.d, h, g.d, 0, 0, w->W_DQ, cq16, g.d_cq, 0, false,
-                  1.f, s, false, false, wt));
-    MLA_TRY(wgemm(GemmTile{4, 1}, T, (int)nq, g.d_cq, cq16, g.d_cq, 0, 0, w->W_UQ, q16, wq, 0,
-                  false, g.scale, s, false, false, wt, g.d_h, g.d_h + g.d_r));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.d_cq, g.d, h, g.d, w->W_DQ, wt, cq16, g.d_cq, false,
+                      1.f, s));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, T, (int)nq, g.d_cq, cq16, g.d_cq, w->W_UQ, wt, q16, wq,
+                      false, g.scale, s, g.d_h, g.d_h + g.d_r));
     // scale W_QR,i c^Q in fp32, rotated and packed into columns 128..191
-    MLA_TRY(wgemm(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, 0, 0, w->W_QR, qr,
-                  (long)g.n_h * g.d_r, 0, true, g.scale, s, false, false, wt));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, w->W_QR, wt, qr,
+                      (long)g.n_h * g.d_r, true, g.scale, s));
     MLA_TRY(prefill_rope_q_v2(g, qr, positions, T, rope_table, rope_len, q16, s));
     // order A: k_ij = [W_UK,i c_j | k^R_j] and v_ij = W_UV,i c_j from the rows
     MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, kv_len, rows16, k16, s));
-    MLA_TRY(wgemm(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, 0, 0, w->W_UK, k16, wq,
-                  0, false, 1.f, s, false, false, wt, g.d_h, g.d_h + g.d_r));
-    MLA_TRY(wgemm(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, 0, 0, w->W_UV, v16, nq,
-                  0, false, 1.f, s, false, false, wt));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, w->W_UK, wt, k16,
+                      wq, false, 1.f, s, g.d_h, g.d_h + g.d_r));
+    MLA_TRY(gemm_rows(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, w->W_UV, wt, v16, nq,
+                      false, 1.f, s));
     // causal attention, then u = W_O o
     MLA_TRY(attn_prefill_v2(g, q16, k16, v16, positions, T, kv_len, o16, s));
-    MLA_TRY(wgemm(GemmTile{5, 1}, T, g.d, (int)nq, o16, nq, 0, 0, w->W_O, out, g.d, 0, false, 1.f,
-                  s, false, false, wt));
+    MLA_TRY(gemm_rows(GemmTile{5, 1}, T, g.d, (int)nq, o16, nq, w->W_O, wt, out, g.d, false, 1.f,
+                      s));
     return MLA_OK;
   }
   // query: c^Q, then per head [q^C_i | q^R_i] (192-d at V2), RoPE on q^R

@@ -268,6 +268,15 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
                  long y_split_stride, bool out_f32, float alpha, hipStream_t s,
                  bool x_blocked = false, bool y_blocked = false, bool w_tiled = false,
                  int y_grp = 0, long y_grp_stride = 0);
+// Tiled MFMA GEMM for many rows (k_tgemm.hip): Y = alpha * X . W^T, X [M][K]
+// bf16 rows (ldx), W [N][K] bf16 row-major or tiled, Y bf16 or fp32 (ldy;
+// y_grp > 0, bf16: column n at (n / y_grp) * y_grp_stride + n % y_grp).
+// hipErrorNotSupported (nothing launched) when no tile fits the shape: K a
+// multiple of 32, N of 128 or 192 or 320.
+int tgemm_pick(int M, int N, int K);
+hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bool w_tiled,
+                 void* Y, long ldy, bool out_f32, float alpha, hipStream_t s, int y_grp = 0,
+                 long y_grp_stride = 0);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i and q_abs[b][i][512:576] =
