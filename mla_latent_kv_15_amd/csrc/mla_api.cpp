@@ -1036,14 +1036,17 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
     void* v16 = p.vbuf;                                     // [kv_len][n_h][d_h]
     void* o16 = p.o;                                        // [T][n_h d_h]
     const long nq = (long)g.n_h * g.d_h;
-    // c^Q = W_DQ h; q^C_i = scale W_UQ,i c^Q into columns 0..127 of head i
+    // the query carries the softmax scale and log2(e): the attention kernel's
+    // scores come out in log2 units
+    const float qscale = g.scale * 1.4426950408889634f;
+    // c^Q = W_DQ h; q^C_i = qscale W_UQ,i c^Q into columns 0..127 of head i
     MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.d_cq, g.d, h, g.d, w->W_DQ, wt, cq16, g.d_cq, false,
                       1.f, s));
     MLA_TRY(gemm_rows(GemmTile{4, 1}, T, (int)nq, g.d_cq, cq16, g.d_cq, w->W_UQ, wt, q16, wq,
-                      false, g.scale, s, g.d_h, g.d_h + g.d_r));
-    // scale W_QR,i c^Q in fp32, rotated and packed into columns 128..191
+                      false, qscale, s, g.d_h, g.d_h + g.d_r));
+    // qscale W_QR,i c^Q in fp32, rotated and packed into columns 128..191
     MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, w->W_QR, wt, qr,
-                      (long)g.n_h * g.d_r, true, g.scale, s));
+                      (long)g.n_h * g.d_r, true, qscale, s));
     MLA_TRY(prefill_rope_q_v2(g, qr, positions, T, rope_table, rope_len, q16, s));
     // order A: k_ij = [W_UK,i c_j | k^R_j] and v_ij = W_UV,i c_j from the rows
     MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, kv_len, rows16, k16, s));

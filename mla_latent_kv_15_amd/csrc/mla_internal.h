@@ -164,8 +164,9 @@ hipError_t attn_prefill_generic(const Geo& g, const float* q, const float* kbuf,
                                 const float* vbuf, const int32_t* positions, int T, int kv_len,
                                 int rope_len, float* o, hipStream_t s);
 // The same causal attention on bf16 MFMA for the DeepSeek-V2 head shape:
-// q [T][n_h][192], k [kv_len][n_h][192], v [kv_len][n_h][128] bf16 (p rounded
-// to bf16, fp32 accumulation); o is bf16 [T][n_h * d_h].
+// q [T][n_h][192] (times the softmax scale and log2 e), k [kv_len][n_h][192],
+// v [kv_len][n_h][128] bf16 (p rounded to bf16, fp32 accumulation); o is bf16
+// [T][n_h * d_h].
 bool prefill_v2_supported(const Geo& g);
 hipError_t attn_prefill_v2(const Geo& g, const void* q, const void* kbuf, const void* vbuf,
                            const int32_t* positions, int T, int kv_len, void* o, hipStream_t s);
