@@ -431,6 +431,31 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const __bf16* __restri
   }
 }
 
+// dC[j] = [sum_z lat[z][j] | sum_i dkr[i][j]], one work-group per cached row,
+// both sums in a fixed order: two latent columns per thread, and the RoPE
+// part as four quarters of the heads per column, added through LDS.
+__global__ __launch_bounds__(256) void bwd_dc_v2_kernel(int N, const float* __restrict__ lat,
+                                                        int splits,
+                                                        const float* __restrict__ dkr,
+                                                        float* __restrict__ dC) {
+  constexpr int kC = 512, kR = kW - kDv, kRow = kC + kR;
+  __shared__ float part[4][kR];
+  const int j = blockIdx.x, tid = threadIdx.x;
+#pragma unroll
+  for (int e = tid; e < kC; e += 256) {
+    float a = 0.f;
+    for (int z = 0; z < splits; ++z) a += lat[((long)z * N + j) * kC + e];
+    dC[(long)j * kRow + e] = a;
+  }
+  const int d = tid & (kR - 1), qtr = tid >> 6;   // 64 dims x 4 quarters of the heads
+  float a = 0.f;
+#pragma unroll 8
+  for (int i = qtr * (kH / 4); i < (qtr + 1) * (kH / 4); ++i) a += dkr[((long)i * N + j) * kR + d];
+  part[qtr][d] = a;
+  __syncthreads();
+  if (tid < kR) dC[(long)j * kRow + kC + tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
 // q (fp32, RoPE applied) times the softmax scale, and dO, as bf16 rows
 __global__ __launch_bounds__(256) void bwd_inputs_v2_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ dO, long nq,
@@ -477,6 +502,21 @@ hipError_t attn_bwd_v2(const Geo& g, int N, int T, const float* q, const float* 
                      dim3(64 * kWv), 0, s, (const __bf16*)q16, (const __bf16*)do16,
                      (const __bf16*)k16, (const __bf16*)v16, (const f32x4*)rec, qblk_far, T, N,
                      attn_bwd_v2_npad(N), (__bf16*)dkv16, (__bf16*)dkT16, (__bf16*)dvT16, dkr);
+  return hipGetLastError();
+}
+
+int bwd_lat_splits(int N) {
+  const int units = tgemm_units(N, 512, 2 * kH * kDv);
+  if (units <= 0) return 1;
+  int sp = 1;
+  while (sp < 32 && units * sp * 2 <= 256) sp *= 2;
+  return sp;
+}
+
+hipError_t bwd_dc_v2(int N, const float* lat, int splits, const float* dkr, float* dC,
+                     hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dc_v2_kernel, dim3(N), dim3(256), 0, s, N, lat, splits, dkr, dC);
   return hipGetLastError();
 }
 

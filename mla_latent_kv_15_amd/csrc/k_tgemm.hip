@@ -36,11 +36,14 @@ __device__ inline int row_swz(int r) {
   return U == 8 ? (r >> 1) & 7 : (r >> 2) & 3;
 }
 
+// K split: work-group z of the grid's third dimension takes columns
+// [z kc, (z + 1) kc) and writes its fp32 partial at Y + z y_split_stride.
 template <int BM, int BN, int WM, int WN, int BK, int S, bool F32, bool WT>
-__global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K,
+__global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int kc,
                                                        const __bf16* __restrict__ X, long ldx,
                                                        const __bf16* __restrict__ W,
-                                                       void* __restrict__ Y, long ldy, float alpha,
+                                                       void* __restrict__ Y, long ldy,
+                                                       long y_split_stride, float alpha,
                                                        int y_grp, long y_grp_stride) {
   static_assert(WM * WN == 8, "eight waves");
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
@@ -60,7 +63,8 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K,
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wm = wave % WM, wn = wave / WM;
-  const int nk = K / BK;
+  const int nk = kc / BK;
+  const int kz = blockIdx.z * kc;   // this split's first column
 
   // Load k of wave w carries units 64 (w + 8k) .. of a step: W rows, then X
   // rows, then padding.  voff: the lane's source offset from the step's first
@@ -84,8 +88,9 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K,
     }
   }
   const int mvalid = min(BM, M - m0);
-  const __bf16* wblk = W + (WT ? (long)(n0 / 16) * (K / 32) * 512 : (long)n0 * K);
-  const __bf16* xblk = X + (long)m0 * ldx;
+  const __bf16* wblk =
+      W + (WT ? (long)(n0 / 16) * (K / 32) * 512 + (long)(kz / 32) * 512 : (long)n0 * K + kz);
+  const __bf16* xblk = X + (long)m0 * ldx + kz;
   // step kb into stage `stage` (padding past the last step: zero ranges)
   auto issue = [&](int kb, int stage) {
     const bool real = kb < nk;
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K,
                          alpha * a[4 * g + 3]};
         const long col = y_grp > 0 ? (long)(n / y_grp) * y_grp_stride + n % y_grp : n;
         if constexpr (F32) {
-          *(f32x4*)((float*)Y + (long)m * ldy + col) = v;
+          *(f32x4*)((float*)Y + blockIdx.z * y_split_stride + (long)m * ldy + col) = v;
         } else {
           const u32x2 pk = {__builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[0], (__bf16)v[1]}),
                             __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2], (__bf16)v[3]})};
@@ -200,6 +205,12 @@ int n_compute_units() {
 
 }  // namespace
 
+int tgemm_units(int M, int N, int K) {
+  const int t = tgemm_pick(M, N, K);
+  if (t < 0) return -1;
+  return ((M + kTiles[t].bm - 1) / kTiles[t].bm) * (N / kTiles[t].bn);
+}
+
 int tgemm_pick(int M, int N, int K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % kBK != 0) return -1;
   const int G = n_compute_units();
@@ -221,33 +232,32 @@ int tgemm_pick(int M, int N, int K) {
 
 hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bool w_tiled,
                  void* Y, long ldy, bool out_f32, float alpha, hipStream_t s, int y_grp,
-                 long y_grp_stride) {
+                 long y_grp_stride, int splits, long y_split_stride) {
   if (M <= 0) return hipSuccess;
-  const int t = tgemm_pick(M, N, K);
+  if (splits < 1 || K % (splits * kBK) != 0 || (splits > 1 && (!out_f32 || y_grp > 0)))
+    return hipErrorNotSupported;
+  const int kc = K / splits;
+  const int t = tgemm_pick(M, N, kc);
   if (t < 0 || ldx % 8 != 0 || ldx < K || (long)256 * ldx * 2 >= 0x7fffffffL || ldy % 4 != 0 ||
       (y_grp > 0 && (y_grp % 32 != 0 || y_grp_stride % 4 != 0 || out_f32)) ||
       (w_tiled && N % 16 != 0))
     return hipErrorNotSupported;
   const dim3 block(512);
-#define MLA_TG(BM, BN, WM, WN, S)                                                              \
-  do {                                                                                         \
-    const dim3 grid(N / BN, (M + BM - 1) / BM);                                                \
-    if (out_f32 && w_tiled)                                                                    \
-      hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, true, true>), grid, block, 0, s, M, N,  \
-                         K, (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, alpha, y_grp,     \
-                         y_grp_stride);                                                        \
-    else if (out_f32)                                                                          \
-      hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, true, false>), grid, block, 0, s, M, N, \
-                         K, (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, alpha, y_grp,     \
-                         y_grp_stride);                                                        \
-    else if (w_tiled)                                                                          \
-      hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, false, true>), grid, block, 0, s, M, N, \
-                         K, (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, alpha, y_grp,     \
-                         y_grp_stride);                                                        \
-    else                                                                                       \
-      hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, false, false>), grid, block, 0, s, M,   \
-                         N, K, (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, alpha, y_grp,  \
-                         y_grp_stride);                                                        \
+#define MLA_TG_GO(BM, BN, WM, WN, S, F32, WT)                                                  \
+  hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, F32, WT>),                          \
+                     dim3(N / BN, (M + BM - 1) / BM, splits), block, 0, s, M, N, K, kc,       \
+                     (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, y_split_stride, alpha,   \
+                     y_grp, y_grp_stride)
+#define MLA_TG(BM, BN, WM, WN, S)                        \
+  do {                                                   \
+    if (out_f32 && w_tiled)                              \
+      MLA_TG_GO(BM, BN, WM, WN, S, true, true);          \
+    else if (out_f32)                                    \
+      MLA_TG_GO(BM, BN, WM, WN, S, true, false);         \
+    else if (w_tiled)                                    \
+      MLA_TG_GO(BM, BN, WM, WN, S, false, true);         \
+    else                                                 \
+      MLA_TG_GO(BM, BN, WM, WN, S, false, false);        \
   } while (0)
   switch (t) {
     case 0: MLA_TG(256, 256, 2, 4, 4); break;
@@ -256,6 +266,7 @@ hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bo
     default: MLA_TG(128, 192, 4, 2, 6); break;
   }
 #undef MLA_TG
+#undef MLA_TG_GO
   return hipGetLastError();
 }
 

@@ -244,7 +244,7 @@ void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
   w->cT16 = c.take(2 * (size_t)g.d_c * Np);
   w->wT16 = c.take(2 * (size_t)g.d_c * 2 * hd);
   w->dkr = (float*)c.take(sizeof(float) * (size_t)g.n_h * N * g.d_r);
-  w->lat = (float*)c.take(sizeof(float) * 2 * (size_t)N * g.d_c);
+  w->lat = (float*)c.take(sizeof(float) * (size_t)bwd_lat_splits(N) * N * g.d_c);
 }
 bool use_bwd_v2(const Geo& g, int T, int N) {
   return attn_bwd_v2_supported(g) && T <= attn_bwd_v2_max_queries() &&
@@ -951,13 +951,14 @@ int mla_attention_backward(const mla_config* cfg, const mla_weights* w, const fl
                       true, 1.f, s));
     MLA_TRY(gemm_rows(GemmTile{4, 1}, nq, g.d_c, Np, b.dvT16, Np, b.cT16, false, dW_UV, g.d_c,
                       true, 1.f, s));
-    // dc_j = [dk^C_j | dv_j] . [W_UK ; W_UV] in two K halves, summed with
-    // the heads' dk^R into dC
+    // dc_j = [dk^C_j | dv_j] . [W_UK ; W_UV] in K chunks, summed with the
+    // heads' dk^R into dC
     MLA_TRY(transpose16(w->W_UK, g.d_c, wt, g.d_c, nq, nq, b.wT16, 2L * nq, 0, s));
     MLA_TRY(transpose16(w->W_UV, g.d_c, wt, g.d_c, nq, nq, b.wT16, 2L * nq, nq, s));
-    MLA_TRY(wgemm(GemmTile{4, 2}, N, g.d_c, 2 * nq, b.dkv16, 2L * nq, 0, 0, b.wT16, b.lat, g.d_c,
-                  (long)N * g.d_c, true, 1.f, s));
-    MLA_TRY(attn_bwd_dc(g, N, b.lat, b.lat + (size_t)N * g.d_c, b.dkr, dC, s));
+    const int lsp = bwd_lat_splits(N);
+    MLA_TRY(tgemm(N, g.d_c, 2 * nq, b.dkv16, 2L * nq, b.wT16, false, b.lat, g.d_c, true, 1.f, s, 0,
+                  0, lsp, (long)N * g.d_c));
+    MLA_TRY(bwd_dc_v2(N, b.lat, lsp, b.dkr, dC, s));
     return MLA_OK;
   }
   BwdWs b;

@@ -211,6 +211,12 @@ hipError_t attn_bwd_v2(const Geo& g, int N, int T, const float* q, const float* 
 // C and Rpad multiples of 64.
 hipError_t transpose16(const void* src, long ld_src, bool tiled, int C, int R, int Rpad, void* dst,
                        long ld_dst, long dst_off, hipStream_t s);
+// The K split of the latent-gradient product over N cached rows (so that its
+// tiles fill the compute units), and dC [N][576] = [sum of the splits'
+// partials lat [splits][N][512] | sum over the heads of dkr [128][N][64]].
+int bwd_lat_splits(int N);
+hipError_t bwd_dc_v2(int N, const float* lat, int splits, const float* dkr, float* dC,
+                     hipStream_t s);
 
 // MHA-equivalent decode attention over a [pages][page][2][n_h][d_h] cache
 // (k_mha.hip): d_h a multiple of 16 with d_h / 16 a power of two <= 64.
@@ -273,11 +279,14 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
 // bf16 rows (ldx), W [N][K] bf16 row-major or tiled, Y bf16 or fp32 (ldy;
 // y_grp > 0, bf16: column n at (n / y_grp) * y_grp_stride + n % y_grp).
 // hipErrorNotSupported (nothing launched) when no tile fits the shape: K a
-// multiple of 32, N of 128 or 192 or 320.
+// multiple of 32, N of 128 or 192 or 320.  splits > 1 (fp32 Y only): equal K
+// chunks, chunk z's partial at Y + z * y_split_stride.  tgemm_units: the
+// output tiles the shape takes (-1: none).
 int tgemm_pick(int M, int N, int K);
+int tgemm_units(int M, int N, int K);
 hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bool w_tiled,
                  void* Y, long ldy, bool out_f32, float alpha, hipStream_t s, int y_grp = 0,
-                 long y_grp_stride = 0);
+                 long y_grp_stride = 0, int splits = 1, long y_split_stride = 0);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i and q_abs[b][i][512:576] =
