@@ -8,6 +8,8 @@
 // S = Q K^T, P = softmax_causal(S), O = P V and the incoming dO:
 //   dP = dO V^T,  D_t = sum_j P_tj dP_tj (= dO_t . O_t),
 //   dS = P o (dP - D),  dV = P^T dO,  dK = dS^T Q,  dq = scale * dS K.
+// The kernels take Q times log2(e) (q16), so that S comes out in log2 units
+// for exp2; dK is scaled back by ln 2 as it leaves.
 // A query whose position lies outside [0, kv_len) gets NaN rows of P and dS
 // over every key, so its dq row and every key's dK and dV are NaN (the
 // generic path's rule).
@@ -80,11 +82,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
   const bool valid = pos >= 0 && pos < N;
   // keys this query sees: 0 .. last (an invalid position: all of them, NaN)
   const int last = t_ok ? (valid ? pos : N - 1) : -1;
-  int far = last;
-  for (int off = 32; off >= 1; off >>= 1) far = max(far, __shfl_xor(far, off));
+  int far = last, near = last;   // the block's furthest and nearest last keys
+  for (int off = 32; off >= 1; off >>= 1) {
+    far = max(far, __shfl_xor(far, off));
+    near = min(near, __shfl_xor(near, off));
+  }
   if (lane == 0) {
     s_far[wave] = far;
-    if (i == 0 && qb * kB < T) qblk_far[qb] = far;
+    if (i == 0 && qb * kB < T) {
+      qblk_far[2 * qb] = far;
+      qblk_far[2 * qb + 1] = near;
+    }
   }
   // Q^T and dO^T as B operands: K-step ks holds dims 16 ks + 8h .. + 7
   bf16x8 qv[kQK], dv[kVK];
@@ -144,13 +152,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
     if (j0 <= far) {
       f32x16 s, dp;
       scores(lds + (b % kSlots) * kSlotA, lane, s, dp);
-      float bm = -INFINITY;
+      // (log2 units: q16 carries log2 e; the mask only where the block
+      // reaches past some query's last key)
+      if (j0 + kB - 1 > near) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        s[r] = key <= last ? s[r] * kLog2e : -INFINITY;
-        bm = fmaxf(bm, s[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          s[r] = key <= last ? s[r] : -INFINITY;
+        }
       }
+      float bm = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
       const float mn = fmaxf(m, swap_max(bm));
       const float ref = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m - ref);
@@ -185,11 +198,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
       const int ln = lane;
       f32x16 s, dp;
       scores(slot, ln, s, dp);
+      if (j0 + kB - 1 > near) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float p = key <= last ? __builtin_amdgcn_exp2f(fmaf(s[r], kLog2e, -lse)) : 0.f;
-        s[r] = p * (dp[r] - dd);   // dS^T
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float p = key <= last ? __builtin_amdgcn_exp2f(s[r] - lse) : 0.f;
+          s[r] = p * (dp[r] - dd);   // dS^T
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - lse) * (dp[r] - dd);
       }
       bf16x8 pb[2];
       rows_as_b(s, pb);
@@ -220,6 +238,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_v2_kernel(
 // key side: dK (its latent part per head, its RoPE part per head) and dV
 // ---------------------------------------------------------------------------
 constexpr int kMaxQb = 2048;                       // query blocks (their far keys sit in LDS)
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTrPitch = kB + 8;                   // keys per LDS row of the transposed tiles
 static_assert(kWv * kDv * kTrPitch * 2 <= kSlots * kSlotB, "transposed tiles fit the ring");
 
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
     __bf16* __restrict__ dkv16, __bf16* __restrict__ dkT16, __bf16* __restrict__ dvT16,
     float* __restrict__ dkr) {
   __shared__ __attribute__((aligned(16))) char ring[kSlots * kSlotB];
-  __shared__ int s_qf[kMaxQb];
+  __shared__ int s_qf[kMaxQb], s_qn[kMaxQb];
   lds_char* const lds = (lds_char*)ring;
   int i, xb;
   xcd_head_block(i, xb);
@@ -255,7 +274,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
   // The blocks' far keys are read once into LDS (nqb <= kMaxQb), so that the
   // scan below costs no memory round trips.
   const int nqb = (T + kB - 1) / kB;
-  for (int e = tid; e < nqb; e += 256) s_qf[e] = qblk_far[e];
+  for (int e = tid; e < nqb; e += 256) {
+    s_qf[e] = qblk_far[2 * e];
+    s_qn[e] = qblk_far[2 * e + 1];
+  }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);   // the ring below counts its own loads
   __syncthreads();
   auto qfar = [&](int qb) { return s_qf[qb]; };
@@ -311,8 +333,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
 #pragma unroll
       for (int ks = 1; ks < kVK; ++ks) mfma_acc(dp, row16(slot, ln, ks), vv[ks]);
       mfma_drain(s, dp);
-      // rows 8 g + 4h + e: the records of those four queries
+      // rows 8 g + 4h + e: the records of those four queries (S in log2
+      // units: q16 carries log2 e).  The mask only where some (query, key)
+      // pair of the block is not seen (a key past N stays exactly zero even
+      // beside a NaN query row).
       f32x16 ds;
+      const bool all_seen = j0 + kB - 1 <= s_qn[qb];
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -320,11 +346,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
           const int r = 4 * g + e;
           const f32x4 st =
               *(const lds_f32x4*)(slot + 16 * (kUnitsW + kUnitsV + 8 * g + 4 * h + e));
-          // (a key past N stays exactly zero even beside a NaN query row)
-          const bool seen = key_ok && key < __float_as_int(st[2]);
-          const float p = seen ? __builtin_amdgcn_exp2f(fmaf(s[r], kLog2e, -st[0])) : 0.f;
-          s[r] = p;                                  // P
-          ds[r] = seen ? p * (dp[r] - st[1]) : 0.f;  // dS
+          if (all_seen) {
+            const float p = __builtin_amdgcn_exp2f(s[r] - st[0]);
+            s[r] = p;                   // P
+            ds[r] = p * (dp[r] - st[1]);  // dS
+          } else {
+            const bool seen = key_ok && key < __float_as_int(st[2]);
+            const float p = seen ? __builtin_amdgcn_exp2f(s[r] - st[0]) : 0.f;
+            s[r] = p;
+            ds[r] = seen ? p * (dp[r] - st[1]) : 0.f;
+          }
         }
       bf16x8 pbP[2], pbS[2];
       rows_as_b(s, pbP);
@@ -346,6 +377,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_v2_kernel(
   mfma_drain_acc(accK);
   mfma_drain_acc(accV);
   wait_vm<0>();      // the padding loads still write LDS
+  // dK^T += Q16^T dS with Q16 = scale log2(e) q: dK = ln 2 . accK
+#pragma unroll
+  for (int dt = 0; dt < kW / 32; ++dt) accK[dt] *= kLn2;
   __syncthreads();   // and every wave is done with the ring
   // lane (c, h) holds dims 32 dt + 8 g + 4h .. + 3 (g = r >> 2) of key `key`
   if (key_ok) {
@@ -456,7 +490,8 @@ __global__ __launch_bounds__(256) void bwd_dc_v2_kernel(int N, const float* __re
   if (tid < kR) dC[(long)j * kRow + kC + tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
 }
 
-// q (fp32, RoPE applied) times the softmax scale, and dO, as bf16 rows
+// q (fp32, RoPE applied) times `scale` (the softmax scale times log2 e), and
+// dO, as bf16 rows
 __global__ __launch_bounds__(256) void bwd_inputs_v2_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ dO, long nq,
                                                             long nd, float scale,
@@ -492,8 +527,9 @@ hipError_t attn_bwd_v2(const Geo& g, int N, int T, const float* q, const float* 
   if (!attn_bwd_v2_supported(g) || T > attn_bwd_v2_max_queries() || N > attn_bwd_v2_max_keys())
     return hipErrorInvalidValue;
   const long nq = (long)T * kH * kW, nd = (long)T * kH * kDv;
+  // q16 = scale log2(e) q: the scores come out in log2 units
   hipLaunchKernelGGL(bwd_inputs_v2_kernel, dim3((unsigned)((nq / 4 + 255) / 256)), dim3(256), 0, s,
-                     q, dO, nq, nd, g.scale, (__bf16*)q16, (__bf16*)do16);
+                     q, dO, nq, nd, g.scale * kLog2e, (__bf16*)q16, (__bf16*)do16);
   hipLaunchKernelGGL(attn_bwd_dq_v2_kernel, dim3((T + kWv * kB - 1) / (kWv * kB), kH),
                      dim3(64 * kWv), 0, s, (const __bf16*)q16, (const __bf16*)do16,
                      (const __bf16*)k16, (const __bf16*)v16, positions, T, N, g.scale, (f32x4*)rec,

@@ -237,7 +237,7 @@ void carve_bwd_v2(Carver& c, const Geo& g, int T, int N, BwdWsV2* w) {
   w->q16 = c.take(2 * (size_t)T * wq);
   w->do16 = c.take(2 * (size_t)T * hd);
   w->rec = c.take(16 * (size_t)g.n_h * T);
-  w->qblk_far = (int*)c.take(sizeof(int) * (size_t)((T + 31) / 32));
+  w->qblk_far = (int*)c.take(2 * sizeof(int) * (size_t)((T + 31) / 32));
   w->dkv16 = c.take(2 * (size_t)N * 2 * hd);
   w->dkT16 = c.take(2 * hd * Np);
   w->dvT16 = c.take(2 * hd * Np);

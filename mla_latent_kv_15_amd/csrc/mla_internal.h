@@ -192,7 +192,8 @@ hipError_t attn_bwd_dc(const Geo& g, int N, const float* lat_k, const float* lat
 // (k_backward_v2.hip).  Inputs: q [T][128][192] and dO [T][128][128] fp32, k16
 // [N][128][192] and v16 [N][128][128] bf16.  Scratch: q16, do16 (the bf16
 // scaled query and dO), rec [128][T] x 16 bytes (LSE, D and the keys seen per
-// query and head), qblk_far [ceil(T / 32)].  Outputs:
+// query and head), qblk_far [ceil(T / 32)][2] (each query block's furthest and
+// nearest last key).  Outputs:
 // dq [T][128][192] fp32 (final), dkr [128][N][64] fp32 (per head), and dk^C,
 // dv in bf16 as rows dkv16 [N][2 * 128 * 128] (all heads' dk^C, then all
 // heads' dv) and key-contiguous dkT16, dvT16 [128 * 128][Npad] with zeros past
