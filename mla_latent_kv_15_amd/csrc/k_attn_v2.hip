@@ -194,6 +194,11 @@ __device__ inline void lds_store(int byte, T v) {
 // ring data itself: an explicit vmcnt wait for its own sub-tile, then a
 // barrier.  (The loads write no registers, so no register result of an asm
 // load is ever left in flight.)
+//
+// Each cache row is read once per step, so the loads carry the nontemporal
+// hint (nt): on the batch-64 workload attention plus merge took 4.6% less
+// time with it.  A plain read stream of the cache's size showed the same
+// thing, 6.5 TB/s with the hint against 5.9 without.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct Refill {
   i32x4 rs;   // buffer descriptor (base, valid bytes) in scalar registers
@@ -213,7 +218,7 @@ __device__ inline i32x4 make_rsrc(const void* p, int bytes) {
 __device__ inline void lds_dma16(const i32x4& rs, int voff, int lds_byte) {
   const int m0 = __builtin_amdgcn_readfirstlane(
       (int)(uintptr_t)((lds_char*)g_lds + lds_byte));
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                :: "v"(voff), "s"(rs), "s"(m0) : "m0");
 }
 
