@@ -378,7 +378,7 @@ def prefill_measure(args, T):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch64", choices=sorted(WORKLOADS))
     ap.add_argument("--splits", type=int, default=0)

@@ -823,24 +823,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
     }
 
     // ---- unnormalised partial (m, l, o~): o~ rounded to bf16, in register
-    // order (8-byte piece 4x + a of a lane holds elements 4a .. 4a + 3 of
+    // order (16-byte piece 2x + e of a lane holds elements 8e .. 8e + 7 of
     // accumulator x); merged later
     {
       const int ln = lane_here();
-      uint2* dst = (uint2*)(part_o + (long)k * kHeads * kDc) + (wave * 64 + ln);
+      uint4* dst = (uint4*)(part_o + (long)k * kHeads * kDc) + (wave * 64 + ln);
 #pragma unroll
       for (int x = 0; x < 16; ++x)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float f0 = acc[x][4 * a], f1 = acc[x][4 * a + 1];
-          const float f2 = acc[x][4 * a + 2], f3 = acc[x][4 * a + 3];
+        for (int e = 0; e < 2; ++e) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          const bf16x2 p0 = {(__bf16)f0, (__bf16)f1}, p1 = {(__bf16)f2, (__bf16)f3};
-          dst[(x * 4 + a) * kThreads] =
-              uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_bit_cast(
+                uint32_t, bf16x2{(__bf16)acc[x][8 * e + 2 * j], (__bf16)acc[x][8 * e + 2 * j + 1]});
+          dst[(x * 2 + e) * kThreads] = uint4{w[0], w[1], w[2], w[3]};
           // one accumulator at a time: the next query is arriving in the
           // VGPRs, and reading all accumulators ahead would not fit beside it
-          if (a == 3) __builtin_amdgcn_sched_barrier(0);
+          if (e == 1) __builtin_amdgcn_sched_barrier(0);
         }
       // l over all 32 tokens of a sub-tile: lanes (m32, 0) and (m32, 1) hold
       // halves of head m32's sum
@@ -913,16 +914,16 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
   // the two halves of the work-group sum the even and the odd segments, four
   // segments' loads in flight per half at once
   constexpr int kU = 4;
-  uint2 v[kU][16];
+  uint4 v[kU][8];   // [u][2 mb + e]: elements 8e .. 8e + 7 of accumulator 4 mb + n
   auto load_round = [&](int c0, int s0, int nc) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (s0 + 2 * u >= nc) break;
-      const uint2* src = (const uint2*)(part_o + (long)(k0 + c0 + s0 + 2 * u) * kHeads * kDc) + tt;
+      const uint4* src = (const uint4*)(part_o + (long)(k0 + c0 + s0 + 2 * u) * kHeads * kDc) + tt;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) v[u][4 * mb + a] = src[((4 * mb + n) * 4 + a) * kThreads];
+        for (int e = 0; e < 2; ++e) v[u][2 * mb + e] = src[((4 * mb + n) * 2 + e) * kThreads];
     }
   };
   // the first round's partials go out before the softmax statistics, which
@@ -974,11 +975,16 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
         if (s0 + 2 * u >= nc) break;
         const float ws = w[s0 + 2 * u][hd_l];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[r] += ws * f32x4{__uint_as_float(v[u][r].x << 16),
-                               __uint_as_float(v[u][r].x & 0xffff0000u),
-                               __uint_as_float(v[u][r].y << 16),
-                               __uint_as_float(v[u][r].y & 0xffff0000u)};
+        for (int r = 0; r < 8; ++r) {
+          acc[2 * r] += ws * f32x4{__uint_as_float(v[u][r].x << 16),
+                                   __uint_as_float(v[u][r].x & 0xffff0000u),
+                                   __uint_as_float(v[u][r].y << 16),
+                                   __uint_as_float(v[u][r].y & 0xffff0000u)};
+          acc[2 * r + 1] += ws * f32x4{__uint_as_float(v[u][r].z << 16),
+                                       __uint_as_float(v[u][r].z & 0xffff0000u),
+                                       __uint_as_float(v[u][r].w << 16),
+                                       __uint_as_float(v[u][r].w & 0xffff0000u)};
+        }
       }
     }
   }
@@ -1047,15 +1053,15 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
   const int hd_l = lane & 31;
   // this wave's segments s = q, q + kRunWaves, ...: the first kU in flight now
   constexpr int kU = 8;
-  uint2 v[kU][4];
+  uint4 v[kU][2];   // [u][e]: elements 8e .. 8e + 7 of accumulator 4 mz + n
   auto issue = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int su = min(s0 + kRunWaves * u, cnt - 1);   // past the end: re-read, weight 0
-      const uint2* src =
-          (const uint2*)(part_o + (long)(k0 + su) * kHeads * kDc) + wo * 64 + lane;
+      const uint4* src =
+          (const uint4*)(part_o + (long)(k0 + su) * kHeads * kDc) + wo * 64 + lane;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) v[u][a] = src[((4 * mz + n) * 4 + a) * kThreads];
+      for (int e = 0; e < 2; ++e) v[u][e] = src[((4 * mz + n) * 2 + e) * kThreads];
     }
   };
   issue(q);
@@ -1095,11 +1101,16 @@ __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtr
       if (su >= cnt) continue;
       const float ws = s_ml[su][hd_l].x;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        acc[mb] += ws * f32x4{__uint_as_float(v[u][mb].x << 16),
-                              __uint_as_float(v[u][mb].x & 0xffff0000u),
-                              __uint_as_float(v[u][mb].y << 16),
-                              __uint_as_float(v[u][mb].y & 0xffff0000u)};
+      for (int e = 0; e < 2; ++e) {
+        acc[2 * e] += ws * f32x4{__uint_as_float(v[u][e].x << 16),
+                                 __uint_as_float(v[u][e].x & 0xffff0000u),
+                                 __uint_as_float(v[u][e].y << 16),
+                                 __uint_as_float(v[u][e].y & 0xffff0000u)};
+        acc[2 * e + 1] += ws * f32x4{__uint_as_float(v[u][e].z << 16),
+                                     __uint_as_float(v[u][e].z & 0xffff0000u),
+                                     __uint_as_float(v[u][e].w << 16),
+                                     __uint_as_float(v[u][e].w & 0xffff0000u)};
+      }
     }
   }
   if (q > 0)

@@ -242,7 +242,8 @@ hipError_t attn_decode_v2(const Geo& g, const void* q_tiles, bool q_log2e, const
 // Rows [B][128][576] (bf16) rearranged into the query-tile layout (values
 // unchanged).
 hipError_t pack_query_tiles(const void* rows, int B, void* tiles, hipStream_t s);
-// (part_o: bf16 [segments][128 * 512] in the accumulator's register order;
+// (part_o: bf16 [segments][128 * 512] in the accumulator's register order,
+//  16 bytes (8 elements) of one lane per piece;
 //  part_ml: fp32 [segments][128][2] = (reference max in nats, sum of numerators))
 // Weight-streaming MFMA GEMM: Y = alpha * X . W^T (W [N][K] bf16, row-major
 // or, w_tiled, in the tiled layout; X bf16 rows);
