@@ -43,7 +43,8 @@ NO_SCRATCH = {"k_attn_v2.hip": ("combine_v2", "qtile_pack"), "k_gemm_v2.hip": ("
               "k_mha.hip": ("mha_decode",),
               "k_prefill.hip": ("attn_prefill_v2", "prefill_rows_v2", "prefill_rope_q_v2"),
               "k_backward_v2.hip": ("attn_bwd_dq_v2", "attn_bwd_dkv_v2", "transpose16",
-                                    "bwd_inputs_v2")}
+                                    "bwd_inputs_v2"),
+              "k_tgemm.hip": ("tgemm",)}
 _SPILL_OPS = ("scratch_", "buffer_store", "buffer_load", "v_accvgpr_read", "v_accvgpr_write",
               "v_accvgpr_mov")
 

@@ -105,10 +105,22 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int 
       dma16(part[k] == 0 ? rw : (part[k] == 1 ? rx : rz), voff[k], dst + 8192 * k);
   };
 
+  // Up to 128 fp32 sums per lane stay in the accumulation registers.  The
+  // 256 x 320 tile has 160: at two waves per SIMD the accumulation
+  // registers hold at most 128 of a wave's 256, so its sums live in ordinary
+  // registers (and the wait states around the MFMA chain cover all ten of
+  // them in one statement, which nothing can be scheduled across).
+  constexpr bool kVacc = TM * TN > 8;
+  static_assert(!kVacc || TM * TN == 10, "register sums: the 256 x 320 tile only");
   f32x16 acc[TN * TM];
 #pragma unroll
   for (int t = 0; t < TN * TM; ++t) acc[t] = f32x16{};
-  settle_acc(acc);
+  if constexpr (kVacc)
+    asm volatile("s_nop 4"
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]),
+                   "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]));
+  else
+    settle_acc(acc);
   static_assert(BK == 32, "the loop below holds two K-steps of 16 per step");
   const int xc = row_swz<U>(c);
   // the operands of K-step ks (0 or 1) of the step in `stage`
@@ -127,7 +139,14 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int 
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) mfma_agpr(acc[tn * TM + tm], a[tn], b[tm]);
+      for (int tm = 0; tm < TM; ++tm) {
+        if constexpr (kVacc)
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+              : "+v"(acc[tn * TM + tm])
+              : "v"(a[tn]), "v"(b[tm]));
+        else
+          mfma_agpr(acc[tn * TM + tm], a[tn], b[tm]);
+      }
   };
   // The ring holds steps kb .. kb + S - 1.  The second K-step's operands of
   // step kb stay in registers across the barrier that frees its stage, so the
@@ -152,7 +171,12 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int 
     mult(a1, b1);
     cur = nx;
   }
-  mfma_drain_acc(acc);
+  if constexpr (kVacc)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]),
+                   "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]));
+  else
+    mfma_drain_acc(acc);
   wait_vm<0>();   // the padding loads of the ring's tail still write LDS
 
   // acc[tn][tm] is Y^T: lane (c, h) holds row m = ... + c of Y, columns
@@ -186,8 +210,11 @@ struct TileCfg {
 };
 // The candidate tiles in order of preference (larger tiles reuse each
 // operand more); the first that fills at least 90% of a round of work-groups
-// on the compute units wins, else the one that fills the most.
-constexpr TileCfg kTiles[] = {{256, 256}, {128, 320}, {256, 128}, {128, 192}};
+// on the compute units wins, else the one that fills the most.  (256 x 320:
+// a 4096 x 5120 output is exactly one round of 256 tiles, and each 32-wide
+// K-step moves 36 KB into LDS for 5.2 MFLOP, 142 flop/B, against 91 for
+// 128 x 320.)
+constexpr TileCfg kTiles[] = {{256, 320}, {256, 256}, {128, 320}, {256, 128}, {128, 192}};
 
 int n_compute_units() {
   static int cus = 0;
@@ -260,9 +287,10 @@ hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bo
       MLA_TG_GO(BM, BN, WM, WN, S, false, false);        \
   } while (0)
   switch (t) {
-    case 0: MLA_TG(256, 256, 2, 4, 4); break;
-    case 1: MLA_TG(128, 320, 4, 2, 4); break;
-    case 2: MLA_TG(256, 128, 4, 2, 5); break;
+    case 0: MLA_TG(256, 320, 4, 2, 3); break;
+    case 1: MLA_TG(256, 256, 2, 4, 4); break;
+    case 2: MLA_TG(128, 320, 4, 2, 4); break;
+    case 3: MLA_TG(256, 128, 4, 2, 5); break;
     default: MLA_TG(128, 192, 4, 2, 6); break;
   }
 #undef MLA_TG

@@ -224,13 +224,15 @@ def test_v2_long_context():
 
 # ---------------------------------------------------------------------------
 # V2 causal prefill (order A) of 4096 tokens, rows against the oracle and the
-# last 64 rows against mla_decode (order B) at kv_len = p + 1
+# last 64 rows against mla_decode (order B) at kv_len = p + 1; and of 3700
+# tokens, whose projections end in a partial block of output rows (the
+# 3700 x 5120 output product takes 15 blocks of 256 rows, 116 in the last)
 # ---------------------------------------------------------------------------
 
-def test_v2_prefill_4096():
+@pytest.mark.parametrize("T", [4096, 3700])
+def test_v2_prefill_long(T):
     s = inputs.V2
     layer = Layer(s, 5, "bf16")
-    T = 4096
     H = inputs.make_hidden(T, s, 5, "bf16")
     paged = inputs.make_paged([T], 64, 5, shuffle=True)
     rope = layer.rope(T)
@@ -250,7 +252,7 @@ def test_v2_prefill_4096():
     log("v2 prefill: oracle rows")
     H64 = H.f64()
     c, kr = oracle.latent_rows(H64, layer.W64["W_DKV"], layer.W64["W_KR"], np.arange(T), BASE)
-    sel = [0, 1, 63, 64, 65, 700, T - 1]
+    sel = [0, 1, 63, 64, 65, 700, 3583, 3584, 3650, T - 1]
     ref = oracle.prefill_order_a(H64, np.arange(T), c, kr, layer.W64, s.n_h, BASE, rows=sel)
     err = oracle.max_rel_error(u[sel], ref)
     log(f"prefill vs oracle: {err:.3e}")
