@@ -22,7 +22,7 @@
 // turn the numerators into the B operand of O^T[dim][query] += V^T . P^T,
 // whose V^T operand comes from transposing LDS reads.  Accumulation is fp32
 // with an online softmax in the log2 domain; O is rescaled only in the
-// blocks where some query's maximum rises.  Key blocks past a wave's
+// blocks where some query's maximum passes its reference by more than 8.  Key blocks past a wave's
 // furthest query position are skipped (causality).  Q, K and V arrive as
 // bf16 (written so by the MFMA GEMMs); o is written as bf16 rows
 // [T][n_h * d_h], the input of the W_O product.
@@ -54,6 +54,8 @@ __device__ __forceinline__ void drain_o(f32x16 (&o)[4]) {
 __device__ __forceinline__ void settle_o(f32x16 (&o)[4]) {
   asm volatile("s_nop 4" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
 }
+
+constexpr float kLazy = 8.f;   // log2 units a block's maximum may exceed the reference
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kbuf, const __bf16* __restrict__ vbuf,
@@ -110,7 +112,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
 #pragma unroll
   for (int d = 0; d < kDv / 32; ++d) acc[d] = f32x16{};
   settle_o(acc);
-  float m = -INFINITY, l = 0.f;   // running max (log2 units) and sum of this lane's query
+  // this lane's query: the reference u (log2 units) of O and l, and l, the
+  // sum of the numerators 2^(s - u).  Any reference gives the same softmax;
+  // u moves only when a block's maximum exceeds it by more than kLazy, so
+  // the numerators stay at most 2^kLazy and O is rarely rescaled.
+  float u = -INFINITY, l = 0.f;
 
   // block kb in slot kb % kPSlots; the loop body is instantiated once per slot
   // so that the slot's offset is an immediate of the LDS reads
@@ -140,20 +146,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       float bm = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
-      const float mn = fmaxf(m, swap_max(bm));
-      const float ref = mn == -INFINITY ? 0.f : mn;   // no key seen yet: all numerators 0
-      const float alpha = __builtin_amdgcn_exp2f(m - ref);
-      float ps = 0.f;
+      bm = swap_max(bm);
+      // a new reference where the block's maximum passes u + kLazy (the
+      // first key a query sees always does: u starts at -inf, alpha = 0 with
+      // O and l still 0); no key seen yet: u stays -inf, numerators 0
+      const bool raise = bm > u + kLazy;
+      const float nu = raise ? bm : u;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(u - nu) : 1.f;
+      const float ref = nu == -INFINITY ? 0.f : nu;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
-        ps += s[r];
-      }
-      l = l * alpha + swap_sum(ps);
-      m = mn;
-      // rescale O only where some query's maximum rose (alpha < 1); a query
-      // that has seen no key yet has alpha = 0 and O = 0
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
+      u = nu;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
         drain_o(acc);
 #pragma unroll
         for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
@@ -161,6 +165,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       }
       bf16x8 pb[2];
       rows_as_b(s, pb);
+      // l sums the bf16-rounded numerators, the values the product uses:
+      // pairs dotted with (1, 1); pb holds 16 of the query's 32 keys, the
+      // lane 32 apart the other 16
+      {
+        // (constant shuffle indices: each pair is its own register)
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float ps0 = 0.f, ps1 = 0.f;
+#define MLA_PAIR_SUM(e)                                                                       \
+  ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[0], pb[0], 2 * e, 2 * e + 1), \
+                                        one, ps0, false);                                     \
+  ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[1], pb[1], 2 * e, 2 * e + 1), \
+                                        one, ps1, false);
+        MLA_PAIR_SUM(0)
+        MLA_PAIR_SUM(1)
+        MLA_PAIR_SUM(2)
+        MLA_PAIR_SUM(3)
+#undef MLA_PAIR_SUM
+        l = l * alpha + swap_sum(ps0 + ps1);
+      }
       settle(pb);
       // O^T += V^T . P^T: the A operand of dim tile d, K-step kap is dim
       // 32 d + c of the block's keys 16 kap + 8h .. + 7
