@@ -109,6 +109,23 @@ __device__ inline bf16x8 tr_operand(const lds_char* slot, int lane, int k0, int 
   const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(slot + 16 * u1 + half));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// The same operand from byte offsets formed once: tr_offsets gives the two
+// reads' offsets within a slot (lane-dependent, loop-invariant), tr_read
+// reads them from a slot, so that a loop over blocks issues each read as a
+// register plus the slot's immediate offset.
+template <bool W24>
+__device__ inline void tr_offsets(int lane, int k0, int D0, int& o0, int& o1) {
+  const int j = k0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int p = D0 / 8 + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int half = 8 * (lane & 1);
+  o0 = 16 * (W24 ? unit24(j, p) : unit16(j, p)) + half;
+  o1 = 16 * (W24 ? unit24(j + 4, p) : unit16(j + 4, p)) + half;
+}
+__device__ inline bf16x8 tr_read(const lds_char* slot, int o0, int o1) {
+  const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(slot + o0));
+  const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(slot + o1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 // Row reads: lane (c, h) gets unit 2 ks + h of row c (an A operand).
 __device__ inline bf16x8 row24(const lds_char* slot, int lane, int ks) {
   const int c = lane & 31, h = lane >> 5;

@@ -117,6 +117,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
   // u moves only when a block's maximum exceeds it by more than kLazy, so
   // the numerators stay at most 2^kLazy and O is rarely rescaled.
   float u = -INFINITY, l = 0.f;
+  // byte offsets of the V^T operand reads (K-step kap, dim tile d), formed
+  // once; the empty asm keeps each a single register, so a read is that
+  // register plus the slot's immediate (left to itself the compiler shares
+  // the lanes' 8-byte half between them and adds it back at every read)
+  int tro[2][kDv / 32][2];
+#pragma unroll
+  for (int kap = 0; kap < 2; ++kap)
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d) {
+      tr_offsets<false>(lane, 16 * kap, 32 * d, tro[kap][d][0], tro[kap][d][1]);
+      asm volatile("" : "+v"(tro[kap][d][0]), "+v"(tro[kap][d][1]));
+    }
 
   // block kb in slot kb % kPSlots; the loop body is instantiated once per slot
   // so that the slot's offset is an immediate of the LDS reads
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
         for (int d = 0; d < kDv / 32; ++d)
-          mfma_acc(acc[d], tr_operand<false>(slot, lane, 16 * kap, 32 * d), pb[kap]);
+          mfma_acc(acc[d], tr_read(slot, tro[kap][d][0], tro[kap][d][1]), pb[kap]);
     }
   };
   static_assert(kPSlots == 3, "the loop below runs three slots");
