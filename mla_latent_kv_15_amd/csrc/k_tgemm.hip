@@ -7,12 +7,13 @@
 // weight-streaming kernel's 64-row blocks: one work-group of eight waves per
 // compute unit owns a BM x BN tile of Y and walks K in steps of 32.  Each
 // step's W rows (BN x 32) and X rows (BM x 32) go to LDS by direct-to-LDS
-// buffer loads through a ring of four to six stages, so that the next three
-// to five steps' loads fly while this step's MFMAs run.  The products are v_mfma_f32_32x32x16_bf16 with the W
-// rows as the A operand and the X rows as the B operand, i.e. the tile is
-// formed as Y^T: every lane then owns one row of Y and four consecutive
-// columns per result group, stored as one 16-byte (fp32) or 8-byte (bf16)
-// write.  The fp32 sums stay in the accumulation registers.
+// buffer loads through a ring of three to six stages, so that the next two
+// to five steps' loads fly while this step's MFMAs run.  The products are
+// v_mfma_f32_32x32x16_bf16 with the W rows as the A operand and the X rows
+// as the B operand, i.e. the tile is formed as Y^T: every lane then owns one
+// row of Y and four consecutive columns per result group, stored as one
+// 16-byte (fp32) or 8-byte (bf16) write.  The fp32 sums stay in the
+// accumulation registers (in ordinary registers for the 256 x 320 tile).
 #include "lds_stream.h"
 #include "mla_internal.h"
 
