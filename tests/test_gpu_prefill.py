@@ -57,3 +57,53 @@ def test_v2_prefill_scattered_positions():
     err = oracle.max_rel_error(u[sel], ref)
     log(f"prefill vs oracle: {err:.3e}")
     assert err < TOL["bf16"]
+
+
+def test_v2_prefill_score_jumps():
+    """Hidden rows scaled by 6 at positions 40, 130 and 250: their keys lift
+    the score maximum of many (query, head) pairs by far more than 8 log2
+    units in blocks after the first, so the prefill's softmax reference moves
+    (and O is rescaled) mid-stream, not only at a query's first key block.
+    That the data does so is checked on the CPU from the oracle's scores;
+    rows after each jump against the fp64 oracle, the last 64 against decode."""
+    s = inputs.V2
+    layer = Layer(s, 72, "bf16")
+    N = 300
+    jumps = [40, 130, 250]
+    f = inputs.normal((N, s.d), 1.0, 72, inputs.STREAM_HIDDEN)
+    f[jumps] *= 6.0   # (larger factors make the bf16 rounding of the scores dominate)
+    H = inputs.Array(f, "bf16")
+    H64 = H.f64()
+    W = layer.W64
+    c, kr = oracle.latent_rows(H64, W["W_DKV"], W["W_KR"], np.arange(N), BASE)
+    # the data's own jumps: running maximum (log2 units) over 32-key blocks
+    scale = oracle.default_scale(s.d_h, s.d_r) / np.log(2.0)
+    t = N - 1
+    q_c, q_r = oracle.query(H64[t], W["W_DQ"], W["W_UQ"], W["W_QR"], t, s.n_h, BASE)
+    lifted = 0
+    for i in range(s.n_h):
+        k = np.concatenate([c @ W["W_UK"][i * s.d_h:(i + 1) * s.d_h].T, kr], axis=1)
+        sc = k @ np.concatenate([q_c[i], q_r[i]]) * scale
+        run = np.maximum.accumulate([sc[j0:j0 + 32].max() for j0 in range(0, N, 32)])
+        lifted += int((np.diff(run) > 8.0).any())
+    log(f"prefill score jumps: {lifted} of {s.n_h} heads of query {t} lift their maximum by > 8")
+    assert lifted >= 8
+    paged = inputs.make_paged([N], 64, 72, shuffle=True)
+    rope = layer.rope(N + 16)
+    cache = layer.empty_cache(paged.num_pages)
+    h_all = device.tensor(H)
+    layer.append(h_all, np.arange(N), paged.slots(0), cache, rope)
+    pos = np.arange(N)
+    u = device.to_f64(layer.prefill(h_all, pos, cache, paged.page_table[0], N, rope))
+    assert np.isfinite(u).all()
+    P = np.arange(N - 64, N)
+    dec = device.to_f64(layer.decode(h_all[N - 64:], P, cache, np.repeat(paged.page_table, 64, 0),
+                                     P + 1, N, rope))
+    xerr = oracle.max_rel_error(u[N - 64:], dec)
+    log(f"prefill vs decode (jumps): {xerr:.3e}")
+    assert xerr < 2 * TOL["bf16"]
+    sel = [0, 39, 40, 41, 100, 129, 130, 131, 249, 250, 251, 299]
+    ref = oracle.prefill_order_a(H64, pos, c, kr, W, s.n_h, BASE, rows=sel)
+    err = oracle.max_rel_error(u[sel], ref)
+    log(f"prefill vs oracle (jumps): {err:.3e}")
+    assert err < TOL["bf16"]
