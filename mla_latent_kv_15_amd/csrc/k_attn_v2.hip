@@ -574,16 +574,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
       // quarter of j-1's accumulation.  Iteration 0 accumulates P = 0 over
       // sub-tile 0; the drain after the loop accumulates the last sub-tile.
       // Every pass starts with exactly two positions loaded ahead.
+      // scalar set-up of iteration jj's ring loads (position base + jj + 2).
+      // Iteration j uses the set-up formed during iteration j - 1, in the
+      // shadow of its score MFMAs (between iterations the MFMAs would idle
+      // through it); iteration 0's is formed here, for this pass.
+      auto ring_setup = [&](int jj) {
+        if (jj + 2 < nsub) return refill_at(base + jj + 2);
+        if (pf_next) return refill_next(base + jj + 2, nxt, jj + 2 - nsub);
+        return no_refill(base + jj + 2);
+      };
+      Refill rf_next = ring_setup(0);
 #pragma clang loop unroll(disable)
       for (int j = 0; j < nsub; ++j) {
-        // scalar set-up of the ring loads (issued below), ahead of the waits
-        Refill rf;
-        if (j + 2 < nsub)
-          rf = refill_at(base + j + 2);
-        else if (pf_next)
-          rf = refill_next(base + j + 2, nxt, j + 2 - nsub);
-        else
-          rf = no_refill(base + j + 2);
+        const Refill rf = rf_next;
         static_assert(kInstsPerWave == 9, "vmcnt immediates below assume 9 loads per sub-tile");
         // positions base and base + 1 landed before the query did (except at
         // the work-group start); from j = 1 on, only the loads of position
@@ -654,6 +657,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_v2_kernel(
           constexpr int r = decltype(rc)::value;
           qk(rc);
           if constexpr (r < kInstsPerWave) ring_load(rf, r, wave, lat16, rope_off);
+          // the next iteration's ring set-up (past the last iteration it
+          // forms an unused descriptor: no cursor step, at most a repeated
+          // mark of a bad page in the next segment)
+          if constexpr (r == 12) rf_next = ring_setup(j + 1);
           if constexpr (r == 19) pv_read_at(dv, 1);
           if constexpr (r >= 3 && r < 19) {
             constexpr int idx = r - 3, n = idx >> 2, mb = idx & 3;
