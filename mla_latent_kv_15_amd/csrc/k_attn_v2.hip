@@ -23,7 +23,8 @@
 //    cache operand of the second contraction comes straight from
 //    ds_read_b64_tr_b16 (no register shuffles), the softmax is an exp2 and a
 //    pack per score in one branch-free block beside the accumulation MFMAs,
-//    and the ring refill between sub-tiles is a short run of scalar selects.
+//    and the scalar set-up of the next sub-tile's ring loads is formed in
+//    the shadow of the current sub-tile's score MFMAs.
 //  * 32-token sub-tiles stream through a four-slot LDS ring with 16-byte
 //    direct-to-LDS buffer loads, two sub-tiles in flight while the scores of
 //    sub-tile j and the accumulation of sub-tile j-1 run.  A slot holds the
