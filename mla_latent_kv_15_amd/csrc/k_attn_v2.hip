@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(512) void combine_v2_kernel(PlanPtrs plan,
 // statistics are formed, and the waves' sums are added at the end in a fixed
 // order.
 // ---------------------------------------------------------------------------
-constexpr int kRunWaves = 4;   // waves per merge work-group, each a share of the segments
+constexpr int kRunWaves = 8;   // waves per merge work-group, each a share of the segments
 constexpr int kRunSegs = 264;   // (m, l) kept in LDS: every automatic plan (<= CUs + 1 segments)
 
 __global__ __launch_bounds__(64 * kRunWaves) void combine_v2_runs_kernel(PlanPtrs plan,
