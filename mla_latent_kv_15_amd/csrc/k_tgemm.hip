@@ -14,6 +14,8 @@
 // row of Y and four consecutive columns per result group, stored as one
 // 16-byte (fp32) or 8-byte (bf16) write.  The fp32 sums stay in the
 // accumulation registers (in ordinary registers for the 256 x 320 tile).
+// Those four columns are two whole (2k, 2k + 1) pairs, so a bf16 Y can also
+// leave the epilogue RoPE-rotated (the prefill's q^R) with no lane exchange.
 #include "lds_stream.h"
 #include "mla_internal.h"
 
@@ -45,7 +47,10 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int 
                                                        const __bf16* __restrict__ W,
                                                        void* __restrict__ Y, long ldy,
                                                        long y_split_stride, float alpha,
-                                                       int y_grp, long y_grp_stride) {
+                                                       int y_grp, long y_grp_stride,
+                                                       const int32_t* __restrict__ rope_pos,
+                                                       const float* __restrict__ rope_tab,
+                                                       int rope_len) {
   static_assert(WM * WN == 8, "eight waves");
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "whole MFMA tiles");
@@ -186,15 +191,36 @@ __global__ __launch_bounds__(512, 1) void tgemm_kernel(int M, int N, int K, int 
   for (int tm = 0; tm < TM; ++tm) {
     const int m = m0 + (wm * TM + tm) * 32 + c;
     if (m >= M) continue;
+    // RoPE (bf16 Y only): row m's position, -1 where the table has no row
+    int pos = -1;
+    if (!F32 && rope_tab) {
+      const int p = rope_pos[m];
+      pos = p >= 0 && p < rope_len ? p : -1;
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + (wn * TN + tn) * 32 + 8 * g + 4 * h;
         const f32x16& a = acc[tn * TM + tm];
-        const f32x4 v = {alpha * a[4 * g], alpha * a[4 * g + 1], alpha * a[4 * g + 2],
-                         alpha * a[4 * g + 3]};
+        f32x4 v = {alpha * a[4 * g], alpha * a[4 * g + 1], alpha * a[4 * g + 2],
+                   alpha * a[4 * g + 3]};
         const long col = y_grp > 0 ? (long)(n / y_grp) * y_grp_stride + n % y_grp : n;
+        if (!F32 && rope_tab) {
+          // the lane's four columns are the pairs (2k, 2k + 1), (2k + 2,
+          // 2k + 3) of a column group, k = (n % y_grp) / 2 even: each pair
+          // turns by the angle of pair k (k + 1) at position pos, the
+          // table's (cos, sin) entries k, k + 1 being one 16-byte read
+          if (pos >= 0) {
+            const f32x4 cs =
+                *(const f32x4*)(rope_tab + ((long)pos * (y_grp / 2) + (n % y_grp) / 2) * 2);
+            v = f32x4{v[0] * cs[0] - v[1] * cs[1], v[0] * cs[1] + v[1] * cs[0],
+                      v[2] * cs[2] - v[3] * cs[3], v[2] * cs[3] + v[3] * cs[2]};
+          } else {
+            v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                      __builtin_nanf("")};
+          }
+        }
         if constexpr (F32) {
           *(f32x4*)((float*)Y + blockIdx.z * y_split_stride + (long)m * ldy + col) = v;
         } else {
@@ -260,10 +286,13 @@ int tgemm_pick(int M, int N, int K) {
 
 hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bool w_tiled,
                  void* Y, long ldy, bool out_f32, float alpha, hipStream_t s, int y_grp,
-                 long y_grp_stride, int splits, long y_split_stride) {
+                 long y_grp_stride, int splits, long y_split_stride, const int32_t* rope_pos,
+                 const float* rope_tab, int rope_len) {
   if (M <= 0) return hipSuccess;
   if (splits < 1 || K % (splits * kBK) != 0 || (splits > 1 && (!out_f32 || y_grp > 0)))
     return hipErrorNotSupported;
+  if (rope_tab && (!rope_pos || out_f32 || y_grp <= 0 || rope_len <= 0))
+    return hipErrorInvalidValue;
   const int kc = K / splits;
   const int t = tgemm_pick(M, N, kc);
   if (t < 0 || ldx % 8 != 0 || ldx < K || (long)256 * ldx * 2 >= 0x7fffffffL || ldy % 4 != 0 ||
@@ -275,7 +304,7 @@ hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bo
   hipLaunchKernelGGL((tgemm_kernel<BM, BN, WM, WN, kBK, S, F32, WT>),                          \
                      dim3(N / BN, (M + BM - 1) / BM, splits), block, 0, s, M, N, K, kc,       \
                      (const __bf16*)X, ldx, (const __bf16*)W, Y, ldy, y_split_stride, alpha,   \
-                     y_grp, y_grp_stride)
+                     y_grp, y_grp_stride, rope_pos, rope_tab, rope_len)
 #define MLA_TG(BM, BN, WM, WN, S)                        \
   do {                                                   \
     if (out_f32 && w_tiled)                              \

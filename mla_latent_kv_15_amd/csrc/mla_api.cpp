@@ -1045,10 +1045,20 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* h,
                       1.f, s));
     MLA_TRY(gemm_rows(GemmTile{4, 1}, T, (int)nq, g.d_cq, cq16, g.d_cq, w->W_UQ, wt, q16, wq,
                       false, qscale, s, g.d_h, g.d_h + g.d_r));
-    // qscale W_QR,i c^Q in fp32, rotated and packed into columns 128..191
-    MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, w->W_QR, wt, qr,
-                      (long)g.n_h * g.d_r, true, qscale, s));
-    MLA_TRY(prefill_rope_q_v2(g, qr, positions, T, rope_table, rope_len, q16, s));
+    // qscale RoPE(W_QR,i c^Q) into columns 128..191 of head i: turned and
+    // packed in the tiled product's epilogue, else (fewer rows than a tile
+    // takes) the product in fp32, then the rotation
+    hipError_t qe = hipErrorNotSupported;
+    if (T >= kTiledGemmRows)
+      qe = tgemm(T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, w->W_QR, wt, (__bf16*)q16 + g.d_h, wq,
+                 false, qscale, s, g.d_r, g.d_h + g.d_r, 1, 0, positions, rope_table, rope_len);
+    if (qe == hipErrorNotSupported) {
+      MLA_TRY(gemm_rows(GemmTile{4, 1}, T, g.n_h * g.d_r, g.d_cq, cq16, g.d_cq, w->W_QR, wt, qr,
+                        (long)g.n_h * g.d_r, true, qscale, s));
+      MLA_TRY(prefill_rope_q_v2(g, qr, positions, T, rope_table, rope_len, q16, s));
+    } else {
+      MLA_TRY(qe);
+    }
     // order A: k_ij = [W_UK,i c_j | k^R_j] and v_ij = W_UV,i c_j from the rows
     MLA_TRY(prefill_rows_v2(g, kv_cache, num_pages, page_table, kv_len, rows16, k16, s));
     MLA_TRY(gemm_rows(GemmTile{4, 1}, kv_len, (int)nq, g.d_c, rows16, g.row, w->W_UK, wt, k16,

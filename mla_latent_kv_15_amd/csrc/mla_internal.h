@@ -283,12 +283,18 @@ hipError_t wgemm(const GemmTile& t, int M, int N, int K, const void* X, long ldx
 // hipErrorNotSupported (nothing launched) when no tile fits the shape: K a
 // multiple of 32, N of 128 or 192 or 320.  splits > 1 (fp32 Y only): equal K
 // chunks, chunk z's partial at Y + z * y_split_stride.  tgemm_units: the
-// output tiles the shape takes (-1: none).
+// output tiles the shape takes (-1: none).  rope_tab (bf16 Y with y_grp > 0
+// only): each y_grp-column group of row m is the RoPE input, and Y receives
+// it turned by position rope_pos[m] (pairs (2k, 2k + 1) by the table's
+// (cos, sin) entry k of that position, y_grp / 2 entries per position; NaN
+// where the position is outside [0, rope_len)).
 int tgemm_pick(int M, int N, int K);
 int tgemm_units(int M, int N, int K);
 hipError_t tgemm(int M, int N, int K, const void* X, long ldx, const void* W, bool w_tiled,
                  void* Y, long ldy, bool out_f32, float alpha, hipStream_t s, int y_grp = 0,
-                 long y_grp_stride = 0, int splits = 1, long y_split_stride = 0);
+                 long y_grp_stride = 0, int splits = 1, long y_split_stride = 0,
+                 const int32_t* rope_pos = nullptr, const float* rope_tab = nullptr,
+                 int rope_len = 0);
 hipError_t splitk_reduce(int M, int N, int S, const float* part, long split_stride, void* out,
                          long ldo, hipStream_t s, bool blocked = false);
 // q_abs[b][i][0:512] = scale * W_UK,i^T q^C_i and q_abs[b][i][512:576] =

@@ -1,7 +1,7 @@
 """Causal prefill (mla_prefill, order A) on the DeepSeek-V2 head shape, where
 the attention runs on bf16 MFMA (one wave per block of 32 queries and head):
 query positions in any order with repeats, a context of 300 rows (not a
-multiple of the 32-key block), 66 queries (a ragged last block), queries at
+multiple of the 32-key block), 66 or 147 queries (a ragged last block), queries at
 positions 0 and N - 1, and a position outside the context (NaN row).  Rows
 against the fp64 oracle (a sample) and against mla_decode at kv_len = p + 1
 (all rows).
@@ -22,7 +22,10 @@ def _lib():
     require_lib()
 
 
-def test_v2_prefill_scattered_positions():
+@pytest.mark.parametrize("n_rand", [59, 140])
+def test_v2_prefill_scattered_positions(n_rand):
+    """66 queries take the weight-streaming products (RoPE query input in
+    fp32, then rotated); 147 the tiled ones, RoPE in the product's epilogue."""
     s = inputs.V2
     layer = Layer(s, 71, "bf16")
     N = 300
@@ -34,11 +37,11 @@ def test_v2_prefill_scattered_positions():
     log("v2 prefill, scattered positions: append 300 rows")
     layer.append(h_all, np.arange(N), paged.slots(0), cache, rope)
     rng = np.random.default_rng(71)
-    src = np.concatenate([[0, N - 1, 31, 32, 33, 31], rng.integers(0, N, 59), [7]])
+    src = np.concatenate([[0, N - 1, 31, 32, 33, 31], rng.integers(0, N, n_rand), [7]])
     pos = src.copy()
     pos[-1] = N + 5   # outside the context
     hq = h_all[torch.from_numpy(src).cuda()]
-    log("v2 prefill, scattered positions: prefill of 66 queries")
+    log(f"v2 prefill, scattered positions: prefill of {len(src)} queries")
     u = device.to_f64(layer.prefill(hq, pos, cache, paged.page_table[0], N, rope))
     assert np.isnan(u[-1]).all()
     assert np.isfinite(u[:-1]).all()
