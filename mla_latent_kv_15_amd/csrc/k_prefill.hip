@@ -254,6 +254,8 @@ __global__ __launch_bounds__(256) void prefill_rows_v2_kernel(
 
 // q[t][i][128 ..] = RoPE(qr[t][i][0 .. 64], p_t) as bf16 (qr fp32, already
 // scaled); NaN for a position outside the table.  One thread per pair.
+// (Prefills of fewer rows than the tiled GEMM takes; from there on that
+// GEMM's epilogue rotates q^R.)
 __global__ __launch_bounds__(256) void prefill_rope_q_v2_kernel(
     const float* __restrict__ qr, const int32_t* __restrict__ positions, long n,
     const float* __restrict__ rope, int rope_len, __bf16* __restrict__ q) {

@@ -173,7 +173,8 @@ hipError_t attn_prefill_v2(const Geo& g, const void* q, const void* kbuf, const 
 // Its inputs besides the GEMM outputs: the cached rows [kv_len][576] bf16
 // gathered through the page table (NaN for a bad page id) with k^R_j
 // copied into every head's key, and RoPE of the scaled fp32 q^R into q
-// (NaN for a position outside the table).
+// (NaN for a position outside the table; the products of fewer rows than
+// the tiled GEMM takes: from 128 rows on, that GEMM rotates q^R itself).
 hipError_t prefill_rows_v2(const Geo& g, const void* cache, int num_pages,
                            const int32_t* page_table, int kv_len, void* rows, void* kbuf,
                            hipStream_t s);
