@@ -152,6 +152,11 @@ __device__ __forceinline__ void mfma_first(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// the first product of a chain that starts from c instead of zero (c from
+// registers that no VALU instruction has just written)
+__device__ __forceinline__ void mfma_from(f32x16& d, bf16x8 a, bf16x8 b, const f32x16& c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+}
 __device__ __forceinline__ void mfma_drain(f32x16& s) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
@@ -163,6 +168,9 @@ __device__ __forceinline__ void mfma_drain(f32x16& s, f32x16& dp) {
 // 2 wait states an MFMA read of them needs in between.
 __device__ __forceinline__ void settle(bf16x8 (&x)[2]) {
   asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]));
+}
+__device__ __forceinline__ void settle(f32x16& x) {
+  asm volatile("s_nop 4" : "+v"(x));
 }
 
 // Work-groups are dispatched round-robin over the eight XCDs (linear index

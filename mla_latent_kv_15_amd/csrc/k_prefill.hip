@@ -115,8 +115,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
   // this lane's query: the reference u (log2 units) of O and l, and l, the
   // sum of the numerators 2^(s - u).  Any reference gives the same softmax;
   // u moves only when a block's maximum exceeds it by more than kLazy, so
-  // the numerators stay at most 2^kLazy and O is rarely rescaled.
-  float u = -INFINITY, l = 0.f;
+  // the numerators stay at most 2^kLazy and O is rarely rescaled.  The score
+  // products start from -R, R = u (0 while u = -inf), so they give s - R
+  // directly: a block that keeps the reference needs no subtraction.
+  float u = -INFINITY, l = 0.f, R = 0.f;
+  f32x16 negr = {};
+  settle(negr);
   // byte offsets of the V^T operand reads (K-step kap, dim tile d), formed
   // once; the empty asm keeps each a single register, so a read is that
   // register plus the slot's immediate (left to itself the compiler shares
@@ -140,9 +144,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const int j0 = kb * kB;
     if (j0 <= far) {   // the wave has a query that sees a key of this block
       const lds_char* slot = lds + kSlot * kPSlot;
-      // S^T = K . Q^T (log2 units: q carries log2 e)
+      // S^T - R = K . Q^T - R (log2 units: q carries log2 e)
       f32x16 s;
-      mfma_first(s, row24(slot, lane, 0), qv[0]);
+      mfma_from(s, row24(slot, lane, 0), qv[0], negr);
 #pragma unroll
       for (int ks = 1; ks < kQK; ++ks) mfma_acc(s, row24(slot, lane, ks), qv[ks]);
       mfma_drain(s);
@@ -155,26 +159,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
           s[r] = key <= last ? s[r] : -INFINITY;
         }
       }
-      float bm = s[0];
+      float bm = s[0];   // (the block's maximum less R)
 #pragma unroll
       for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
       bm = swap_max(bm);
       // a new reference where the block's maximum passes u + kLazy (the
       // first key a query sees always does: u starts at -inf, alpha = 0 with
       // O and l still 0); no key seen yet: u stays -inf, numerators 0
-      const bool raise = bm > u + kLazy;
-      const float nu = raise ? bm : u;
+      const bool raise = bm > (u == -INFINITY ? -INFINITY : kLazy);
+      const float nu = raise ? bm + R : u;
       const float alpha = raise ? __builtin_amdgcn_exp2f(u - nu) : 1.f;
-      const float ref = nu == -INFINITY ? 0.f : nu;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - ref);
       u = nu;
       if (__builtin_amdgcn_ballot_w64(raise)) {
+        // scores to the new reference (a shift of 0 where it stays)
+        const float nr = nu == -INFINITY ? 0.f : nu;
+        const float shift = nr - R;
+        R = nr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] -= shift;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negr[r] = -nr;
+        settle(negr);
         drain_o(acc);
 #pragma unroll
         for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
         settle_o(acc);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]);
       bf16x8 pb[2];
       rows_as_b(s, pb);
       // l sums the bf16-rounded numerators, the values the product uses:
