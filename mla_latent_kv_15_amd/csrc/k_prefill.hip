@@ -12,9 +12,11 @@
 //
 // Design: one wave per (block of 32 queries, head), four such waves of one
 // head per work-group, two work-groups per compute unit.  The work-group
-// streams the blocks of 32 keys (K and V rows) through a ring of three LDS
+// streams the blocks of 32 keys (K and V rows) through a ring of four LDS
 // slots by direct-to-LDS loads, rows swizzled so that row reads and
-// transposing reads are free of bank conflicts (head_blocks.h).  The scores
+// transposing reads are free of bank conflicts (head_blocks.h).  Each wave
+// forms block kb + 1's scores between the exp2s of block kb's softmax,
+// one MFMA at a time, then block kb's O update.  The scores
 // are formed transposed, S^T[key][query] = K . Q^T, with
 // v_mfma_f32_32x32x16_bf16, so that every lane owns one query: its softmax
 // statistics stay in the lane apart from one permlane32 swap with the lane
@@ -37,7 +39,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPSlots = 3;                                 // ring slots (two blocks in flight)
+// ring slots: block kb (its V rows for P.V), block kb + 1 (its K rows for
+// the scores formed beside block kb's softmax), kb + 2 and kb + 3 in flight
+constexpr int kPSlots = 4;
 template <int I>
 using ic = std::integral_constant<int, I>;
 constexpr int kPLoads = (kUnitsW + kUnitsV) / 64 / kWv;    // 5 loads per wave per block
@@ -61,7 +65,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kbuf, const __bf16* __restrict__ vbuf,
     const int32_t* __restrict__ positions, int T, int kv_len, __bf16* __restrict__ o) {
   __shared__ __attribute__((aligned(16))) char ring[kPSlots * kPSlot];
-  __shared__ int s_far[kWv];
+  // (80 KB: two work-groups fill a compute unit's LDS.  The waves' furthest
+  // keys pass through the last slot, which no load writes before every wave
+  // has read them.)
+  int* const s_far = (int*)(ring + (kPSlots - 1) * kPSlot);
   lds_char* const lds = (lds_char*)ring;
   int i, xb;
   xcd_head_block(i, xb);
@@ -134,21 +141,29 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
       asm volatile("" : "+v"(tro[kap][d][0]), "+v"(tro[kap][d][1]));
     }
 
-  // block kb in slot kb % kPSlots; the loop body is instantiated once per slot
-  // so that the slot's offset is an immediate of the LDS reads
+  // Software pipeline over key blocks: iteration kb runs block kb's
+  // softmax and O^T += V^T . P^T, and between them block kb + 1's score
+  // products, one MFMA at a time with two of block kb's exp2s (or one pair's
+  // packing) issued behind each, so that the VALU work runs while the
+  // MFMA pipe is busy.  Each K-step's operand is read from LDS two MFMAs
+  // ahead.  Block kb's slot is an immediate in every read: the loop body is
+  // instantiated once per slot.
+  // block b's scores less R in sb[b % 2] (formed during iteration b - 1;
+  // b % 2 is the parity of its slot, so each copy of the body names fixed
+  // registers and no tile is copied)
+  f32x16 sb[2];
   auto step = [&](int kb, auto slot_c) {
     constexpr int kSlot = decltype(slot_c)::value;
-    wait_vm<kPLoads*(kPSlots - 2)>();   // this wave's loads of block kb
-    __syncthreads();                      // everyone's; slot (kb - 1) is free
+    constexpr int kNext = (kSlot + 1) % kPSlots;
+    f32x16& s = sb[kSlot & 1];
+    f32x16& sn = sb[kNext & 1];
+    wait_vm<kPLoads*(kPSlots - 3)>();   // this wave's loads of block kb + 1
+    __syncthreads();   // everyone's; block kb - 1's slot is free
     issue(kb + kPSlots - 1);
     const int j0 = kb * kB;
     if (j0 <= far) {   // the wave has a query that sees a key of this block
       const lds_char* slot = lds + kSlot * kPSlot;
-      // S^T - R = K . Q^T - R (log2 units: q carries log2 e)
-      f32x16 s;
-      mfma_from(s, row24(slot, lane, 0), qv[0], negr);
-#pragma unroll
-      for (int ks = 1; ks < kQK; ++ks) mfma_acc(s, row24(slot, lane, ks), qv[ks]);
+      const lds_char* nslot = lds + kNext * kPSlot;
       mfma_drain(s);
       // causal mask (only where the block reaches past some query's last
       // key) and the block's max for this query (both lane halves)
@@ -185,10 +200,43 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
         for (int d = 0; d < kDv / 32; ++d) acc[d] *= alpha;
         settle_o(acc);
       }
+      // block kb + 1's scores (past the wave's last block: formed, unused)
+      // beside block kb's numerators 2^(s - R) and their bf16 pairs
+      uint32_t pr[8];
+      bf16x8 ka[3];
+      ka[0] = row24(nslot, lane, 0);
+      ka[1] = row24(nslot, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]);
+      for (int ks = 0; ks < kQK; ++ks) {
+        if (ks + 2 < kQK) ka[(ks + 2) % 3] = row24(nslot, lane, ks + 2);
+        if (ks == 0)
+          mfma_from(sn, ka[0], qv[0], negr);
+        else
+          mfma_acc(sn, ka[ks % 3], qv[ks]);
+        if (ks < 8) {
+          s[2 * ks] = __builtin_amdgcn_exp2f(s[2 * ks]);
+          s[2 * ks + 1] = __builtin_amdgcn_exp2f(s[2 * ks + 1]);
+        } else {
+          pr[2 * (ks - 8)] = pack2(s[4 * (ks - 8)], s[4 * (ks - 8) + 1]);
+          pr[2 * (ks - 8) + 1] = pack2(s[4 * (ks - 8) + 2], s[4 * (ks - 8) + 3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the pairs as the B operands of P^T (rows_as_b's exchange: a lane
+      // holds rows 4h .. 4h + 3 of each eight, the lane 32 apart the others)
+#pragma unroll
+      for (int k = 0; k < 8; k += 4) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pr[k], pr[k + 2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pr[k + 1], pr[k + 3], false, false);
+        pr[k] = s0[0];
+        pr[k + 2] = s0[1];
+        pr[k + 1] = s1[0];
+        pr[k + 3] = s1[1];
+      }
       bf16x8 pb[2];
-      rows_as_b(s, pb);
+      pb[0] = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+      pb[1] = __builtin_bit_cast(bf16x8, u32x4{pr[4], pr[5], pr[6], pr[7]});
       // l sums the bf16-rounded numerators, the values the product uses:
       // pairs dotted with (1, 1); pb holds 16 of the query's 32 keys, the
       // lane 32 apart the other 16
@@ -218,17 +266,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_v2_kernel(
           mfma_acc(acc[d], tr_read(slot, tro[kap][d][0], tro[kap][d][1]), pb[kap]);
     }
   };
-  static_assert(kPSlots == 3, "the loop below runs three slots");
+  static_assert(kPSlots == 4, "the loop below runs four slots");
 #pragma unroll
   for (int b = 0; b < kPSlots - 1; ++b) issue(b);
+  wait_vm<kPLoads*(kPSlots - 2)>();   // this wave's loads of block 0
+  __syncthreads();
+  if (far >= 0) {   // block 0's scores
+    mfma_from(sb[0], row24(lds, lane, 0), qv[0], negr);
+#pragma unroll
+    for (int ks = 1; ks < kQK; ++ks) mfma_acc(sb[0], row24(lds, lane, ks), qv[ks]);
+  }
   int kb = 0;
-  for (; kb + 3 <= nkb; kb += 3) {
+  for (; kb + 4 <= nkb; kb += 4) {
     step(kb, ic<0>{});
     step(kb + 1, ic<1>{});
     step(kb + 2, ic<2>{});
+    step(kb + 3, ic<3>{});
   }
   if (kb < nkb) step(kb, ic<0>{});
   if (kb + 1 < nkb) step(kb + 1, ic<1>{});
+  if (kb + 2 < nkb) step(kb + 2, ic<2>{});
   wait_vm<0>();   // the padding loads of the ring's tail still write LDS
   drain_o(acc);
   if (!t_ok) return;
