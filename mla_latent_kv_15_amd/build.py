@@ -45,6 +45,17 @@ NO_SCRATCH = {"k_attn_v2.hip": ("combine_v2", "qtile_pack"), "k_gemm_v2.hip": ("
               "k_backward_v2.hip": ("attn_bwd_dq_v2", "attn_bwd_dkv_v2", "transpose16",
                                     "bwd_inputs_v2"),
               "k_tgemm.hip": ("tgemm",)}
+# Kernels that chain inline-asm MFMAs: the compiler does not model their
+# hazards, so a register copy it places between two of them (a VGPR restored
+# from an AGPR under register pressure, an accumulator moved) can read or
+# overwrite a register an MFMA still uses.  From the first MFMA of each
+# instantiation to its last, no scratch access and no AGPR copy is allowed.
+# (A 160-row weight-streaming tile with a four-step load ring once compiled to
+# such restores and returned garbage.)
+MFMA_SPAN_KERNELS = {"k_gemm_v2.hip": ("wgemm_kernel", "wgemm_plan_kernel"),
+                     "k_tgemm.hip": ("tgemm_kernel",),
+                     "k_prefill.hip": ("attn_prefill_v2_kernel",)}
+_SPAN_OPS = ("scratch_", "v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov")
 _SPILL_OPS = ("scratch_", "buffer_store", "buffer_load", "v_accvgpr_read", "v_accvgpr_write",
               "v_accvgpr_mov")
 
@@ -109,6 +120,38 @@ def _check_hot_blocks(src: str, asm: str):
                            + "\n  ".join(bad[:10]))
 
 
+def _check_mfma_spans(src: str, asm: str):
+    """No scratch access or AGPR copy between the first and the last MFMA of
+    any instantiation of the MFMA_SPAN_KERNELS of this source."""
+    base = os.path.basename(src)
+    names = MFMA_SPAN_KERNELS[base]
+    bad, found, cur, body = [], 0, None, []
+
+    def close():
+        if cur is None:
+            return
+        idx = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
+        if idx:
+            bad.extend(f"{cur[:60]}: {x}" for x in body[idx[0]:idx[-1]]
+                       if x.startswith(_SPAN_OPS))
+
+    for line in asm.splitlines():
+        c = line.split(";")[0].rstrip()
+        if c.endswith(":") and not c.startswith((".", "\t", " ")):
+            close()
+            cur = c[:-1] if any(n in c for n in names) else None
+            found += cur is not None
+            body = []
+        elif cur is not None:
+            body.append(c.strip())
+    close()
+    if not found:
+        raise RuntimeError(f"{base}: none of {names} found in the assembly")
+    if bad:
+        raise RuntimeError(f"{base}: register copies between inline-asm MFMAs:\n  "
+                           + "\n  ".join(bad[:10]))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
@@ -116,14 +159,19 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     _check_scratch(src, r.stderr)
-    if os.path.basename(src) in HOT_KERNELS:
-        s_file = os.path.join(BUILD, os.path.basename(src) + ".s")
+    base = os.path.basename(src)
+    if base in HOT_KERNELS or base in MFMA_SPAN_KERNELS:
+        s_file = os.path.join(BUILD, base + ".s")
         cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-S", src, "-o", s_file]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
         with open(s_file) as f:
-            _check_hot_blocks(src, f.read())
+            asm = f.read()
+        if base in HOT_KERNELS:
+            _check_hot_blocks(src, asm)
+        if base in MFMA_SPAN_KERNELS:
+            _check_mfma_spans(src, asm)
     return obj
 
 

@@ -68,3 +68,41 @@ def test_no_scratch_kernels_reject_any_spill():
     build._check_scratch("/x/k_attn_v2.hip", hot)
     with pytest.raises(RuntimeError):
         build._check_scratch("/x/k_attn_v2.hip", hot.replace(": 64", ": 4096"))
+
+
+def _span_asm(body, name="_ZN3mla12_GLOBAL__N_112wgemm_kernelILi5ELi32ELi4ELb1ELb1EEEv"):
+    return "\n".join([f"{name}:", *body, "\ts_endpgm", ".Lfunc_end1:"])
+
+
+SPAN_CLEAN = [
+    "\tv_accvgpr_write_b32 a0, 0",
+    "\tv_accvgpr_mov_b32 a1, a0",
+    "\tglobal_load_dwordx4 v[8:11], v[2:3], off",
+    "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], a[0:3]",
+    "\tglobal_load_dwordx4 v[8:11], v[2:3], off offset:1024",
+    "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], a[0:3]",
+    "\ts_nop 7",
+    "\tv_accvgpr_read_b32 v12, a0",
+]
+
+
+def test_mfma_span_allows_copies_outside_the_chain():
+    build._check_mfma_spans("k_gemm_v2.hip", _span_asm(SPAN_CLEAN))
+
+
+@pytest.mark.parametrize("copy", [
+    "\tv_accvgpr_read_b32 v152, a214",      # a VGPR restored from a spill AGPR
+    "\tv_accvgpr_write_b32 a187, v103",     # a VGPR spilled into an AGPR
+    "\tv_accvgpr_mov_b32 a40, a0",
+    "\tscratch_load_dword v6, off, off offset:12",
+])
+def test_mfma_span_rejects_copies_inside_the_chain(copy):
+    body = list(SPAN_CLEAN)
+    body.insert(4, copy)
+    with pytest.raises(RuntimeError, match="register copies between inline-asm MFMAs"):
+        build._check_mfma_spans("k_gemm_v2.hip", _span_asm(body))
+
+
+def test_mfma_span_needs_the_kernel():
+    with pytest.raises(RuntimeError, match="found in the assembly"):
+        build._check_mfma_spans("k_gemm_v2.hip", _span_asm(SPAN_CLEAN, name="_Z5otherv"))
