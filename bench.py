@@ -156,6 +156,65 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
                             "attn_v2_traffic_batch64.txt")
 
 
+def sclk_files():
+    """The GPU's shader-clock level files (the kernel driver lists the
+    levels, the current one marked with '*')."""
+    import glob
+    return sorted(f for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+                  if os.access(f, os.R_OK))
+
+
+def read_sclk(path):
+    """The marked (current) level of a pp_dpm_sclk file, in MHz, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def sample_clock(run_steps, n_steps, period_s=0.002):
+    """Median, min and max shader clock sampled from sysfs while n_steps
+    decode steps run back to back; None where the driver's files are absent."""
+    import threading
+
+    import numpy as np
+    import torch
+    files = sclk_files()
+    if not files:
+        return None
+    samples = {f: [] for f in files}
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            for f in files:
+                v = read_sclk(f)
+                if v is not None:
+                    samples[f].append(v)
+            time.sleep(period_s)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    run_steps(n_steps)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    # the busy card is the one whose clock moved most above its lowest level
+    best = max(files, key=lambda f: (np.median(samples[f]) if samples[f] else -1.0))
+    v = np.array(samples[best])
+    if v.size == 0:
+        return None
+    return {"sclk_mhz_median": float(np.median(v)), "sclk_mhz_min": float(v.min()),
+            "sclk_mhz_max": float(v.max()), "samples": int(v.size),
+            "source": f"{best} (current level), sampled every {period_s * 1e3:.0f} ms over "
+                      f"{n_steps} decode steps run back to back",
+            "bf16_mfma_peak_at_median_tflops": BF16_PEAK_TFLOPS * float(np.median(v)) / 2400.0}
+
+
 def measured_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, if
     it was taken on the current attention and planner sources and on this
@@ -486,6 +545,11 @@ def main():
     torch.cuda.synchronize()
     attn_ms, attn_merge_ms, launches = lib.profile_read()
     lib.profile_enable(False)
+    # 4) the shader clock while steps run (the peaks above assume 2.4 GHz)
+    def run_steps(n):
+        for i in range(n):
+            step(i)
+    clock = sample_clock(run_steps, max(1000, args.steps))
     attn_avg = attn_ms / max(launches, 1)
     am_avg = attn_merge_ms / max(launches, 1)
     # per-launch algorithmic work: the cached rows of the step's batch (sets alternate)
@@ -538,6 +602,7 @@ def main():
         },
         "attention_mfma_tflops": mfma_tflops,
         "attention_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
+        "clock": clock,
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
     }
