@@ -176,9 +176,24 @@ def read_sclk(path):
     return None
 
 
-def sample_clock(run_steps, n_steps, period_s=0.002):
-    """Median, min and max shader clock sampled from sysfs while n_steps
-    decode steps run back to back; None where the driver's files are absent."""
+def read_power_w(card_dir):
+    """The board power the driver reports (hwmon power1_average, else
+    power1_input, microwatts) in watts, or None."""
+    import glob
+    for name in ("power1_average", "power1_input"):
+        for f in sorted(glob.glob(os.path.join(card_dir, "hwmon", "hwmon*", name))):
+            try:
+                with open(f) as fh:
+                    return float(fh.read().strip()) * 1e-6
+            except (OSError, ValueError):
+                continue
+    return None
+
+
+def sample_clock(run_steps, n_steps, what="decode steps", period_s=0.002):
+    """Median, min and max shader clock (and board power where readable)
+    sampled from sysfs while n_steps calls run back to back; None where the
+    driver's files are absent."""
     import threading
 
     import numpy as np
@@ -187,6 +202,7 @@ def sample_clock(run_steps, n_steps, period_s=0.002):
     if not files:
         return None
     samples = {f: [] for f in files}
+    power = {f: [] for f in files}
     stop = threading.Event()
 
     def sampler():
@@ -195,6 +211,9 @@ def sample_clock(run_steps, n_steps, period_s=0.002):
                 v = read_sclk(f)
                 if v is not None:
                     samples[f].append(v)
+                w = read_power_w(os.path.dirname(f))
+                if w is not None:
+                    power[f].append(w)
             time.sleep(period_s)
 
     th = threading.Thread(target=sampler, daemon=True)
@@ -208,10 +227,13 @@ def sample_clock(run_steps, n_steps, period_s=0.002):
     v = np.array(samples[best])
     if v.size == 0:
         return None
+    pw = np.array(power[best])
     return {"sclk_mhz_median": float(np.median(v)), "sclk_mhz_min": float(v.min()),
             "sclk_mhz_max": float(v.max()), "samples": int(v.size),
-            "source": f"{best} (current level), sampled every {period_s * 1e3:.0f} ms over "
-                      f"{n_steps} decode steps run back to back",
+            "board_power_w_median": float(np.median(pw)) if pw.size else None,
+            "board_power_w_max": float(pw.max()) if pw.size else None,
+            "source": f"{best} (current level) and its hwmon power, sampled every "
+                      f"{period_s * 1e3:.0f} ms over {n_steps} {what} run back to back",
             "bf16_mfma_peak_at_median_tflops": BF16_PEAK_TFLOPS * float(np.median(v)) / 2400.0}
 
 
@@ -550,6 +572,20 @@ def main():
         for i in range(n):
             step(i)
     clock = sample_clock(run_steps, max(1000, args.steps))
+    # the same while only the cache stream runs (mla_decode_attention: query
+    # tiles, plan, attention kernel, merge) on a random absorbed query
+    qa = (torch.randn(B, s.n_h, s.row, device="cuda") * 0.05).to(torch.bfloat16)
+    ws_a = device.workspace(lib.workspace_size(cfg, lib.OP_DECODE_ATTENTION, B, max_kv,
+                                               args.splits))
+    lat = torch.empty(B, s.n_h, s.d_c, dtype=torch.bfloat16, device="cuda")
+
+    def run_attention(n):
+        for i in range(n):
+            st = sets[i % len(sets)]
+            lib.decode_attention(cfg, qa, st["cache"], st["pt"], st["kv_d"], max_kv, args.splits,
+                                 ws_a, lat)
+    clock_attention = sample_clock(run_attention, max(2000, args.steps),
+                                   "mla_decode_attention calls")
     attn_avg = attn_ms / max(launches, 1)
     am_avg = attn_merge_ms / max(launches, 1)
     # per-launch algorithmic work: the cached rows of the step's batch (sets alternate)
@@ -603,6 +639,7 @@ def main():
         "attention_mfma_tflops": mfma_tflops,
         "attention_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
         "clock": clock,
+        "clock_attention": clock_attention,
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
     }
